@@ -1,0 +1,580 @@
+// C ABI of the DFlash drafter library: validation, workspace carving, weight
+// re-tiling at create time, and the orchestration of encode, inject, the block
+// step (optionally captured into a HIP graph) and the acceptance scan.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "dflash_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(DFLASH_EHIP, "%s failed: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                          \
+    do {                                             \
+        hipError_t _e = (expr);                      \
+        if (_e != hipSuccess) return hip_fail(_e, what); \
+    } while (0)
+
+size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int dtype_bytes(int dt) { return dt == DFLASH_F32 ? 4 : dt == DFLASH_BF16 ? 2 : 1; }
+
+int check_config(const dflash_config *c) {
+    if (!c) return fail(DFLASH_EINVAL, "config is NULL");
+    if (c->n_layer < 1 || c->n_layer > 16) return fail(DFLASH_EUNSUPPORTED, "n_layer must be in 1..16");
+    if (c->head_dim != 64 && c->head_dim != 128) return fail(DFLASH_EUNSUPPORTED, "head_dim must be 64 or 128");
+    if (c->n_head_kv < 1 || c->n_head < c->n_head_kv || c->n_head % c->n_head_kv)
+        return fail(DFLASH_EUNSUPPORTED, "n_head must be a positive multiple of n_head_kv");
+    if (c->n_head / c->n_head_kv > 4)
+        return fail(DFLASH_EUNSUPPORTED, "at most 4 query heads per kv head are supported");
+    if (c->block != 16) return fail(DFLASH_EUNSUPPORTED, "block must be 16");
+    const int64_t m64[] = {c->n_embd, c->n_ff, c->n_vocab, (int64_t)c->n_capture * c->target_hidden,
+                           (int64_t)c->n_head * c->head_dim, (int64_t)c->n_head_kv * c->head_dim, c->window};
+    for (int64_t v : m64)
+        if (v <= 0 || v % 64) return fail(DFLASH_EUNSUPPORTED, "dimensions must be positive multiples of 64");
+    if (c->window > 65536) return fail(DFLASH_EUNSUPPORTED, "window must be <= 65536");
+    if (c->max_batch < 1 || c->max_batch > 8) return fail(DFLASH_EUNSUPPORTED, "max_batch must be in 1..8");
+    if (c->max_inject < 1) return fail(DFLASH_EINVAL, "max_inject must be >= 1");
+    if (c->mask_id < 0 || c->mask_id >= c->n_vocab) return fail(DFLASH_EINVAL, "mask_id out of range");
+    if (!(c->rms_eps >= 0.0f) || !(c->rope_base > 0.0)) return fail(DFLASH_EINVAL, "bad rms_eps or rope_base");
+    if (c->weight_dtype < DFLASH_F32 || c->weight_dtype > DFLASH_FP8_E4M3)
+        return fail(DFLASH_EINVAL, "weight_dtype must be F32, BF16 or FP8_E4M3");
+    if (c->aux_dtype != DFLASH_F32 && c->aux_dtype != DFLASH_BF16) return fail(DFLASH_EINVAL, "aux_dtype must be F32 or BF16");
+    if (c->ring_dtype != DFLASH_F32 && c->ring_dtype != DFLASH_BF16) return fail(DFLASH_EINVAL, "ring_dtype must be F32 or BF16");
+    if (c->feature_dtype != DFLASH_F32 && c->feature_dtype != DFLASH_BF16)
+        return fail(DFLASH_EINVAL, "feature_dtype must be F32 or BF16");
+    return DFLASH_OK;
+}
+
+// k-split of a weight-streaming launch: aim for ~768 workgroups (three per
+// CU) with at least 8 k-blocks (two per wave) in each.
+void choose_split(int G, int KB, int &S, int &kbps) {
+    S = std::max(1, std::min((KB + 7) / 8, (768 + G - 1) / G));
+    kbps = (KB + S - 1) / S;
+    S = (KB + kbps - 1) / kbps;
+}
+
+int mt_for(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
+
+struct Carver {
+    char *base;
+    size_t off = 0;
+    explicit Carver(char *b) : base(b) {}
+    template <typename T>
+    T *take(size_t bytes) {
+        size_t o = off;
+        off = a256(off + bytes);
+        return base ? (T *)(base + o) : nullptr;
+    }
+};
+
+// Carve (or, with base == nullptr, just size) the workspace.
+size_t carve(dflash_ctx &x, char *base) {
+    const dflash_config &c = x.cfg;
+    Carver cv(base);
+    const int E = c.n_embd, L = c.n_layer, D = c.head_dim, F = c.n_ff, V = c.n_vocab;
+    const int qdim = c.n_head * D, kvdim = c.n_head_kv * D, nqkv = qdim + 2 * kvdim;
+    const int Cin = c.n_capture * c.target_hidden;
+    const int Mmax = 16 * c.max_batch;
+    const size_t esw = dtype_bytes(c.weight_dtype), esa = dtype_bytes(c.aux_dtype);
+    const bool fp8 = c.weight_dtype == DFLASH_FP8_E4M3;
+    const int act_fmt = c.weight_dtype == DFLASH_F32 ? ACT_F32 : ACT_SPLIT3;
+    const size_t act_es = act_fmt == ACT_F32 ? 4 : 6;  // bytes per activation element (3 bf16 planes)
+
+    x.inv_freq = cv.take<double>(sizeof(double) * D / 2);
+    x.hidden_norm = cv.take<float>(4ull * E);
+    x.output_norm = cv.take<float>(4ull * E);
+    x.attn_norm = cv.take<float>(4ull * L * E);
+    x.ffn_norm = cv.take<float>(4ull * L * E);
+    x.q_norm = cv.take<float>(4ull * L * D);
+    x.k_norm = cv.take<float>(4ull * L * D);
+    x.fc = cv.take<void>(esa * E * Cin);
+    x.kv = cv.take<void>(esw * (size_t)L * 2 * kvdim * E);
+    x.s_kv = fp8 ? cv.take<float>(4ull * L * 2 * kvdim) : nullptr;
+    for (int l = 0; l < L; ++l) {
+        LayerBufs &b = x.layer[l];
+        b.qkv = cv.take<void>(esw * nqkv * E);
+        b.o = cv.take<void>(esw * E * qdim);
+        b.gu = cv.take<void>(esw * 2ull * F * E);
+        b.down = cv.take<void>(esw * (size_t)E * F);
+        b.s_qkv = fp8 ? cv.take<float>(4ull * nqkv) : nullptr;
+        b.s_o = fp8 ? cv.take<float>(4ull * E) : nullptr;
+        b.s_gu = fp8 ? cv.take<float>(8ull * F) : nullptr;
+        b.s_down = fp8 ? cv.take<float>(4ull * E) : nullptr;
+    }
+    x.lm = cv.take<void>(esw * (size_t)V * E);
+    x.s_lm = fp8 ? cv.take<float>(4ull * V) : nullptr;
+
+    const int G_E = E / GROUP_N, G = c.n_head / c.n_head_kv, NCH = c.window / 64;
+    x.x = cv.take<float>(4ull * Mmax * E);
+    x.act_a = cv.take<void>(act_es * Mmax * E);
+    x.act_f = cv.take<void>(act_es * Mmax * E);
+    x.act_d = cv.take<void>(act_es * Mmax * F);
+    x.act_o = cv.take<void>(act_es * Mmax * qdim);
+    x.ss_a = cv.take<float>(4ull * G_E * Mmax);
+    x.ss_f = cv.take<float>(4ull * G_E * Mmax);
+    x.qkv_out = cv.take<float>(4ull * Mmax * nqkv);
+    x.rope_cs = cv.take<float>(4ull * c.max_batch * c.block * D);
+    x.att_ml = cv.take<float>(4ull * c.max_batch * c.n_head_kv * (NCH + 1) * G * 16 * 2);
+    x.att_o = cv.take<float>(4ull * c.max_batch * c.n_head_kv * (NCH + 1) * G * 16 * D);
+    // split-K partials: the largest S * G * Mp * 64 over the step's launches
+    const int Mp = 16 * mt_for(Mmax);
+    const int shapes[5][2] = {{nqkv, E}, {E, qdim}, {2 * F, E}, {E, F}, {V, E}};
+    size_t pmax = 0;
+    int gmax = 0;
+    for (auto &sh : shapes) {
+        int Gn = sh[0] / GROUP_N, KB = sh[1] / KBLK, S, kbps;
+        choose_split(Gn, KB, S, kbps);
+        pmax = std::max(pmax, (size_t)S * Gn * Mp * GROUP_N);
+        gmax = std::max(gmax, Gn);
+    }
+    x.partial = cv.take<float>(4 * pmax);
+    x.partial_floats = pmax;
+    x.counters = cv.take<int>(4ull * gmax);
+    x.n_counters = gmax;
+    x.am_val = cv.take<float>(4ull * (V / GROUP_N) * Mmax);
+    x.am_idx = cv.take<int>(4ull * (V / GROUP_N) * Mmax);
+    x.am_counter = cv.take<int>(4);
+    x.ids = cv.take<int32_t>(4ull * Mmax);
+
+    const int T = c.max_inject;
+    x.enc_y = cv.take<float>(4ull * T * E);
+    x.enc_act = nullptr;
+    if (c.aux_dtype == DFLASH_F32 && c.feature_dtype == DFLASH_BF16) x.enc_act = cv.take<void>(4ull * T * Cin);
+    if (c.aux_dtype == DFLASH_BF16 && c.feature_dtype == DFLASH_F32) x.enc_act = cv.take<void>(6ull * T * Cin);
+    x.inj_act = act_fmt == ACT_SPLIT3 ? cv.take<void>(6ull * T * E) : nullptr;
+    x.inj_kv = cv.take<float>(4ull * T * L * 2 * kvdim);
+    return cv.off;
+}
+
+void derive(dflash_ctx &x) {
+    const dflash_config &c = x.cfg;
+    x.E = c.n_embd;
+    x.H = c.n_head;
+    x.Hkv = c.n_head_kv;
+    x.D = c.head_dim;
+    x.F = c.n_ff;
+    x.W = c.window;
+    x.L = c.n_layer;
+    x.V = c.n_vocab;
+    x.C = c.n_capture * c.target_hidden;
+    x.qdim = x.H * x.D;
+    x.kvdim = x.Hkv * x.D;
+    x.nqkv = x.qdim + 2 * x.kvdim;
+    x.Mmax = 16 * c.max_batch;
+    x.G_E = x.E / GROUP_N;
+    x.NCH = x.W / 64;
+    x.act_fmt = c.weight_dtype == DFLASH_F32 ? ACT_F32 : ACT_SPLIT3;
+    x.wbytes_el = dtype_bytes(c.weight_dtype);
+}
+
+size_t ring_bytes_of(const dflash_config &c) {
+    const int es = dtype_bytes(c.ring_dtype);
+    const size_t kv = a256((size_t)c.n_layer * c.n_head_kv * c.window * c.head_dim * es);
+    return 2 * kv + a256(4ull * c.window);
+}
+
+int tile_matrix(const void *src, int rows, int K, int es, void *dst, int row_map, int row0, int half, hipStream_t s) {
+    HIP_TRY(launch_tile_weights(src, rows, K, es, dst, K / KBLK, row_map, row0, half, s), "weight tiling launch");
+    return DFLASH_OK;
+}
+
+int tile_scales(const float *src, int rows, float *dst, int row_map, int row0, int half, hipStream_t s) {
+    if (!dst) return DFLASH_OK;
+    HIP_TRY(launch_tile_scales(src, rows, dst, row_map, row0, half, s), "scale tiling launch");
+    return DFLASH_OK;
+}
+
+#define TRY(expr)                      \
+    do {                               \
+        int _r = (expr);               \
+        if (_r != DFLASH_OK) return _r; \
+    } while (0)
+
+int check_weights(const dflash_config &c, const dflash_weights *w) {
+    if (!w) return fail(DFLASH_EINVAL, "weights is NULL");
+    if (!w->tok_embd || !w->lm_head || !w->fc || !w->hidden_norm || !w->output_norm || !w->layers)
+        return fail(DFLASH_EINVAL, "a global weight pointer is NULL");
+    const bool fp8 = c.weight_dtype == DFLASH_FP8_E4M3;
+    if (fp8 && !w->s_lm_head) return fail(DFLASH_EINVAL, "s_lm_head is NULL for FP8 weights");
+    for (int l = 0; l < c.n_layer; ++l) {
+        const dflash_layer_weights &lw = w->layers[l];
+        if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.q_norm || !lw.k_norm || !lw.ffn_norm ||
+            !lw.w_gate || !lw.w_up || !lw.w_down)
+            return fail(DFLASH_EINVAL, "a weight pointer of layer %d is NULL", l);
+        if (fp8 && (!lw.s_q || !lw.s_k || !lw.s_v || !lw.s_o || !lw.s_gate || !lw.s_up || !lw.s_down))
+            return fail(DFLASH_EINVAL, "an FP8 scale pointer of layer %d is NULL", l);
+    }
+    return DFLASH_OK;
+}
+
+int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
+    const dflash_config &c = x.cfg;
+    const int E = x.E, L = x.L, D = x.D, F = x.F, V = x.V;
+    const int esw = (int)x.wbytes_el, esa = dtype_bytes(c.aux_dtype);
+    std::vector<double> f(D / 2);
+    for (int i = 0; i < D / 2; ++i) f[i] = pow(c.rope_base, -2.0 * i / D);
+    HIP_TRY(hipMemcpyAsync(x.inv_freq, f.data(), sizeof(double) * f.size(), hipMemcpyHostToDevice, s),
+            "inverse-frequency upload");
+    HIP_TRY(hipStreamSynchronize(s), "inverse-frequency upload");
+    HIP_TRY(launch_vec_to_f32(w->hidden_norm, c.aux_dtype, E, x.hidden_norm, s), "norm copy");
+    HIP_TRY(launch_vec_to_f32(w->output_norm, c.aux_dtype, E, x.output_norm, s), "norm copy");
+    for (int l = 0; l < L; ++l) {
+        const dflash_layer_weights &lw = w->layers[l];
+        HIP_TRY(launch_vec_to_f32(lw.attn_norm, c.aux_dtype, E, x.attn_norm + (size_t)l * E, s), "norm copy");
+        HIP_TRY(launch_vec_to_f32(lw.ffn_norm, c.aux_dtype, E, x.ffn_norm + (size_t)l * E, s), "norm copy");
+        HIP_TRY(launch_vec_to_f32(lw.q_norm, c.aux_dtype, D, x.q_norm + (size_t)l * D, s), "norm copy");
+        HIP_TRY(launch_vec_to_f32(lw.k_norm, c.aux_dtype, D, x.k_norm + (size_t)l * D, s), "norm copy");
+    }
+    TRY(tile_matrix(w->fc, E, x.C, esa, x.fc, 0, 0, 0, s));
+    for (int l = 0; l < L; ++l) {
+        const dflash_layer_weights &lw = w->layers[l];
+        const int r0 = l * 2 * x.kvdim;
+        TRY(tile_matrix(lw.wk, x.kvdim, E, esw, x.kv, 0, r0, 0, s));
+        TRY(tile_matrix(lw.wv, x.kvdim, E, esw, x.kv, 0, r0 + x.kvdim, 0, s));
+        TRY(tile_scales(lw.s_k, x.kvdim, x.s_kv, 0, r0, 0, s));
+        TRY(tile_scales(lw.s_v, x.kvdim, x.s_kv, 0, r0 + x.kvdim, 0, s));
+        LayerBufs &b = x.layer[l];
+        TRY(tile_matrix(lw.wq, x.qdim, E, esw, b.qkv, 0, 0, 0, s));
+        TRY(tile_matrix(lw.wk, x.kvdim, E, esw, b.qkv, 0, x.qdim, 0, s));
+        TRY(tile_matrix(lw.wv, x.kvdim, E, esw, b.qkv, 0, x.qdim + x.kvdim, 0, s));
+        TRY(tile_scales(lw.s_q, x.qdim, b.s_qkv, 0, 0, 0, s));
+        TRY(tile_scales(lw.s_k, x.kvdim, b.s_qkv, 0, x.qdim, 0, s));
+        TRY(tile_scales(lw.s_v, x.kvdim, b.s_qkv, 0, x.qdim + x.kvdim, 0, s));
+        TRY(tile_matrix(lw.wo, E, x.qdim, esw, b.o, 0, 0, 0, s));
+        TRY(tile_scales(lw.s_o, E, b.s_o, 0, 0, 0, s));
+        TRY(tile_matrix(lw.w_gate, F, E, esw, b.gu, 1, 0, 0, s));
+        TRY(tile_matrix(lw.w_up, F, E, esw, b.gu, 1, 0, 1, s));
+        TRY(tile_scales(lw.s_gate, F, b.s_gu, 1, 0, 0, s));
+        TRY(tile_scales(lw.s_up, F, b.s_gu, 1, 0, 1, s));
+        TRY(tile_matrix(lw.w_down, E, F, esw, b.down, 0, 0, 0, s));
+        TRY(tile_scales(lw.s_down, E, b.s_down, 0, 0, 0, s));
+    }
+    TRY(tile_matrix(w->lm_head, V, E, esw, x.lm, 0, 0, 0, s));
+    TRY(tile_scales(w->s_lm_head, V, x.s_lm, 0, 0, 0, s));
+    HIP_TRY(launch_fill_i32(x.counters, 0, x.n_counters, s), "counter reset");
+    HIP_TRY(launch_fill_i32(x.am_counter, 0, 1, s), "counter reset");
+    return DFLASH_OK;
+}
+
+EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
+    EpiArgs e = {};
+    e.kind = kind;
+    e.M = M;
+    e.ss_stride = x.Mmax;
+    e.inv_E = 1.0f / (float)x.E;
+    e.eps = x.cfg.rms_eps;
+    e.block = x.cfg.block;
+    e.act_rows = x.Mmax;
+    e.act_fmt = x.act_fmt;
+    return e;
+}
+
+int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, const EpiArgs &epi, hipStream_t s) {
+    GemvArgs a = {};
+    a.W = W;
+    a.N = N;
+    a.K = K;
+    a.act = act;
+    a.act_rows = x.Mmax;
+    const int G = N / GROUP_N, KB = K / KBLK;
+    choose_split(G, KB, a.S, a.kb_per_split);
+    a.partial = x.partial;
+    a.counters = x.counters;
+    a.epi = epi;
+    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), dim3(G, a.S), a, s), "block-step GEMV launch");
+    return DFLASH_OK;
+}
+
+int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const int32_t *block_ids,
+             const int32_t *n_past, int B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
+             hipStream_t s) {
+    const int M = 16 * B, E = x.E;
+    HIP_TRY(launch_embed(&x, id_last, block_ids, n_past, B, s), "embed launch");
+    for (int l = 0; l < x.L; ++l) {
+        const LayerBufs &b = x.layer[l];
+        EpiArgs e = epi_base(x, EPI_SCALED, M);
+        e.wscale = b.s_qkv;
+        e.ss = x.ss_a;
+        e.ss_groups = x.G_E;
+        e.out = x.qkv_out;
+        e.ld_out = x.nqkv;
+        TRY(gemv(x, b.qkv, x.nqkv, E, x.act_a, e, s));
+
+        HIP_TRY(launch_attention(&x, l, rings, n_past, B, s), "attention launch");
+
+        e = epi_base(x, EPI_RESID, M);
+        e.wscale = b.s_o;
+        e.x = x.x;
+        e.ld_x = E;
+        e.wnext = x.ffn_norm + (size_t)l * E;
+        e.act_out = x.act_f;
+        e.act_K = E;
+        e.ss_out = x.ss_f;
+        TRY(gemv(x, b.o, E, x.qdim, x.act_o, e, s));
+
+        e = epi_base(x, EPI_SWIGLU, M);
+        e.wscale = b.s_gu;
+        e.ss = x.ss_f;
+        e.ss_groups = x.G_E;
+        e.act_out = x.act_d;
+        e.act_K = x.F;
+        TRY(gemv(x, b.gu, 2 * x.F, E, x.act_f, e, s));
+
+        e = epi_base(x, EPI_RESID, M);
+        e.wscale = b.s_down;
+        e.x = x.x;
+        e.ld_x = E;
+        e.wnext = l + 1 < x.L ? x.attn_norm + (size_t)(l + 1) * E : x.output_norm;
+        e.act_out = x.act_a;
+        e.act_K = E;
+        e.ss_out = x.ss_a;
+        TRY(gemv(x, b.down, E, x.F, x.act_d, e, s));
+    }
+    EpiArgs e = epi_base(x, EPI_LOGITS, M);
+    e.wscale = x.s_lm;
+    e.ss = x.ss_a;
+    e.ss_groups = x.G_E;
+    e.out = logits;
+    e.ld_out = x.V;
+    e.am_val = x.am_val;
+    e.am_idx = x.am_idx;
+    e.am_counter = x.am_counter;
+    e.drafts = drafts;
+    e.target = target;
+    e.n_ok = n_ok;
+    TRY(gemv(x, x.lm, x.V, E, x.act_a, e, s));
+    return DFLASH_OK;
+}
+
+int check_step_args(dflash_ctx *x, void *const *rings, const void *ids, const int32_t *n_past, int B, float *logits,
+                     int32_t *drafts) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    if (!rings || !ids || !n_past || !logits || !drafts) return fail(DFLASH_EINVAL, "a step pointer is NULL");
+    if (B < 1 || B > x->cfg.max_batch) return fail(DFLASH_ERANGE, "B=%d outside 1..max_batch=%d", B, x->cfg.max_batch);
+    return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dflash_last_error(void) { return g_err.c_str(); }
+
+size_t dflash_workspace_bytes(const dflash_config *cfg) {
+    if (check_config(cfg) != DFLASH_OK) return 0;
+    dflash_ctx x = {};
+    x.cfg = *cfg;
+    derive(x);
+    return carve(x, nullptr);
+}
+
+size_t dflash_ring_bytes(const dflash_config *cfg) {
+    if (check_config(cfg) != DFLASH_OK) return 0;
+    return ring_bytes_of(*cfg);
+}
+
+int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *workspace, size_t workspace_bytes,
+                  void *stream, dflash_ctx **out) {
+    if (!out) return fail(DFLASH_EINVAL, "out is NULL");
+    *out = nullptr;
+    TRY(check_config(cfg));
+    TRY(check_weights(*cfg, w));
+    if (!workspace) return fail(DFLASH_EINVAL, "workspace is NULL");
+    if ((uintptr_t)workspace % 256) return fail(DFLASH_EINVAL, "workspace must be 256-byte aligned");
+    dflash_ctx *x = new dflash_ctx();
+    x->cfg = *cfg;
+    derive(*x);
+    const size_t need = carve(*x, nullptr);
+    if (workspace_bytes < need) {
+        delete x;
+        return fail(DFLASH_ERANGE, "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+    }
+    carve(*x, (char *)workspace);
+    x->ws = (char *)workspace;
+    x->ws_bytes = workspace_bytes;
+    x->tok_embd = w->tok_embd;
+    hipError_t e = hipGetDevice(&x->device);
+    if (e != hipSuccess) {
+        delete x;
+        return hip_fail(e, "hipGetDevice");
+    }
+    int r = prepare(*x, w, (hipStream_t)stream);
+    if (r != DFLASH_OK) {
+        delete x;
+        return r;
+    }
+    *out = x;
+    return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_ctx *ctx) { delete ctx; }
+
+int dflash_ring_reset(dflash_ctx *x, void *ring, void *stream) {
+    if (!x || !ring) return fail(DFLASH_EINVAL, "ctx or ring is NULL");
+    if ((uintptr_t)ring % 256) return fail(DFLASH_EINVAL, "ring must be 256-byte aligned");
+    const int es = dtype_bytes(x->cfg.ring_dtype);
+    const size_t kv = a256((size_t)x->L * x->Hkv * x->W * x->D * es);
+    HIP_TRY(launch_fill_i32((int32_t *)((char *)ring + 2 * kv), -1, x->W, (hipStream_t)stream), "ring reset launch");
+    return DFLASH_OK;
+}
+
+int dflash_encode(dflash_ctx *x, const void *feats, int32_t T, float *h, void *stream) {
+    if (!x || !feats || !h) return fail(DFLASH_EINVAL, "ctx, feats or h is NULL");
+    if (T < 1 || T > x->cfg.max_inject) return fail(DFLASH_ERANGE, "T=%d outside 1..max_inject=%d", T, x->cfg.max_inject);
+    hipStream_t s = (hipStream_t)stream;
+    const dflash_config &c = x->cfg;
+    const void *act = feats;
+    int fmt;
+    int act_rows = T;
+    if (c.aux_dtype == DFLASH_F32) {
+        fmt = ACT_F32;
+        if (c.feature_dtype == DFLASH_BF16) {
+            HIP_TRY(launch_bf16_to_f32((const uint16_t *)feats, (size_t)T * x->C, (float *)x->enc_act, s),
+                    "feature conversion launch");
+            act = x->enc_act;
+        }
+    } else if (c.feature_dtype == DFLASH_BF16) {
+        fmt = ACT_BF16;
+    } else {
+        fmt = ACT_SPLIT3;
+        act_rows = c.max_inject;
+        HIP_TRY(launch_split((const float *)feats, T, x->C, x->C, x->enc_act, ACT_SPLIT3, act_rows, s),
+                "feature split launch");
+        act = x->enc_act;
+    }
+    GemmArgs g = {};
+    g.W = x->fc;
+    g.N = x->E;
+    g.K = x->C;
+    g.M = T;
+    g.act = act;
+    g.act_rows = act_rows;
+    g.out = x->enc_y;
+    HIP_TRY(launch_gemm(c.aux_dtype, fmt, g, s), "encode GEMM launch");
+    HIP_TRY(launch_rmsnorm_rows(x->enc_y, T, x->E, x->hidden_norm, c.rms_eps, h, s), "encode norm launch");
+    return DFLASH_OK;
+}
+
+int dflash_inject(dflash_ctx *x, void *ring, const float *h, const int32_t *pos, int32_t T, void *stream) {
+    if (!x || !ring || !h || !pos) return fail(DFLASH_EINVAL, "ctx, ring, h or pos is NULL");
+    if ((uintptr_t)ring % 256) return fail(DFLASH_EINVAL, "ring must be 256-byte aligned");
+    if (T < 1 || T > x->W || T > x->cfg.max_inject)
+        return fail(DFLASH_ERANGE, "T=%d outside 1..min(window=%d, max_inject=%d)", T, x->W, x->cfg.max_inject);
+    hipStream_t s = (hipStream_t)stream;
+    const void *act = h;
+    int act_rows = T;
+    if (x->act_fmt == ACT_SPLIT3) {
+        act_rows = x->cfg.max_inject;
+        HIP_TRY(launch_split(h, T, x->E, x->E, x->inj_act, ACT_SPLIT3, act_rows, s), "inject split launch");
+        act = x->inj_act;
+    }
+    GemmArgs g = {};
+    g.W = x->kv;
+    g.wscale = x->s_kv;
+    g.N = x->L * 2 * x->kvdim;
+    g.K = x->E;
+    g.M = T;
+    g.act = act;
+    g.act_rows = act_rows;
+    g.out = x->inj_kv;
+    HIP_TRY(launch_gemm(x->cfg.weight_dtype, x->act_fmt, g, s), "inject GEMM launch");
+    HIP_TRY(launch_inject(x, ring, pos, T, s), "inject launch");
+    return DFLASH_OK;
+}
+
+int dflash_block_step(dflash_ctx *x, void *const *rings, const int32_t *id_last, const int32_t *n_past, int32_t B,
+                      float *logits, int32_t *drafts, void *stream) {
+    TRY(check_step_args(x, rings, id_last, n_past, B, logits, drafts));
+    return run_step(*x, rings, id_last, nullptr, n_past, B, logits, drafts, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int dflash_block_forward(dflash_ctx *x, void *const *rings, const int32_t *block_ids, const int32_t *n_past, int32_t B,
+                         float *logits, int32_t *drafts, void *stream) {
+    TRY(check_step_args(x, rings, block_ids, n_past, B, logits, drafts));
+    return run_step(*x, rings, nullptr, block_ids, n_past, B, logits, drafts, nullptr, nullptr, (hipStream_t)stream);
+}
+
+int dflash_accept(dflash_ctx *x, const int32_t *drafts, const int32_t *target, int32_t B, int32_t *n_ok,
+                  void *stream) {
+    if (!x || !drafts || !target || !n_ok) return fail(DFLASH_EINVAL, "a pointer is NULL");
+    if (B < 1 || B > x->cfg.max_batch) return fail(DFLASH_ERANGE, "B=%d outside 1..max_batch=%d", B, x->cfg.max_batch);
+    HIP_TRY(launch_accept(drafts, target, B, x->cfg.block - 1, n_ok, (hipStream_t)stream), "accept launch");
+    return DFLASH_OK;
+}
+
+int dflash_step_graph_create(dflash_ctx *x, void *const *rings, const int32_t *id_last, const int32_t *n_past,
+                             int32_t B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
+                             void *stream, dflash_graph **out) {
+    if (!out) return fail(DFLASH_EINVAL, "out is NULL");
+    *out = nullptr;
+    TRY(check_step_args(x, rings, id_last, n_past, B, logits, drafts));
+    if ((target == nullptr) != (n_ok == nullptr)) return fail(DFLASH_EINVAL, "target and n_ok go together");
+    hipStream_t s = (hipStream_t)stream;
+    if (s == nullptr) return fail(DFLASH_EINVAL, "graph capture needs a non-default stream");
+    hipStreamCaptureStatus st;
+    HIP_TRY(hipStreamIsCapturing(s, &st), "hipStreamIsCapturing");
+    if (st != hipStreamCaptureStatusNone) return fail(DFLASH_ESTATE, "stream is already capturing");
+    HIP_TRY(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+    int r = run_step(*x, rings, id_last, nullptr, n_past, B, logits, drafts, target, n_ok, s);
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamEndCapture(s, &graph);
+    if (r != DFLASH_OK) {
+        if (graph) hipGraphDestroy(graph);
+        return r;
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        hipGraphDestroy(graph);
+        return hip_fail(e, "hipGraphInstantiate");
+    }
+    dflash_graph *g = new dflash_graph();
+    g->ctx = x;
+    g->graph = graph;
+    g->exec = exec;
+    *out = g;
+    return DFLASH_OK;
+}
+
+int dflash_step_graph_launch(dflash_graph *g, void *stream) {
+    if (!g || !g->exec) return fail(DFLASH_EINVAL, "graph is NULL");
+    HIP_TRY(hipGraphLaunch(g->exec, (hipStream_t)stream), "hipGraphLaunch");
+    return DFLASH_OK;
+}
+
+void dflash_graph_destroy(dflash_graph *g) {
+    if (!g) return;
+    if (g->exec) hipGraphExecDestroy(g->exec);
+    if (g->graph) hipGraphDestroy(g->graph);
+    delete g;
+}
+
+int dflash_quantize_fp8_rows(const float *w, int32_t rows, int32_t cols, uint8_t *codes, float *scales, void *stream) {
+    if (!w || !codes || !scales) return fail(DFLASH_EINVAL, "a pointer is NULL");
+    if (rows < 1 || cols < 1) return fail(DFLASH_EINVAL, "rows and cols must be positive");
+    HIP_TRY(launch_quantize_fp8(w, rows, cols, codes, scales, (hipStream_t)stream), "quantize launch");
+    return DFLASH_OK;
+}
+
+}  // extern "C"

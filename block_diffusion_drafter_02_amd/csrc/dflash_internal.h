@@ -1,0 +1,268 @@
+// Internal declarations of the DFlash HIP library: device helpers, the weight
+// tiling, the context layout and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/dflash.h"
+
+// ---------------------------------------------------------------------------
+// Tiling of streamed weights
+// ---------------------------------------------------------------------------
+// Every matrix the step streams is re-tiled once at create time so that one
+// wavefront load of a tile is a single contiguous run of memory.
+//
+// A tile covers 16 output rows x 64 reduction columns (one "k-block"). Lane
+// l (0..63) of a wavefront owns row (l % 16) and the 16 consecutive columns
+// starting at 16 * (l / 16); the tile stores lane 0's 16 elements, then lane
+// 1's, and so on. Four tiles side by side (64 output rows) form a column
+// group; memory order is [group][k-block][tile 0..3][lane][16 elements].
+//
+// The MFMA 16x16x32 bf16 operands take 8 reduction elements per lane, so a
+// lane's 16 elements feed two MFMAs; for f32 weights they feed sixteen
+// 16x16x4 f32 MFMAs. Because the A (activation) operand is loaded with the same
+// lane -> (row, columns) map, any permutation of the reduction index inside a
+// k-block cancels out.
+constexpr int TILE_N = 16;
+constexpr int KBLK = 64;
+constexpr int TILES_PER_GROUP = 4;
+constexpr int GROUP_N = TILE_N * TILES_PER_GROUP;  // 64 output columns per group
+constexpr int LANE_ELEMS = 16;
+
+// element offset of weight (n, k) in a tiled matrix with KB = K / 64 k-blocks
+__host__ __device__ inline size_t tiled_offset(int n, int k, int KB) {
+    int g = n / GROUP_N, t = (n / TILE_N) % TILES_PER_GROUP, r = n % TILE_N;
+    int kb = k / KBLK, c = (k % KBLK) / LANE_ELEMS, j = k % LANE_ELEMS;
+    int lane = r + 16 * c;
+    return ((((size_t)g * KB + kb) * TILES_PER_GROUP + t) * 64 + lane) * LANE_ELEMS + j;
+}
+
+// ---------------------------------------------------------------------------
+// Scalar conversions (device)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// float -> bfloat16, round to nearest even (finite inputs; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Exact three-term split v = t0 + t1 + t2 with each term a bfloat16. Each
+// subtraction is exact (Sterbenz: the operands agree to within a factor of
+// two), and the last remainder has at most 8 significant bits, so the three
+// bf16 products with a bf16 weight reproduce the fp32 product exactly.
+__device__ __forceinline__ void split3(float v, uint16_t &t0, uint16_t &t1, uint16_t &t2) {
+    t0 = f32_to_bf16(v);
+    float r = v - bf16_to_f32(t0);
+    t1 = f32_to_bf16(r);
+    r = r - bf16_to_f32(t1);
+    t2 = f32_to_bf16(r);
+}
+
+// E4M3FN code -> bfloat16 bits (exact: 3 mantissa bits and exponents
+// 2^-9 .. 2^8 all fit bf16). The NaN code is not supported.
+__device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
+    uint32_t s = (c & 0x80u) << 8;
+    uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    if (e == 0) {
+        if (m == 0) return (uint16_t)s;
+        int p = 31 - __clz(m);  // m = 2^p * (1 + f), value m * 2^-9
+        return (uint16_t)(s | ((uint32_t)(p - 9 + 127) << 7) | ((m << (7 - p)) & 0x7Fu));
+    }
+    return (uint16_t)(s | ((e + 120u) << 7) | (m << 4));
+}
+
+// fp32 -> E4M3FN code, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t s = (u >> 24) & 0x80u;
+    float a = fabsf(v);
+    if (!(a < 448.0f)) return (uint8_t)(s | 0x7Eu);  // >= 448 (and NaN) saturate
+    if (a >= 0.015625f) {                             // normal: keep 3 mantissa bits
+        uint32_t au = u & 0x7fffffffu;
+        au += 0x7ffffu + ((au >> 20) & 1u);
+        au &= 0xfff00000u;
+        if (__uint_as_float(au) > 448.0f) return (uint8_t)(s | 0x7Eu);
+        int e = (int)(au >> 23) - 127;
+        return (uint8_t)(s | ((uint32_t)(e + 7) << 3) | ((au >> 20) & 7u));
+    }
+    float q = rintf(a * 512.0f);  // subnormal quantum 2^-9; q == 8 is the smallest normal
+    return (uint8_t)(s | (uint32_t)q);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_f32(const T *p, size_t i);
+template <>
+__device__ __forceinline__ float load_f32<float>(const float *p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_f32<uint16_t>(const uint16_t *p, size_t i) { return bf16_to_f32(p[i]); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Activation formats for the weight-streaming kernels
+// ---------------------------------------------------------------------------
+// ACT_SPLIT3: bf16 [3][Mrows][K] (exact three-term split of fp32 values), used
+//             with bf16 and fp8 weights.
+// ACT_F32:    f32 [Mrows][K], used with f32 weights (f32 MFMA).
+// ACT_BF16:   bf16 [Mrows][K] holding exact values (features already bf16).
+enum ActFmt { ACT_SPLIT3 = 0, ACT_F32 = 1, ACT_BF16 = 2 };
+
+// ---------------------------------------------------------------------------
+// Epilogues of the split-K weight-streaming kernel
+// ---------------------------------------------------------------------------
+enum EpiKind { EPI_SCALED = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+struct EpiArgs {
+    int kind;
+    int M;                // live rows (16 * B)
+    const float *wscale;  // fp8 per-column scales in tiled column order, or null
+    // row normalisation folded into the consumer: rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps)
+    const float *ss;      // [ss_groups][Mstride] partial sums of squares, or null
+    int ss_groups;
+    int ss_stride;        // Mstride of ss
+    float inv_E, eps;
+    // EPI_SCALED / EPI_LOGITS output [M][ld_out]
+    float *out;
+    int ld_out;
+    // EPI_RESID: residual stream x [M][ld_x] updated in place; next activation
+    float *x;
+    int ld_x;
+    const float *wnext;   // next norm weight [E]
+    void *act_out;        // next activation (format act_fmt, K = ld_x or F)
+    int act_fmt;
+    int act_rows;         // row stride of act_out (Mmax)
+    int act_K;
+    float *ss_out;        // [G][ss_stride] sums of squares of the updated x
+    // EPI_LOGITS: argmax across groups
+    float *am_val;
+    int *am_idx;
+    int *am_counter;
+    int32_t *drafts;      // [B][block-1]
+    const int32_t *target;  // [B][block-1] or null
+    int32_t *n_ok;        // [B] or null
+    int block;
+};
+
+struct GemvArgs {
+    const void *W;  // tiled weights
+    int N, K;       // output columns (multiple of 64), reduction length (multiple of 64)
+    const void *act;
+    int act_rows;   // row stride of the activation terms (>= M)
+    int S;          // k-splits
+    int kb_per_split;
+    float *partial; // [S][G][Mp][64]
+    int *counters;  // [G], zero between launches
+    EpiArgs epi;
+};
+
+struct GemmArgs {
+    const void *W;  // tiled weights [N, K]
+    const float *wscale;
+    int N, K, M;
+    const void *act;
+    int act_rows;   // row stride between terms (for ACT_SPLIT3)
+    float *out;     // [M][N] f32
+};
+
+// ---------------------------------------------------------------------------
+// Context
+// ---------------------------------------------------------------------------
+struct LayerBufs {
+    void *qkv, *o, *gu, *down;           // tiled weights
+    float *s_qkv, *s_o, *s_gu, *s_down;  // fp8 scales in tiled column order (or null)
+};
+
+struct dflash_ctx {
+    dflash_config cfg;
+    int device;
+    int E, H, Hkv, D, F, W, L, V, C, qdim, kvdim, nqkv, Mmax, G_E, NCH;
+    int act_fmt;       // activation format of the step GEMVs
+    size_t wbytes_el;  // bytes per streamed weight element (4, 2, 1)
+    char *ws;
+    size_t ws_bytes;
+    // fixed tables and weights
+    double *inv_freq;
+    float *hidden_norm, *output_norm;
+    void *fc;      // tiled [E, C]
+    void *kv;      // tiled [L*2*kvdim, E], rows [K0; V0; K1; V1; ...]
+    float *s_kv;
+    void *lm;
+    float *s_lm;
+    LayerBufs layer[16];
+    // fp32 copies of the norm vectors, one contiguous array per family
+    float *attn_norm;   // [L][E]
+    float *ffn_norm;    // [L][E]
+    float *q_norm;      // [L][D]
+    float *k_norm;      // [L][D]
+    const void *tok_embd;
+    // step buffers
+    float *x;           // [Mmax][E]
+    void *act_a;        // attention-norm input (x * attn_norm), format act_fmt, [.][Mmax][E]
+    void *act_f;        // ffn-norm input
+    void *act_d;        // SwiGLU output [.][Mmax][F]
+    void *act_o;        // attention output [.][Mmax][qdim]
+    float *ss_a, *ss_f; // [G_E][Mmax]
+    float *qkv_out;     // [Mmax][nqkv]
+    float *rope_cs;     // [max_batch][block][D/2][2]
+    float *att_ml;      // [max_batch][Hkv][NCH+1][G*16][2]
+    float *att_o;       // [max_batch][Hkv][NCH+1][G*16][D]
+    float *partial;
+    size_t partial_floats;
+    int *counters;
+    int n_counters;
+    float *am_val;
+    int *am_idx;
+    int *am_counter;
+    int32_t *ids;       // [Mmax] block ids
+    // encode / inject buffers
+    float *enc_y;       // [max_inject][E]
+    void *enc_act;      // features converted for the fc GEMM (if needed)
+    void *inj_act;      // h converted for the kv GEMM (if needed)
+    float *inj_kv;      // [max_inject][L*2*kvdim]
+};
+
+struct dflash_graph {
+    dflash_ctx *ctx;
+    hipGraph_t graph;
+    hipGraphExec_t exec;
+};
+
+// ---------------------------------------------------------------------------
+// Launchers (kernels_*.hip)
+// ---------------------------------------------------------------------------
+hipError_t launch_tile_weights(const void *src, int src_rows, int K, int esize, void *dst, int KB, int row_map,
+                               int dst_row0, int pair_half, hipStream_t s);
+hipError_t launch_tile_scales(const float *src, int src_rows, float *dst, int row_map, int dst_row0, int pair_half,
+                              hipStream_t s);
+hipError_t launch_vec_to_f32(const void *src, int dtype, int n, float *dst, hipStream_t s);
+hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t s);
+hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *codes, float *scales, hipStream_t s);
+hipError_t launch_gemv(int wdtype, int act_fmt, int MT, dim3 grid, const GemvArgs &a, hipStream_t s);
+hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s);
+hipError_t launch_split(const float *src, int rows, int K, int ld_src, void *dst, int act_fmt, int act_rows,
+                        hipStream_t s);
+hipError_t launch_bf16_to_f32(const uint16_t *src, size_t n, float *dst, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const float *y, int T, int E, const float *w, float eps, float *h, hipStream_t s);
+hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, int T, hipStream_t s);
+hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32_t *block_ids, const int32_t *n_past,
+                        int B, hipStream_t s);
+hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, const int32_t *n_past, int B,
+                            hipStream_t s);
+hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, int n, int32_t *n_ok, hipStream_t s);
+
+// ring layout helpers (host and device)
+__host__ __device__ inline size_t ring_kv_elems(int L, int Hkv, int W, int D) { return (size_t)L * Hkv * W * D; }

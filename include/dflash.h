@@ -1,0 +1,201 @@
+/*
+ * dflash.h -- C ABI of the DFlash block-diffusion drafter block step for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations follow the dflash-ops card (Hugging Face kernels hub):
+ *   - "Usage": encode fused target features, inject them into the ring,
+ *     run the graphed block step on [id_last, mask x 15], take greedy
+ *     drafts at block positions 1..15, and count accepted drafts on the device;
+ *   - "Method": injection through wk/wv with no attention norm, K per-head
+ *     RMS-normed and NEOX-roped, V raw; non-causal block attention; the window
+ *     masks only the deep past (0 <= qpos - kpos < window); rope angles from a
+ *     host fp64 inverse-frequency table; fp32 arithmetic whatever the storage
+ *     dtype; the captured step allocates nothing;
+ *   - "Requirements and limits": slot = pos % window, at most window tokens
+ *     per inject call, later calls overwrite.
+ * The cross-sequence batch (sequence-major rows, weight GEMMs once over all
+ * rows, attention / slot writes / acceptance per sequence) follows the metrale
+ * dflash_head.rs page, DflashBatch; weight-only FP8 E4M3 with per-row f32
+ * scales follows its DflashQuantization.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers unless the comment says "host".
+ *   - `stream` is a hipStream_t (passed as void* so this header needs no HIP
+ *     include). Every call is asynchronous on that stream; nothing is
+ *     allocated; no host synchronisation happens except where stated.
+ *   - The caller owns all memory: weights, workspace, rings, inputs, outputs.
+ *   - Host-checkable errors return a negative dflash_status before any launch
+ *     and leave a message for dflash_last_error() (thread-local).
+ *   - Matrices are row-major [out, in] (the PyTorch / GGUF order); vectors are
+ *     dense.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DFLASH_OK = 0,
+    DFLASH_EINVAL = -1,       /* NULL pointer, bad dtype, inconsistent shape */
+    DFLASH_ERANGE = -2,       /* T > window or T > max_inject, B > max_batch, buffer too small */
+    DFLASH_EUNSUPPORTED = -3, /* a shape the kernels do not support (see dflash_config) */
+    DFLASH_EHIP = -4,         /* a HIP runtime call failed; the message names it */
+    DFLASH_ESTATE = -5        /* object used in the wrong state (e.g. capture already active) */
+} dflash_status;
+
+typedef enum {
+    DFLASH_F32 = 0,
+    DFLASH_BF16 = 1,
+    DFLASH_FP8_E4M3 = 2 /* OCP E4M3FN (max 448, no infinities); NaN codes are not supported */
+} dflash_dtype;
+
+/*
+ * Drafter geometry and storage dtypes.
+ *
+ * Supported shapes: head_dim 64 or 128; n_head a multiple of n_head_kv with
+ * n_head / n_head_kv <= 8; block == 16; n_embd, n_ff, n_vocab,
+ * n_capture * target_hidden, n_head * head_dim and n_head_kv * head_dim
+ * multiples of 64; window a multiple of 64 and <= 65536; 1 <= max_batch <= 8.
+ */
+typedef struct dflash_config {
+    int32_t n_layer;       /* drafter layers (5 for the released drafter) */
+    int32_t n_embd;        /* drafter hidden size E */
+    int32_t n_head;        /* query heads */
+    int32_t n_head_kv;     /* key/value heads (GQA: q head h uses kv head h / (n_head / n_head_kv)) */
+    int32_t head_dim;      /* D; rope covers the whole head */
+    int32_t n_ff;          /* SwiGLU width F */
+    int32_t window;        /* ring slots W per layer */
+    int32_t block;         /* noise block length (16) */
+    int32_t n_vocab;       /* rows of tok_embd and lm_head */
+    int32_t n_capture;     /* captured target layers (5) */
+    int32_t target_hidden; /* target hidden size; fused features are [T, n_capture * target_hidden] */
+    int32_t mask_id;       /* token id of the 15 mask positions */
+    int32_t max_batch;     /* largest B passed to the block step */
+    int32_t max_inject;    /* largest T passed to encode / inject (<= window for inject) */
+    float rms_eps;         /* RMSNorm epsilon (1e-6) */
+    double rope_base;      /* rope theta; inverse frequencies base^(-2i/D) are built in fp64 on the host */
+    int32_t weight_dtype;  /* wq wk wv wo w_gate w_up w_down lm_head: F32, BF16 or FP8_E4M3 */
+    int32_t aux_dtype;     /* tok_embd, fc and every norm vector: F32 or BF16 */
+    int32_t ring_dtype;    /* ring K/V storage: F32 or BF16 */
+    int32_t feature_dtype; /* fused target features: F32 or BF16 */
+} dflash_config;
+
+/* One layer's weights (metrale dflash_head.rs page, DflashLayer; no biases).
+ * Matrices: wq [H*D, E], wk/wv [Hkv*D, E], wo [E, H*D], w_gate/w_up [F, E],
+ * w_down [E, F], in weight_dtype. Norm vectors (aux_dtype): attn_norm [E],
+ * q_norm/k_norm [D], ffn_norm [E]. s_*: FP8 per-row scales [rows] (f32),
+ * required when weight_dtype is FP8_E4M3 and ignored otherwise. */
+typedef struct dflash_layer_weights {
+    const void *attn_norm, *wq, *wk, *wv, *wo, *q_norm, *k_norm, *ffn_norm, *w_gate, *w_up, *w_down;
+    const float *s_q, *s_k, *s_v, *s_o, *s_gate, *s_up, *s_down;
+} dflash_layer_weights;
+
+/* Global weights. tok_embd [V, E] (aux_dtype) and lm_head [V, E]
+ * (weight_dtype, scales s_lm_head for FP8) are the target model's; fc
+ * [E, n_capture*target_hidden], hidden_norm [E] and output_norm [E] are the
+ * drafter's (aux_dtype). `layers` is a HOST array of n_layer entries. */
+typedef struct dflash_weights {
+    const void *tok_embd, *lm_head, *fc, *hidden_norm, *output_norm;
+    const float *s_lm_head;
+    const dflash_layer_weights *layers;
+} dflash_weights;
+
+typedef struct dflash_ctx dflash_ctx;
+typedef struct dflash_graph dflash_graph;
+
+/* Bytes of device workspace dflash_create needs for `cfg`, or 0 if cfg is
+ * invalid (dflash_last_error says why). The workspace holds the re-tiled
+ * copies of every weight matrix the kernels stream, fp32 copies of the norm
+ * vectors, the fp64 inverse-frequency table and every intermediate of
+ * encode / inject / block step. It must be 256-byte aligned. */
+size_t dflash_workspace_bytes(const dflash_config *cfg);
+
+/* Bytes of one sequence's ring: K and V [n_layer][n_kv][window][head_dim] in
+ * ring_dtype, then int32 slot_pos[window] (the position each slot holds, -1
+ * when empty). 256-byte alignment required. */
+size_t dflash_ring_bytes(const dflash_config *cfg);
+
+/* Validate cfg, carve the caller's workspace and, on `stream`, re-tile every
+ * weight matrix into it (the streaming layout of the step kernels) and copy
+ * the norm vectors as fp32. The inverse-frequency table is computed on the
+ * host in fp64 and uploaded with a synchronous copy. After the stream has
+ * drained, the library reads only tok_embd from `w`; every other weight
+ * buffer may be freed. *out receives a host handle; free it with
+ * dflash_destroy. The handle may be used from one host thread at a time. */
+int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *workspace, size_t workspace_bytes,
+                  void *stream, dflash_ctx **out);
+void dflash_destroy(dflash_ctx *ctx);
+
+/* Mark every slot of `ring` empty (slot_pos[] = -1). K/V contents are left
+ * as they are; empty slots are never attended. */
+int dflash_ring_reset(dflash_ctx *ctx, void *ring, void *stream);
+
+/* Cross-layer feature fusion (dflash_engine.py page, TargetContextFeatureFuser):
+ * h = RMSNorm(feats . fc^T) * hidden_norm. feats [T, n_capture*target_hidden]
+ * in feature_dtype, h [T, n_embd] f32. 1 <= T <= max_inject. */
+int dflash_encode(dflash_ctx *ctx, const void *feats, int32_t T, float *h, void *stream);
+
+/* KV injection (dflash-ops card, Method; Requirements and limits): for every
+ * layer l, position t and kv head j, k = rope(RMSNorm(h_t . wk_l^T)[j] *
+ * k_norm_l, pos_t) and v = (h_t . wv_l^T)[j], rounded to ring_dtype and stored
+ * at slot pos_t % window; slot_pos[slot] = pos_t. h [T, n_embd] f32, pos [T]
+ * int32. 1 <= T <= min(window, max_inject). Device preconditions (not
+ * checked): positions of one call map to distinct slots; a negative position
+ * is skipped. */
+int dflash_inject(dflash_ctx *ctx, void *ring, const float *h, const int32_t *pos, int32_t T, void *stream);
+
+/* The drafter block step for B sequences (rows sequence-major, 16 per
+ * sequence). rings: device array [B] of ring pointers; id_last [B] and
+ * n_past [B] int32 (device, so a graph replays with fresh values). Block row
+ * i of sequence b holds [id_last, mask...][i] at position n_past[b] + i and
+ * attends non-causally to all 16 block rows and to the ring slots with
+ * 0 <= n_past[b] + i - slot_pos < window. Outputs logits [16*B, n_vocab] f32
+ * and drafts [B, 15] int32 = argmax of rows 1..15 (ties to the lowest
+ * index). Ids outside [0, n_vocab) embed as zero vectors. 1 <= B <= max_batch. */
+int dflash_block_step(dflash_ctx *ctx, void *const *rings, const int32_t *id_last, const int32_t *n_past, int32_t B,
+                      float *logits, int32_t *drafts, void *stream);
+
+/* As dflash_block_step but with explicit block ids [B, 16] (device) instead
+ * of id_last: a hook for testing joint (non-causal) denoising. */
+int dflash_block_forward(dflash_ctx *ctx, void *const *rings, const int32_t *block_ids, const int32_t *n_past,
+                         int32_t B, float *logits, int32_t *drafts, void *stream);
+
+/* First-mismatch acceptance (dflash-ops card, Usage; dflash_engine.py page,
+ * DFlashSpeculativeVerifier.verify_block): n_ok[b] = number of leading i with
+ * drafts[b][i] == target[b][i], in 0..15. drafts, target [B, 15] int32. */
+int dflash_accept(dflash_ctx *ctx, const int32_t *drafts, const int32_t *target, int32_t B, int32_t *n_ok,
+                  void *stream);
+
+/* Capture the block step (and, when target and n_ok are non-NULL, the
+ * acceptance scan) for fixed pointers into a HIP graph by stream capture on
+ * `stream`. Nothing is allocated inside the capture; every intermediate
+ * lives in the workspace. Replay with dflash_step_graph_launch after writing
+ * fresh values into id_last / n_past / target. The graph reads the ctx's
+ * workspace, so the ctx must outlive it and no other call on the same ctx may
+ * overlap a replay. */
+int dflash_step_graph_create(dflash_ctx *ctx, void *const *rings, const int32_t *id_last, const int32_t *n_past,
+                             int32_t B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
+                             void *stream, dflash_graph **out);
+int dflash_step_graph_launch(dflash_graph *g, void *stream);
+void dflash_graph_destroy(dflash_graph *g);
+
+/* Weight-only FP8 (metrale dflash_head.rs page, DflashQuantization): for
+ * each row r of w [rows, cols] f32, scales[r] = amax_r / 448 (1 for an
+ * all-zero row) and codes[r][c] = E4M3FN(w[r][c] / scales[r]), rounded to
+ * nearest even and saturated at +-448; both divisions in IEEE fp32. */
+int dflash_quantize_fp8_rows(const float *w, int32_t rows, int32_t cols, uint8_t *codes, float *scales,
+                             void *stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *dflash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

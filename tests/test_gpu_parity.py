@@ -1,0 +1,266 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Sizes here finish in seconds on the oracle yet span several column groups, the
+split-K path, ragged batches, partially filled and wrapped rings, and every
+storage dtype. Bars (written below): bit-exact slot tables, drafts and
+acceptance counts; logits within 1e-4 absolute for fp32 storage and 2e-2 of
+the oracle logits' standard deviation for bf16 / fp8 storage; ring values
+within 1e-5 (fp32) or one bf16 ulp plus that fp32 allowance (a value that
+cancels to near zero can differ by fp32 rounding alone).
+"""
+import numpy as np
+import pytest
+
+from block_diffusion_drafter_02_amd import synth
+from oracle import dflash_oracle as O
+from tests import workload as WL
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _build(spec, n_ctx, max_batch=1, chunk=None, feats_seed_tag="feats"):
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
+
+    shape = spec.shape
+    chunk = chunk or min(shape.window, 64)
+    raw = synth.weights(shape, spec.weight_dtype, seed=spec.seed)
+    feats = synth.features(shape, n_ctx, spec.feature_dtype, seed=spec.seed, tag=feats_seed_tag)
+    positions = np.arange(n_ctx, dtype=np.int64)
+    dr = Drafter(shape, raw, spec.weight_dtype, spec.ring_dtype, spec.feature_dtype, max_batch=max_batch,
+                 max_inject=chunk)
+    ring = dr.new_ring()
+    fdev = to_device(feats, dr.device)
+    WL.gpu_inject(dr, ring, fdev, positions, chunk)
+    torch.cuda.synchronize()
+    ocfg, ow, oring = WL.oracle_side(spec, raw, feats, positions, chunk)
+    return dr, ring, fdev, (ocfg, ow, oring), raw, feats
+
+
+def _step(dr, rings, id_last, n_past):
+    torch = _torch()
+    table = dr.ring_table(rings)
+    il = torch.tensor(id_last, dtype=torch.int32, device=dr.device)
+    npst = torch.tensor(n_past, dtype=torch.int32, device=dr.device)
+    logits, drafts = dr.block_step(table, il, npst)
+    torch.cuda.synchronize()
+    return logits.cpu().numpy().astype(np.float64), drafts.cpu().numpy()
+
+
+def _check_ring(dr, ring, oring, spec):
+    torch = _torch()
+    K, V, sp = dr.ring_views(ring)
+    np.testing.assert_array_equal(sp.cpu().numpy(), oring.slot_pos.astype(np.int32))
+    w = oring.written
+    Kg = K.float().cpu().numpy().astype(np.float64)[:, :, w]
+    Vg = V.float().cpu().numpy().astype(np.float64)[:, :, w]
+    Ko, Vo = oring.K[:, :, w], oring.V[:, :, w]
+    if spec.ring_dtype == "f32":
+        assert np.abs(Kg - Ko).max() <= WL.RING_ABS_F32
+        assert np.abs(Vg - Vo).max() <= WL.RING_ABS_F32
+    else:
+        # the fp32 values agree to RING_ABS_F32; rounding both to bf16 adds at most one bf16 ulp
+        assert np.all(np.abs(Kg - Ko) <= WL.bf16_ulp(Ko) + WL.RING_ABS_F32)
+        assert np.all(np.abs(Vg - Vo) <= WL.bf16_ulp(Vo) + WL.RING_ABS_F32)
+    del torch
+
+
+def _check_logits(spec, ref, got, label=""):
+    tol = WL.logit_tol(spec, ref)
+    err = np.abs(got - ref).max()
+    assert err <= tol, f"{label} logits max-abs {err:.3g} > {tol:.3g}"
+    return tol
+
+
+SPECS = [
+    WL.Spec(synth.TINY, "f32", "f32", "f32"),
+    WL.Spec(synth.TINY, "bf16", "bf16", "bf16"),
+    WL.Spec(synth.TINY, "fp8", "bf16", "bf16"),
+    WL.Spec(WL.MEDIUM, "f32", "f32", "f32"),
+    WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16"),
+    WL.Spec(WL.MEDIUM, "fp8", "bf16", "bf16"),
+]
+
+
+def _spec_id(s):
+    return f"{'tiny' if s.shape is synth.TINY else 'medium'}-{s.weight_dtype}-{s.ring_dtype}"
+
+
+@pytest.mark.parametrize("spec", SPECS, ids=_spec_id)
+def test_encode_inject_and_block_step_match_oracle(gpu, spec):
+    torch = _torch()
+    n_ctx = spec.shape.window + 16  # the ring wraps: the first 16 slots are overwritten
+    dr, ring, fdev, (ocfg, ow, oring), raw, feats = _build(spec, n_ctx)
+    print(f"[case] {_spec_id(spec)} n_ctx={n_ctx}", flush=True)
+    # encode of the last chunk against the oracle's encode of the same rows
+    last = slice(n_ctx - 16, n_ctx)
+    h = dr.encode(fdev[last]).cpu().numpy().astype(np.float64)
+    h_ref = O.encode(ocfg, ow, feats[last])
+    assert np.abs(h - h_ref).max() <= 2e-5 * max(1.0, np.abs(h_ref).max())
+    _check_ring(dr, ring, oring, spec)
+    st = synth.step_inputs(spec.shape, 1, seed=3)
+    logits, drafts = _step(dr, [ring], st["id_last"], [n_ctx])
+    ref = O.block_forward(ocfg, ow, oring, O.block_ids(ocfg, int(st["id_last"][0])), n_ctx)
+    tol = _check_logits(spec, ref, logits)
+    bad, ties = WL.compare_drafts(ref, drafts[0], tol)
+    assert not bad, f"draft mismatches at rows {bad} (near ties {ties})"
+    # acceptance with a planted mismatch built from the oracle's drafts
+    odr = O.greedy_drafts(ref)
+    tgt = synth.planted_targets(odr[None], st["mismatch"], st["filler"], spec.shape.n_vocab)
+    n_ok = dr.accept(torch.from_numpy(drafts).to(dr.device), torch.from_numpy(tgt).to(dr.device))
+    if not ties:
+        assert int(n_ok.cpu()[0]) == int(st["mismatch"][0]) == O.accept(odr, tgt[0])
+
+
+def test_batch_of_ragged_sequences_matches_per_sequence_oracle(gpu):
+    """B = 3 sequences (rows sequence-major): a partial ring, an exactly full ring, a wrapped ring."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
+
+    spec = WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16")
+    shape = spec.shape
+    raw = synth.weights(shape, "bf16", seed=0)
+    dr = Drafter(shape, raw, "bf16", "bf16", "bf16", max_batch=3, max_inject=128)
+    n_pasts = [40, 256, 300]
+    rings, orings = [], []
+    for b, n in enumerate(n_pasts):
+        feats = synth.features(shape, n, "bf16", seed=0, tag=f"feats{b}")
+        pos = np.arange(n, dtype=np.int64)
+        r = dr.new_ring()
+        WL.gpu_inject(dr, r, to_device(feats, dr.device), pos, 128)
+        rings.append(r)
+        orings.append(WL.oracle_side(spec, raw, feats, pos, 128))
+    st = synth.step_inputs(shape, 3, seed=7)
+    print("[case] batch B=3 n_past=", n_pasts, flush=True)
+    logits, drafts = _step(dr, rings, st["id_last"], n_pasts)
+    for b, n in enumerate(n_pasts):
+        ocfg, ow, oring = orings[b]
+        ref = O.block_forward(ocfg, ow, oring, O.block_ids(ocfg, int(st["id_last"][b])), n)
+        got = logits[16 * b:16 * (b + 1)]
+        tol = _check_logits(spec, ref, got, label=f"seq{b}")
+        bad, ties = WL.compare_drafts(ref, drafts[b], tol)
+        assert not bad, (b, bad, ties)
+    del torch
+
+
+def test_window_masking_by_perturbing_ring_slots(gpu):
+    """1-layer tiny drafter, n_past 80: a slot holding position p is visible to rows i <= p - 17 only."""
+    torch = _torch()
+    spec = WL.Spec(synth.TINY, "f32", "f32", "f32")
+    dr, ring, fdev, _, raw, feats = _build(spec, 80)
+    base_l, _ = _step(dr, [ring], [123], [80])
+    K, V, sp = dr.ring_views(ring)
+    for p in (20, 30, 79):
+        r2 = ring.clone()
+        K2, V2, _ = dr.ring_views(r2)
+        K2[:, :, p % 64] += 0.5
+        V2[:, :, p % 64] -= 0.5
+        got, _ = _step(dr, [r2], [123], [80])
+        for i in range(16):
+            if i <= p - 17:
+                assert np.abs(got[i] - base_l[i]).max() > 1e-6, (p, i)
+            else:
+                np.testing.assert_array_equal(got[i], base_l[i])
+    # a slot no row can see (position 16) and an empty ring slot change nothing
+    r3 = ring.clone()
+    K3, _, sp3 = dr.ring_views(r3)
+    assert int(sp3[16]) == 16
+    K3[:, :, 16] += 3.0
+    got, _ = _step(dr, [r3], [123], [80])
+    np.testing.assert_array_equal(got, base_l)
+    del torch
+
+
+def test_block_attention_is_non_causal(gpu):
+    torch = _torch()
+    spec = WL.Spec(synth.TINY, "f32", "f32", "f32")
+    dr, ring, fdev, (ocfg, ow, oring), raw, feats = _build(spec, 80)
+    table = dr.ring_table([ring])
+    npst = torch.tensor([80], dtype=torch.int32, device=dr.device)
+    ids = O.block_ids(ocfg, 11)
+    ids2 = ids.copy()
+    ids2[15] = 77
+    l1, _ = dr.block_forward(table, torch.tensor(ids[None], dtype=torch.int32, device=dr.device), npst)
+    l2, _ = dr.block_forward(table, torch.tensor(ids2[None], dtype=torch.int32, device=dr.device), npst)
+    l1, l2 = l1.cpu().numpy(), l2.cpu().numpy()
+    assert np.all(np.abs(l2[:15] - l1[:15]).max(axis=1) > 1e-6)
+    ref2 = O.block_forward(ocfg, ow, oring, ids2, 80)
+    _check_logits(spec, ref2, l2.astype(np.float64))
+
+
+def test_graph_replay_is_bitwise_equal_to_eager_with_interleaved_traffic(gpu):
+    torch = _torch()
+    spec = WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16")
+    dr, ring, fdev, _, raw, feats = _build(spec, 300)
+    table = dr.ring_table([ring])
+    il = torch.tensor([5], dtype=torch.int32, device=dr.device)
+    npst = torch.tensor([300], dtype=torch.int32, device=dr.device)
+    e_logits, e_drafts = dr.block_step(table, il, npst)
+    e2_logits, e2_drafts = dr.block_step(table, il, npst)
+    torch.cuda.synchronize()
+    assert torch.equal(e_logits, e2_logits) and torch.equal(e_drafts, e2_drafts)  # determinism
+    logits = torch.empty_like(e_logits)
+    drafts = torch.empty_like(e_drafts)
+    target = e_drafts.clone()
+    target[0, 4] = (target[0, 4] + 1) % spec.shape.n_vocab
+    n_ok = torch.empty((1,), dtype=torch.int32, device=dr.device)
+    stream = torch.cuda.Stream()
+    g = dr.capture_step(table, il, npst, logits, drafts, target, n_ok, stream=stream)
+    for rep in range(4):
+        with torch.cuda.stream(stream):
+            g.launch(stream)
+        stream.synchronize()
+        assert torch.equal(logits, e_logits), rep
+        assert torch.equal(drafts, e_drafts), rep
+        assert int(n_ok.cpu()[0]) == 4
+        # eager traffic between replays: allocations, frees and another eager step
+        junk = torch.randn(1 << 20, device=dr.device) * 3
+        del junk
+        dr.block_step(table, torch.tensor([9], dtype=torch.int32, device=dr.device), npst)
+        torch.cuda.synchronize()
+    # fresh inputs written into the static buffers change the replay like an eager step
+    il.fill_(9)
+    with torch.cuda.stream(stream):
+        g.launch(stream)
+    stream.synchronize()
+    ref9, _ = dr.block_step(table, il, npst)
+    torch.cuda.synchronize()
+    assert torch.equal(logits, ref9)
+    g.close()
+
+
+def test_fp8_quantisation_is_bit_exact(gpu):
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import quantize_fp8_rows
+
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((300, 1000)) / np.sqrt(1000)).astype(np.float32)
+    w[7] = 0.0
+    w[8, :5] = [1e-9, -1e-9, 3e-5, 448.0, -0.0]
+    codes, scales = quantize_fp8_rows(torch.from_numpy(w).cuda())
+    oc, osc = O.quantize_fp8_rows(w)
+    np.testing.assert_array_equal(scales.cpu().numpy(), osc)
+    np.testing.assert_array_equal(codes.cpu().numpy(), oc)
+
+
+def test_accept_scan_bruteforce(gpu):
+    torch = _torch()
+    spec = WL.Spec(synth.TINY, "f32", "f32", "f32")
+    from block_diffusion_drafter_02_amd.drafter import Drafter
+
+    dr = Drafter(spec.shape, synth.weights(spec.shape, "f32"), "f32", "f32", "f32", max_batch=8)
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        d = rng.integers(0, 512, (8, 15)).astype(np.int32)
+        m = rng.integers(0, 16, 8)
+        filler = rng.integers(0, 512, (8, 15))
+        t = synth.planted_targets(d, m, filler, 512)
+        n_ok = dr.accept(torch.from_numpy(d).cuda(), torch.from_numpy(t).cuda()).cpu().numpy()
+        np.testing.assert_array_equal(n_ok, [O.accept(d[b], t[b]) for b in range(8)])
+        np.testing.assert_array_equal(n_ok, m)

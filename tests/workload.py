@@ -1,0 +1,88 @@
+"""Shared helpers of the GPU parity tests: build one seeded workload on both sides and compare.
+
+The oracle side and the HIP side consume the same arrays from the synthetic
+generator; neither ever sees the other's outputs.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+from block_diffusion_drafter_02_amd import synth
+from oracle import dflash_oracle as O
+
+# tolerances (fp32 storage: absolute; bf16/fp8 storage: relative to the oracle logits' std)
+LOGIT_ABS_F32 = 1e-4
+LOGIT_REL_STD = 2e-2
+RING_ABS_F32 = 1e-5
+
+MEDIUM = synth.Shape(n_layer=2, n_embd=1024, n_head=8, n_head_kv=2, head_dim=128, n_ff=2048, window=256,
+                     block=16, n_vocab=1024, n_capture=5, target_hidden=256)
+
+
+@dataclasses.dataclass
+class Spec:
+    shape: synth.Shape
+    weight_dtype: str   # "f32", "bf16", "fp8"
+    ring_dtype: str     # "f32", "bf16"
+    feature_dtype: str  # "f32", "bf16"
+    seed: int = 0
+
+
+def chunks(positions: np.ndarray, size: int):
+    for c0 in range(0, len(positions), size):
+        yield positions[c0:c0 + size]
+
+
+def oracle_side(spec: Spec, raw: dict, feats: np.ndarray, positions: np.ndarray, chunk: int):
+    cfg = O.Config.from_shape(spec.shape, spec.ring_dtype)
+    w = O.Weights(raw, spec.weight_dtype)
+    ring = O.Ring(cfg)
+    row = {int(p): i for i, p in enumerate(positions)}
+    # every chunk is encoded and injected in order; later chunks overwrite earlier slots
+    for pc in chunks(positions, chunk):
+        idx = [row[int(p)] for p in pc]
+        h = O.encode(cfg, w, feats[idx])
+        O.inject(cfg, w, ring, h, pc)
+    return cfg, w, ring
+
+
+def gpu_inject(drafter, ring, feats_dev, positions: np.ndarray, chunk: int):
+    import torch
+
+    hs = []
+    for c0 in range(0, len(positions), chunk):
+        pc = positions[c0:c0 + chunk]
+        f = feats_dev[c0:c0 + len(pc)]
+        h = drafter.encode(f)
+        drafter.inject(ring, h, torch.from_numpy(pc.astype(np.int32)).to(drafter.device))
+        hs.append(h)
+    return hs
+
+
+def logit_tol(spec: Spec, ref: np.ndarray) -> float:
+    if spec.weight_dtype == "f32" and spec.ring_dtype == "f32":
+        return LOGIT_ABS_F32
+    return LOGIT_REL_STD * float(np.std(ref))
+
+
+def compare_drafts(ref_logits: np.ndarray, got_drafts: np.ndarray, tol: float):
+    """(exact mismatches, near ties): a mismatch at a row whose oracle top-2 gap is <= tol is a near tie."""
+    want = O.greedy_drafts(ref_logits)
+    bad, ties = [], []
+    for i, (w, g) in enumerate(zip(want, got_drafts)):
+        if int(w) == int(g):
+            continue
+        row = ref_logits[i + 1]
+        top2 = np.sort(row)[-2:]
+        if top2[1] - top2[0] <= tol and row[int(g)] >= top2[1] - tol:
+            ties.append(i)
+        else:
+            bad.append(i)
+    return bad, ties
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    _, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, e - 8)

@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the DFlash drafter block step on one MI355X.
+
+One step = one captured block step (embed, 5 drafter layers with ring + block
+attention, output norm, lm_head, greedy drafts) plus the device-side
+acceptance scan, on inputs already resident in HBM. Default workload: real
+drafter dimensions (5 layers, n_embd 6656, heads 32/8, head_dim 128, n_ff
+19968, window 2048, block 16, vocab 8192), bf16 weights and bf16 ring, ring full
+(positions 0..2047 injected), n_past 2048, a fresh id_last and target per step.
+
+Prints one JSON line: value = achieved HBM GB/s of the whole step (algorithmic
+bytes / step time), with the step time in ms_per_step and step_us, a roofline
+object for the dominant kernel (the gate/up GEMV) and the CPU oracle's rate
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "drafter block-step µs + achieved HBM GB/s (% of peak), real dims bf16, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "gate_up_gemv_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "block_diffusion_drafter_02_amd", "csrc", "kernels_weights.hip")
+
+WORKLOADS = {
+    # name: (weight dtype, ring dtype, feature dtype, batch, n_past list or None)
+    "bf16": ("bf16", "bf16", "bf16", 1),
+    "f32": ("f32", "f32", "f32", 1),
+    "bf16-batch8": ("bf16", "bf16", "bf16", 8),
+}
+
+
+def esize(dt: str) -> float:
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+
+
+def step_bytes(shape, wdt: str, rdt: str, n_vis: list[int]) -> dict:
+    """Algorithmic HBM bytes of one block step: every streamed weight once (plus fp8 row scales), the visible
+    ring K/V of every layer once per sequence, the norm vectors, the embedding rows, the logits."""
+    E, F, V, L = shape.n_embd, shape.n_ff, shape.n_vocab, shape.n_layer
+    qdim, kvdim = shape.q_dim, shape.kv_dim
+    per_layer = (qdim + 2 * kvdim) * E + E * qdim + 2 * F * E + E * F
+    w = (L * per_layer + V * E) * esize(wdt)
+    if wdt == "fp8":
+        w += (L * (qdim + 2 * kvdim + E + 2 * F + E) + V) * 4
+    aux = "f32" if wdt == "f32" else "bf16"
+    B = len(n_vis)
+    ring = sum(L * shape.n_head_kv * nv * shape.head_dim * 2 * esize(rdt) for nv in n_vis)
+    norms = (L * (2 * E + 2 * shape.head_dim) + E) * 4
+    embed = 16 * B * E * esize(aux)
+    logits = 16 * B * V * 4 + B * 15 * 4
+    return {"weights": w, "ring": ring, "other": norms + embed + logits, "total": w + ring + norms + embed + logits}
+
+
+def visible_slots(n_past: int, window: int, block: int) -> int:
+    """Ring slots visible to at least one block row when positions 0..n_past-1 were injected in order."""
+    lo = max(0, n_past - window)  # oldest position still held by the ring
+    # row 0 (position n_past) sees positions > n_past - window
+    return n_past - max(lo, n_past - window + 1)
+
+
+def kernel_src_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(bytes_per_launch_alg: float):
+    """HBM bytes per launch of the gate/up GEMV from committed rocprofv3 counter runs, or None when the kernel
+    source changed since they were taken."""
+    if not os.path.exists(COUNTERS):
+        return None
+    c = json.load(open(COUNTERS))
+    if c.get("kernel_src_sha256_16") != kernel_src_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes):
+    """The oracle, as it stands, for one block step of one sequence at the same dimensions on a synthetic ring
+    with the same fill; returns the rate in the metric's unit (algorithmic GB/s)."""
+    from oracle import dflash_oracle as O
+
+    cfg = O.Config.from_shape(shape, rdt)
+    w = O.Weights(raw, wdt)
+    ring = O.Ring(cfg)
+    rng = np.random.default_rng(0)
+    rnd = O.round_bf16 if rdt == "bf16" else O.round_f32
+    ring.K[:] = rnd(rng.standard_normal(ring.K.shape))
+    ring.V[:] = rnd(rng.standard_normal(ring.V.shape))
+    held = np.arange(max(0, n_past - cfg.window), n_past)
+    ring.slot_pos[held % cfg.window] = held
+    ring.written[held % cfg.window] = True
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    t0 = time.perf_counter()
+    O.block_forward(cfg, w, ring, O.block_ids(cfg, 1), n_past)
+    dt = time.perf_counter() - t0
+    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds_per_step": round(dt, 3),
+            "sample": f"one block step of one sequence (5 layers + lm_head) at the same dimensions and dtypes, "
+                      f"ring filled to n_past={n_past} with synthetic values (content does not change the cost)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=50)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    from block_diffusion_drafter_02_amd import _lib, synth
+    from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
+
+    wdt, rdt, fdt, B = WORKLOADS[args.workload]
+    shape = synth.REAL
+    t_setup = time.perf_counter()
+    print(f"[bench] generating {args.workload} weights", file=sys.stderr, flush=True)
+    raw = synth.weights(shape, wdt, seed=0)
+    if B == 1:
+        n_pasts = [2300] if wdt == "f32" else [2048]
+    else:
+        n_pasts = [int(v) for v in synth.batch_n_past(B, seed=0)]
+    dr = Drafter(shape, raw, wdt, rdt, fdt, max_batch=B, max_inject=shape.window)
+    print("[bench] injecting context", file=sys.stderr, flush=True)
+    rings = []
+    for b, n in enumerate(n_pasts):
+        ring = dr.new_ring()
+        first = max(0, n - (n // shape.window + 1) * shape.window) if wdt == "f32" else max(0, n - shape.window)
+        pos = np.arange(first, n, dtype=np.int32)
+        feats = to_device(synth.features(shape, len(pos), fdt, seed=0, tag=f"bench.feats{b}"), dr.device)
+        for c0 in range(0, len(pos), shape.window):
+            sl = slice(c0, c0 + shape.window)
+            h = dr.encode(feats[sl])
+            dr.inject(ring, h, torch.from_numpy(pos[sl]).to(dr.device))
+        del feats
+        rings.append(ring)
+    torch.cuda.synchronize()
+    table = dr.ring_table(rings)
+    n_vis = [visible_slots(n, shape.window, shape.block) for n in n_pasts]
+    nb = step_bytes(shape, wdt, rdt, n_vis)
+
+    K, W = args.steps, args.warmup
+    ids_all = torch.from_numpy(synth.integers(0, "bench.id_last", (W + K, B), 0, shape.n_vocab)).to(dr.device)
+    tgt_all = torch.from_numpy(synth.integers(0, "bench.target", (W + K, B, 15), 0, shape.n_vocab)).to(dr.device)
+    il = ids_all[0].clone()
+    npst = torch.tensor(n_pasts, dtype=torch.int32, device=dr.device)
+    logits = torch.empty((16 * B, shape.n_vocab), dtype=torch.float32, device=dr.device)
+    drafts = torch.empty((B, 15), dtype=torch.int32, device=dr.device)
+    target = tgt_all[0].clone()
+    n_ok = torch.empty((B,), dtype=torch.int32, device=dr.device)
+    stream = torch.cuda.Stream()
+    graph = dr.capture_step(table, il, npst, logits, drafts, target, n_ok, stream=stream)
+    setup_s = time.perf_counter() - t_setup
+
+    with torch.cuda.stream(stream):
+        def step(k):
+            il.copy_(ids_all[k])
+            target.copy_(tgt_all[k])
+            graph.launch(stream)
+
+        for k in range(W):
+            step(k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for k in range(K):
+            step(W + k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = e0.elapsed_time(e1) / K
+        # replays alone, without the per-step input refresh
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for k in range(K):
+            graph.launch(stream)
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+        # dominant kernel: the gate/up GEMV of layer 0, launched alone on the same stream
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(3):
+            dr.replay_stage(_lib.STAGE_GATE_UP, 0, stream)
+        r0.record(stream)
+        for _ in range(args.stage_reps):
+            dr.replay_stage(_lib.STAGE_GATE_UP, 0, stream)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        gu_ms = r0.elapsed_time(r1) / args.stage_reps
+
+    ms = wall * 1e3 / K
+    value = nb["total"] / (ms * 1e-3) / 1e9
+    E, F = shape.n_embd, shape.n_ff
+    gu_bytes = 2 * F * E * esize(wdt) + 16 * B * E * 4 + 16 * B * F * 4
+    if wdt == "fp8":
+        gu_bytes += 2 * F * 4
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    traffic = read_traffic(gu_bytes)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "step_us": round(ms * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "event_ms_per_step": round(ev_ms, 5),
+        "graph_only_ms_per_step": round(graph_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wdt == "f32" else "bf16x3-split/f32-accumulate",
+        "data": "synthetic (seeded N(0, 1/fan_in) weights, N(0,1) target features, uniform token ids)",
+        "config": {
+            "workload": f"DFlash drafter block step + acceptance, real dims (5 layers, n_embd 6656, heads 32/8, "
+                        f"head_dim 128, n_ff 19968, window 2048, block 16, vocab 8192), {wdt} weights, {rdt} ring, "
+                        f"batch {B}, n_past {n_pasts}",
+            "batch": B,
+            "algorithmic_bytes_per_step": nb["total"],
+            "weight_bytes_per_step": nb["weights"],
+            "ring_bytes_per_step": nb["ring"],
+        },
+        "roofline": {
+            "kernel": "gate/up GEMV + SwiGLU (layer 0)",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(gu_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": gu_bytes,
+        },
+        "setup_s": round(setup_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(shape, raw, wdt, rdt, n_pasts[0],
+                                            step_bytes(shape, wdt, rdt, n_vis[:1])["total"])
+    else:
+        line["cpu_baseline"] = None
+    graph.close()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -124,7 +124,7 @@ size_t carve(dflash_ctx &x, char *base) {
     x.lm = cv.take<void>(esw * (size_t)V * E);
     x.s_lm = fp8 ? cv.take<float>(4ull * V) : nullptr;
 
-    const int G_E = E / GROUP_N, G = c.n_head / c.n_head_kv, NCH = c.window / 64;
+    const int G_E = E / GROUP_N, G = c.n_head / c.n_head_kv, NCH = c.window / attn_chunk(c.ring_dtype, c.window);
     x.x = cv.take<float>(4ull * Mmax * E);
     x.act_a = cv.take<void>(act_es * Mmax * E);
     x.act_f = cv.take<void>(act_es * Mmax * E);
@@ -182,7 +182,7 @@ void derive(dflash_ctx &x) {
     x.nqkv = x.qdim + 2 * x.kvdim;
     x.Mmax = 16 * c.max_batch;
     x.G_E = x.E / GROUP_N;
-    x.NCH = x.W / 64;
+    x.NCH = x.W / attn_chunk(c.ring_dtype, x.W);
     x.act_fmt = c.weight_dtype == DFLASH_F32 ? ACT_F32 : ACT_SPLIT3;
     x.wbytes_el = dtype_bytes(c.weight_dtype);
 }
@@ -305,51 +305,56 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     return DFLASH_OK;
 }
 
-int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const int32_t *block_ids,
-             const int32_t *n_past, int B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
+int stage_qkv(const dflash_ctx &x, int l, int M, hipStream_t s) {
+    const LayerBufs &b = x.layer[l];
+    EpiArgs e = epi_base(x, EPI_SCALED, M);
+    e.wscale = b.s_qkv;
+    e.ss = x.ss_a;
+    e.ss_groups = x.G_E;
+    e.out = x.qkv_out;
+    e.ld_out = x.nqkv;
+    return gemv(x, b.qkv, x.nqkv, x.E, x.act_a, e, s);
+}
+
+int stage_o(const dflash_ctx &x, int l, int M, hipStream_t s) {
+    const LayerBufs &b = x.layer[l];
+    EpiArgs e = epi_base(x, EPI_RESID, M);
+    e.wscale = b.s_o;
+    e.x = x.x;
+    e.ld_x = x.E;
+    e.wnext = x.ffn_norm + (size_t)l * x.E;
+    e.act_out = x.act_f;
+    e.act_K = x.E;
+    e.ss_out = x.ss_f;
+    return gemv(x, b.o, x.E, x.qdim, x.act_o, e, s);
+}
+
+int stage_gu(const dflash_ctx &x, int l, int M, hipStream_t s) {
+    const LayerBufs &b = x.layer[l];
+    EpiArgs e = epi_base(x, EPI_SWIGLU, M);
+    e.wscale = b.s_gu;
+    e.ss = x.ss_f;
+    e.ss_groups = x.G_E;
+    e.act_out = x.act_d;
+    e.act_K = x.F;
+    return gemv(x, b.gu, 2 * x.F, x.E, x.act_f, e, s);
+}
+
+int stage_down(const dflash_ctx &x, int l, int M, hipStream_t s) {
+    const LayerBufs &b = x.layer[l];
+    EpiArgs e = epi_base(x, EPI_RESID, M);
+    e.wscale = b.s_down;
+    e.x = x.x;
+    e.ld_x = x.E;
+    e.wnext = l + 1 < x.L ? x.attn_norm + (size_t)(l + 1) * x.E : x.output_norm;
+    e.act_out = x.act_a;
+    e.act_K = x.E;
+    e.ss_out = x.ss_a;
+    return gemv(x, b.down, x.E, x.F, x.act_d, e, s);
+}
+
+int stage_lm(const dflash_ctx &x, int M, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
              hipStream_t s) {
-    const int M = 16 * B, E = x.E;
-    HIP_TRY(launch_embed(&x, id_last, block_ids, n_past, B, s), "embed launch");
-    for (int l = 0; l < x.L; ++l) {
-        const LayerBufs &b = x.layer[l];
-        EpiArgs e = epi_base(x, EPI_SCALED, M);
-        e.wscale = b.s_qkv;
-        e.ss = x.ss_a;
-        e.ss_groups = x.G_E;
-        e.out = x.qkv_out;
-        e.ld_out = x.nqkv;
-        TRY(gemv(x, b.qkv, x.nqkv, E, x.act_a, e, s));
-
-        HIP_TRY(launch_attention(&x, l, rings, n_past, B, s), "attention launch");
-
-        e = epi_base(x, EPI_RESID, M);
-        e.wscale = b.s_o;
-        e.x = x.x;
-        e.ld_x = E;
-        e.wnext = x.ffn_norm + (size_t)l * E;
-        e.act_out = x.act_f;
-        e.act_K = E;
-        e.ss_out = x.ss_f;
-        TRY(gemv(x, b.o, E, x.qdim, x.act_o, e, s));
-
-        e = epi_base(x, EPI_SWIGLU, M);
-        e.wscale = b.s_gu;
-        e.ss = x.ss_f;
-        e.ss_groups = x.G_E;
-        e.act_out = x.act_d;
-        e.act_K = x.F;
-        TRY(gemv(x, b.gu, 2 * x.F, E, x.act_f, e, s));
-
-        e = epi_base(x, EPI_RESID, M);
-        e.wscale = b.s_down;
-        e.x = x.x;
-        e.ld_x = E;
-        e.wnext = l + 1 < x.L ? x.attn_norm + (size_t)(l + 1) * E : x.output_norm;
-        e.act_out = x.act_a;
-        e.act_K = E;
-        e.ss_out = x.ss_a;
-        TRY(gemv(x, b.down, E, x.F, x.act_d, e, s));
-    }
     EpiArgs e = epi_base(x, EPI_LOGITS, M);
     e.wscale = x.s_lm;
     e.ss = x.ss_a;
@@ -362,7 +367,25 @@ int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const in
     e.drafts = drafts;
     e.target = target;
     e.n_ok = n_ok;
-    TRY(gemv(x, x.lm, x.V, E, x.act_a, e, s));
+    return gemv(x, x.lm, x.V, x.E, x.act_a, e, s);
+}
+
+// The block step: embed; per layer QKV, attention, Wo (+residual), gate/up
+// (+SwiGLU), down (+residual); lm_head with argmax (and acceptance).
+int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const int32_t *block_ids,
+             const int32_t *n_past, int B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
+             hipStream_t s) {
+    const int M = 16 * B;
+    HIP_TRY(launch_embed(&x, id_last, block_ids, n_past, B, s), "embed launch");
+    for (int l = 0; l < x.L; ++l) {
+        TRY(stage_qkv(x, l, M, s));
+        HIP_TRY(launch_attention(&x, l, rings, n_past, B, s), "attention launch");
+        TRY(stage_o(x, l, M, s));
+        TRY(stage_gu(x, l, M, s));
+        TRY(stage_down(x, l, M, s));
+    }
+    TRY(stage_lm(x, M, logits, drafts, target, n_ok, s));
+    x.last_B = B;
     return DFLASH_OK;
 }
 
@@ -417,6 +440,11 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
     if (e != hipSuccess) {
         delete x;
         return hip_fail(e, "hipGetDevice");
+    }
+    e = attention_set_smem_limit();
+    if (e != hipSuccess) {
+        delete x;
+        return hip_fail(e, "hipFuncSetAttribute (attention LDS)");
     }
     int r = prepare(*x, w, (hipStream_t)stream);
     if (r != DFLASH_OK) {
@@ -568,6 +596,21 @@ void dflash_graph_destroy(dflash_graph *g) {
     if (g->exec) hipGraphExecDestroy(g->exec);
     if (g->graph) hipGraphDestroy(g->graph);
     delete g;
+}
+
+int dflash_replay_stage(dflash_ctx *x, int32_t stage, int32_t layer, void *stream) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    if (x->last_B < 1) return fail(DFLASH_ESTATE, "no block step has run on this ctx yet");
+    if (layer < 0 || layer >= x->L) return fail(DFLASH_ERANGE, "layer %d outside 0..%d", layer, x->L - 1);
+    const int M = 16 * x->last_B;
+    hipStream_t s = (hipStream_t)stream;
+    switch (stage) {
+        case DFLASH_STAGE_QKV: return stage_qkv(*x, layer, M, s);
+        case DFLASH_STAGE_O: return stage_o(*x, layer, M, s);
+        case DFLASH_STAGE_GATE_UP: return stage_gu(*x, layer, M, s);
+        case DFLASH_STAGE_DOWN: return stage_down(*x, layer, M, s);
+        default: return fail(DFLASH_EINVAL, "unknown stage %d", stage);
+    }
 }
 
 int dflash_quantize_fp8_rows(const float *w, int32_t rows, int32_t cols, uint8_t *codes, float *scales, void *stream) {

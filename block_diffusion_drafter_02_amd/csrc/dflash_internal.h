@@ -12,32 +12,47 @@
 // ---------------------------------------------------------------------------
 // Tiling of streamed weights
 // ---------------------------------------------------------------------------
-// Every matrix the step streams is re-tiled once at create time so that one
-// wavefront load of a tile is a single contiguous run of memory.
+// Every matrix the step streams is re-tiled once at create time so that every
+// wavefront load instruction reads one contiguous kilobyte.
 //
 // A tile covers 16 output rows x 64 reduction columns (one "k-block"). Lane
 // l (0..63) of a wavefront owns row (l % 16) and the 16 consecutive columns
-// starting at 16 * (l / 16); the tile stores lane 0's 16 elements, then lane
-// 1's, and so on. Four tiles side by side (64 output rows) form a column
-// group; memory order is [group][k-block][tile 0..3][lane][16 elements].
+// starting at 16 * (l / 16). A lane's 16 elements are cut into 16-byte words
+// (es words of 16/es elements for an element size of es bytes); the tile
+// stores word 0 of lanes 0..63, then word 1 of lanes 0..63, and so on. Four
+// tiles side by side (64 output rows) form a column group; memory order is
+// [group][k-block][tile 0..3][word][lane][16 bytes].
 //
 // The MFMA 16x16x32 bf16 operands take 8 reduction elements per lane, so a
-// lane's 16 elements feed two MFMAs; for f32 weights they feed sixteen
-// 16x16x4 f32 MFMAs. Because the A (activation) operand is loaded with the same
-// lane -> (row, columns) map, any permutation of the reduction index inside a
-// k-block cancels out.
+// lane's two bf16 words feed two MFMAs; for f32 weights the four words feed
+// sixteen 16x16x4 f32 MFMAs. The activation operand is laid out with the same
+// lane -> (row, columns) map and the same word split, so any permutation of
+// the reduction index inside a k-block cancels out.
 constexpr int TILE_N = 16;
 constexpr int KBLK = 64;
 constexpr int TILES_PER_GROUP = 4;
 constexpr int GROUP_N = TILE_N * TILES_PER_GROUP;  // 64 output columns per group
 constexpr int LANE_ELEMS = 16;
 
-// element offset of weight (n, k) in a tiled matrix with KB = K / 64 k-blocks
-__host__ __device__ inline size_t tiled_offset(int n, int k, int KB) {
+// element offset of weight (n, k) in a tiled matrix with KB = K / 64 k-blocks and es-byte elements
+__host__ __device__ inline size_t tiled_offset(int n, int k, int KB, int es) {
+    const int epw = 16 / es;  // elements per 16-byte word
     int g = n / GROUP_N, t = (n / TILE_N) % TILES_PER_GROUP, r = n % TILE_N;
     int kb = k / KBLK, c = (k % KBLK) / LANE_ELEMS, j = k % LANE_ELEMS;
-    int lane = r + 16 * c;
-    return ((((size_t)g * KB + kb) * TILES_PER_GROUP + t) * 64 + lane) * LANE_ELEMS + j;
+    int lane = r + 16 * c, v = j / epw, i = j % epw;
+    return (((((size_t)g * KB + kb) * TILES_PER_GROUP + t) * es + v) * 64 + lane) * epw + i;
+}
+
+// Activation operands of the block-row kernels use the same lane order: for
+// row m, column k of a [rows][K] activation (rows a multiple of 16), element
+// offset inside one plane. es = 2 (bf16 planes of the three-term split) or 4
+// (f32). Plane p of a split activation starts at p * rows * K.
+__host__ __device__ inline size_t act_offset(int m, int k, int K, int es) {
+    const int epw = 16 / es;
+    const int KB = K / KBLK;
+    int mt = m / 16, r = m % 16, kb = k / KBLK, c = (k % KBLK) / LANE_ELEMS, j = k % LANE_ELEMS;
+    int lane = r + 16 * c, v = j / epw, i = j % epw;
+    return ((((size_t)mt * KB + kb) * es + v) * 64 + lane) * epw + i;
 }
 
 // ---------------------------------------------------------------------------
@@ -115,11 +130,30 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---------------------------------------------------------------------------
 // Activation formats for the weight-streaming kernels
 // ---------------------------------------------------------------------------
-// ACT_SPLIT3: bf16 [3][Mrows][K] (exact three-term split of fp32 values), used
-//             with bf16 and fp8 weights.
+// ACT_SPLIT3: three bf16 planes of [Mrows][K] (exact three-term split of fp32
+//             values), used with bf16 and fp8 weights.
 // ACT_F32:    f32 [Mrows][K], used with f32 weights (f32 MFMA).
 // ACT_BF16:   bf16 [Mrows][K] holding exact values (features already bf16).
+// The block-row kernels read lane-ordered planes (act_offset); the large-M
+// GEMM of encode / inject reads row-major planes.
 enum ActFmt { ACT_SPLIT3 = 0, ACT_F32 = 1, ACT_BF16 = 2 };
+
+// Write one activation value in the lane-ordered layout: f32, or the exact
+// three-term bf16 split over three planes of act_rows * K elements.
+__device__ __forceinline__ void write_act(void *act, int fmt, int act_rows, int K, int row, int col, float v) {
+    if (fmt == ACT_F32) {
+        ((float *)act)[act_offset(row, col, K, 4)] = v;
+    } else {
+        uint16_t t0, t1, t2;
+        split3(v, t0, t1, t2);
+        uint16_t *p = (uint16_t *)act;
+        const size_t plane = (size_t)act_rows * K;
+        const size_t o = act_offset(row, col, K, 2);
+        p[o] = t0;
+        p[plane + o] = t1;
+        p[2 * plane + o] = t2;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Epilogues of the split-K weight-streaming kernel
@@ -191,6 +225,7 @@ struct dflash_ctx {
     int device;
     int E, H, Hkv, D, F, W, L, V, C, qdim, kvdim, nqkv, Mmax, G_E, NCH;
     int act_fmt;       // activation format of the step GEMVs
+    int last_B;        // batch of the last block step (0 before the first)
     size_t wbytes_el;  // bytes per streamed weight element (4, 2, 1)
     char *ws;
     size_t ws_bytes;
@@ -218,7 +253,7 @@ struct dflash_ctx {
     float *ss_a, *ss_f; // [G_E][Mmax]
     float *qkv_out;     // [Mmax][nqkv]
     float *rope_cs;     // [max_batch][block][D/2][2]
-    float *att_ml;      // [max_batch][Hkv][NCH+1][G*16][2]
+    float *att_ml;      // [max_batch][Hkv][NCH+1][G*16][2], NCH = window / attn_chunk
     float *att_o;       // [max_batch][Hkv][NCH+1][G*16][D]
     float *partial;
     size_t partial_floats;
@@ -262,6 +297,14 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
                         int B, hipStream_t s);
 hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, const int32_t *n_past, int B,
                             hipStream_t s);
+hipError_t attention_set_smem_limit();
+// ring slots per attention chunk (one workgroup per chunk and kv head): 128
+// (or 64) for a bf16 ring, 32 for an f32 ring (its values take three planes
+// of LDS)
+inline int attn_chunk(int ring_dtype, int W) {
+    if (ring_dtype != DFLASH_BF16) return 32;
+    return W % 128 == 0 ? 128 : 64;
+}
 hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, int n, int32_t *n_ok, hipStream_t s);
 
 // ring layout helpers (host and device)

@@ -139,6 +139,28 @@ __device__ __forceinline__ void head_norm_rope(float (&x)[D / 64], const float *
     }
 }
 
+// Same with the lane's norm weights (nw[e] = w[lane + 64e]) and cos/sin
+// (c = cos, s = sin of the lane's pair) already in registers.
+template <int D>
+__device__ __forceinline__ void head_norm_rope_reg(float (&x)[D / 64], const float (&nw)[D / 64], float c, float s,
+                                                   float eps, int lane) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) ss += x[e] * x[e];
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) x[e] = x[e] * r * nw[e];
+    if constexpr (D == 128) {
+        const float x1 = x[0], x2 = x[1];
+        x[0] = x1 * c - x2 * s;
+        x[1] = x1 * s + x2 * c;
+    } else {
+        const float partner = __shfl_xor(x[0], 32, 64);
+        x[0] = lane < 32 ? x[0] * c - partner * s : partner * s + x[0] * c;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Inject (dflash-ops card, Method; Requirements and limits)
 // ---------------------------------------------------------------------------
@@ -242,17 +264,7 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
                                            : ((const float *)a.tok_embd)[off];
         }
         a.x[(size_t)m * a.E + n] = v;
-        if (a.act_fmt == ACT_F32) {
-            ((float *)a.act_a)[(size_t)m * a.E + n] = v * a.attn_norm0[n];
-        } else {
-            uint16_t t0, t1, t2;
-            split3(v * a.attn_norm0[n], t0, t1, t2);
-            uint16_t *p = (uint16_t *)a.act_a;
-            const size_t plane = (size_t)a.act_rows * a.E;
-            p[(size_t)m * a.E + n] = t0;
-            p[plane + (size_t)m * a.E + n] = t1;
-            p[2 * plane + (size_t)m * a.E + n] = t2;
-        }
+        write_act(a.act_a, a.act_fmt, a.act_rows, a.E, m, n, v * a.attn_norm0[n]);
         const float sq = wave_sum(v * v);
         if (lane == 0) a.ss_a[(size_t)g * a.ss_stride + m] = sq;
     }
@@ -299,162 +311,384 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 // ---------------------------------------------------------------------------
 // Non-causal sliding-window GQA attention (dflash-ops card, Method)
 // ---------------------------------------------------------------------------
-// Partial kernel: grid (NCH + 1, Hkv, B), 256 threads. Chunk c < NCH covers
-// ring slots [64c, 64c + 64); chunk NCH is the block's own 16 keys. The G*16
-// query vectors of kv head j (q heads jG .. jG+G-1, 16 block rows each) are
-// RMS-normed with q_norm and roped at n_past + i, then scaled by 1/sqrt(D).
-// Thread t serves query t/4 and head elements (t%4) + 4e. Keys are taken 16 at a
-// time with a running max and sum; the chunk's (max, sum, unnormalised output)
-// goes to the partial buffers. A ring key at slot s is visible to row i when
-// slot_pos[s] >= 0 and 0 <= n_past + i - slot_pos[s] < W; block keys are always
-// visible.
+// Partial kernel: grid (NCH + 1, Hkv, B), 256 threads = 4 wavefronts. Chunk
+// c < NCH covers ring slots [c*CH, c*CH + CH); chunk NCH is the block's own 16
+// keys. The G*16 query vectors of kv head j (q heads jG .. jG+G-1, 16 block rows
+// each) are RMS-normed with q_norm, roped at n_past + i and scaled by
+// 1/sqrt(D); wave w handles q head jG + w.
+//
+// Scores are computed transposed, S^T = K Q^T (keys as MFMA rows, queries as
+// columns), so that each lane holds the scores of one query for 4 keys of every
+// 16-key tile. Those registers are exactly the B operand of O^T = V^T P^T when
+// lane group c supplies keys {4c..4c+3} of two consecutive key tiles: the
+// reduction index of an MFMA may be permuted freely as long as both operands
+// use the same permutation, and V^T is read from LDS in that order.
+// Operands are exact: fp32 values enter as three bf16 terms (a + b <= 2 cross
+// products, error ~2^-27 relative), bf16 ring keys and values as one term.
+// A ring key at slot s is visible to block row i when slot_pos[s] >= 0 and
+// 0 <= n_past + i - slot_pos[s] < W; block keys are always visible.
 struct AttnArgs {
     const float *qkv;
     int nqkv, qdim, kvdim;
     const float *rope_cs;
     const float *q_norm, *k_norm;  // this layer's [D]
     void *const *rings;
-    int layer, L, Hkv, W, ring_dtype, G, NCH, block;
+    int layer, L, Hkv, W, ring_dtype, G, NCH, CH, block;
+    int vt_elems;  // bf16 elements of the V^T region in LDS
     const int32_t *n_past;
     float eps, scale;
     float *ml, *o;
 };
 
-template <int D>
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+// 8 fp32 values -> three bf16x8 operands (exact split)
+__device__ __forceinline__ void split8(const float (&v)[8], bf16x8_t (&t)[3]) {
+    u32x4_t w0, w1, w2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint16_t a0, a1, a2, b0, b1, b2;
+        split3(v[2 * i], a0, a1, a2);
+        split3(v[2 * i + 1], b0, b1, b2);
+        w0[i] = (uint32_t)a0 | ((uint32_t)b0 << 16);
+        w1[i] = (uint32_t)a1 | ((uint32_t)b1 << 16);
+        w2[i] = (uint32_t)a2 | ((uint32_t)b2 << 16);
+    }
+    t[0] = __builtin_bit_cast(bf16x8_t, w0);
+    t[1] = __builtin_bit_cast(bf16x8_t, w1);
+    t[2] = __builtin_bit_cast(bf16x8_t, w2);
+}
+
+#define MFMA_BF16(A, B, C) __builtin_amdgcn_mfma_f32_16x16x32_bf16((A), (B), (C), 0, 0, 0)
+
+template <int D, int MAXKT>
 __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
-    constexpr int DE = D / 4;  // elements per thread
+    constexpr int KS = D / 32;   // MFMA k-steps over the head dimension
+    constexpr int DT = D / 16;   // 16-wide tiles of the head dimension
+    constexpr int KROW = D + 8;  // bf16 elements per staged K row (+8 spreads LDS banks)
+                                 // MAXKT: 16-key tiles per ring chunk (CH = 16 * MAXKT)
+    extern __shared__ float smem[];
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int NQ = a.G * 16;
     const bool is_block = (c == a.NCH);
-    const int nvec = NQ + (is_block ? 16 : 0);
-    __shared__ float stage[64 + 16][D];
-    __shared__ float ksh[16][D];
-    __shared__ float vsh[16][D];
-    __shared__ int kpos[16];
+    const bool bf16_ring = a.ring_dtype == DFLASH_BF16;
+    const bool split_kv = is_block || !bf16_ring;  // fp32 keys/values need three terms
+    const int nkeys = is_block ? 16 : a.CH;
+    const int nkt = nkeys / 16;            // key tiles
+    const int nks2 = (nkeys + 31) / 32;    // k-steps over keys for P V (the block pads 16 keys to 32)
+    const int CHP = nks2 * 32 + 4;         // V^T row length: keys padded to 32, +4 to spread LDS banks
+    const int nplanes = split_kv ? 3 : 1;
+    float(*stage)[D] = (float(*)[D])smem;                              // [80][D] normed / roped q (and block k)
+    uint16_t *ksh = (uint16_t *)(smem + (64 + 16) * D);                 // [CH][KROW] bf16 ring keys
+    uint16_t *vt = ksh + (bf16_ring ? a.CH * KROW : 0);                 // [planes][D][CHP] V^T in bf16 terms
+    int *kpos = (int *)(vt + a.vt_elems);                               // [CH] positions of the chunk's slots
 
-    // raw q (and block k, v) of this kv head
-    for (int idx = tid; idx < nvec * D; idx += 256) {
-        const int vec = idx / D, d = idx % D;
-        const int i = vec % 16;
-        const size_t m = (size_t)b * a.block + i;
-        float v;
-        if (vec < NQ)
-            v = a.qkv[m * a.nqkv + (size_t)(j * a.G + vec / 16) * D + d];
-        else
-            v = a.qkv[m * a.nqkv + a.qdim + (size_t)j * D + d];
-        stage[vec][d] = v;
-    }
-    if (is_block) {
-        for (int idx = tid; idx < 16 * D; idx += 256) {
-            const int i = idx / D, d = idx % D;
-            vsh[i][d] = a.qkv[((size_t)b * a.block + i) * a.nqkv + a.qdim + a.kvdim + (size_t)j * D + d];
-        }
-    }
-    __syncthreads();
-    for (int vec = wave; vec < nvec; vec += 4) {
-        float x[D / 64];
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e) x[e] = stage[vec][lane + 64 * e];
-        const int i = vec % 16;
-        const float *cs = a.rope_cs + ((size_t)b * a.block + i) * D;  // (D/2) pairs of (cos, sin)
-        head_norm_rope<D>(x, vec < NQ ? a.q_norm : a.k_norm, cs, a.eps, lane);
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e) stage[vec][lane + 64 * e] = x[e];
-    }
-    __syncthreads();
-
-    const int qi = tid >> 2, dq = tid & 3;
-    const bool live = qi < NQ;
-    float q[DE], o[DE];
-#pragma unroll
-    for (int e = 0; e < DE; ++e) {
-        q[e] = live ? stage[qi][dq + 4 * e] * a.scale : 0.0f;
-        o[e] = 0.0f;
-    }
-    const int qpos = a.n_past[b] + (qi & 15);
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    const int es = a.ring_dtype == DFLASH_BF16 ? 2 : 4;
+    const int es = bf16_ring ? 2 : 4;
     const char *rb = (const char *)a.rings[b];
     const void *Kb = rb;
     const void *Vb = rb + ring_v_offset(a.L, a.Hkv, a.W, D, es);
     const int32_t *sp = (const int32_t *)(rb + ring_pos_offset(a.L, a.Hkv, a.W, D, es));
-    const int nsub = is_block ? 1 : 4;
-    for (int st = 0; st < nsub; ++st) {
-        const float(*Kt)[D];
-        const float(*Vt)[D];
-        if (is_block) {
-            Kt = (const float(*)[D]) & stage[NQ][0];
-            Vt = (const float(*)[D]) & vsh[0][0];
-        } else {
-            __syncthreads();
-            const int s0 = c * 64 + st * 16;
-            const size_t base = (((size_t)a.layer * a.Hkv + j) * a.W + s0) * D;
-            for (int idx = tid; idx < 16 * D; idx += 256) {
-                ksh[idx / D][idx % D] = ring_load(Kb, a.ring_dtype, base + idx);
-                vsh[idx / D][idx % D] = ring_load(Vb, a.ring_dtype, base + idx);
+    const size_t head_base = ((size_t)a.layer * a.Hkv + j) * a.W;  // slot-row index of slot 0
+    const int s0 = c * a.CH;
+
+    // ---- raw q (and block k) of this kv head: float4 loads, all issued before any use ----
+    const int nvec = NQ + (is_block ? 16 : 0);
+    {
+        constexpr int V4 = D / 4;
+        constexpr int NB = (80 * V4 + 255) / 256;
+        const int n4 = nvec * V4;
+        float4 buf[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int idx = min(tid + 256 * u, n4 - 1);  // clamped: every lane loads, live ones store
+            const int vec = idx / V4, d4 = idx % V4;
+            const size_t m = (size_t)b * a.block + (vec % 16);
+            const size_t col = vec < NQ ? (size_t)(j * a.G + vec / 16) * D : a.qdim + (size_t)j * D;
+            buf[u] = *(const float4 *)(a.qkv + m * a.nqkv + col + 4 * d4);
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int idx = tid + 256 * u;
+            if (idx < n4) *(float4 *)&stage[idx / V4][4 * (idx % V4)] = buf[u];
+        }
+    }
+    // ---- chunk keys and values into LDS ----
+    if (is_block) {
+        for (int idx = tid; idx < 3 * D * CHP; idx += 256) vt[idx] = 0;  // keys 16..31 pad the k-step
+        __syncthreads();
+        for (int idx = tid; idx < 16 * D; idx += 256) {
+            const int key = idx / D, d = idx % D;
+            const float v = a.qkv[((size_t)b * a.block + key) * a.nqkv + a.qdim + a.kvdim + (size_t)j * D + d];
+            uint16_t t0, t1, t2;
+            split3(v, t0, t1, t2);
+            vt[(0 * D + d) * CHP + key] = t0;
+            vt[(1 * D + d) * CHP + key] = t1;
+            vt[(2 * D + d) * CHP + key] = t2;
+        }
+    } else if (bf16_ring) {
+        // K rows and V rows: CH*D/8 16-byte words each, in batches of 8 words per thread
+        constexpr int NWORD = (16 * MAXKT * D / 8 + 255) / 256;
+        constexpr int BATCH = NWORD < 4 ? NWORD : 4;
+        const int nword = a.CH * D / 8;
+        const uint16_t *kg = (const uint16_t *)Kb + (head_base + s0) * D;
+        const uint16_t *vg = (const uint16_t *)Vb + (head_base + s0) * D;
+#pragma unroll
+        for (int u0 = 0; u0 < NWORD; u0 += BATCH) {
+            uint4 kbuf[BATCH], vbuf[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int w = min(tid + 256 * (u0 + u), nword - 1);
+                kbuf[u] = *(const uint4 *)(kg + 8 * (size_t)w);
+                vbuf[u] = *(const uint4 *)(vg + 8 * (size_t)w);
             }
-            if (tid < 16) kpos[tid] = sp[s0 + tid];
-            __syncthreads();
-            Kt = (const float(*)[D]) & ksh[0][0];
-            Vt = (const float(*)[D]) & vsh[0][0];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int w = tid + 256 * (u0 + u);
+                if (w < nword) {
+                    const int key = (8 * w) / D, d = (8 * w) % D;
+                    *(uint4 *)(ksh + key * KROW + d) = kbuf[u];
+                    const uint32_t pk[4] = {vbuf[u].x, vbuf[u].y, vbuf[u].z, vbuf[u].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        vt[(size_t)(d + 2 * e) * CHP + key] = (uint16_t)(pk[e] & 0xffffu);
+                        vt[(size_t)(d + 2 * e + 1) * CHP + key] = (uint16_t)(pk[e] >> 16);
+                    }
+                }
+            }
         }
-        float sc[16];
+    } else {
+        // f32 ring: values split into three planes (keys are read from memory and split at use)
+        constexpr int NW4 = (16 * MAXKT * D / 4 + 255) / 256;
+        constexpr int BATCH = NW4 < 8 ? NW4 : 8;
+        const int nw4 = a.CH * D / 4;
+        const float *vg = (const float *)Vb + (head_base + s0) * D;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            float acc = 0.0f;
+        for (int u0 = 0; u0 < NW4; u0 += BATCH) {
+            float4 buf[BATCH];
 #pragma unroll
-            for (int e = 0; e < DE; ++e) acc += q[e] * Kt[k][dq + 4 * e];
-            sc[k] = acc;
+            for (int u = 0; u < BATCH; ++u) buf[u] = *(const float4 *)(vg + 4 * (size_t)min(tid + 256 * (u0 + u), nw4 - 1));
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int w = tid + 256 * (u0 + u);
+                if (w < nw4) {
+                    const int key = (4 * w) / D, d = (4 * w) % D;
+                    const float f[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint16_t t0, t1, t2;
+                        split3(f[e], t0, t1, t2);
+                        vt[(size_t)(0 * D + d + e) * CHP + key] = t0;
+                        vt[(size_t)(1 * D + d + e) * CHP + key] = t1;
+                        vt[(size_t)(2 * D + d + e) * CHP + key] = t2;
+                    }
+                }
+            }
+        }
+    }
+    if (!is_block)
+        for (int k = tid; k < a.CH; k += 256) kpos[k] = sp[s0 + k];
+    __syncthreads();
+    // ---- per-head RMSNorm + rope of q (and block k); weights and the 16 rows' cos/sin in registers ----
+    {
+        float qn[D / 64], kn[D / 64], cosr[16], sinr[16];
+        const int pair = D == 128 ? lane : (lane & 31);
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) {
+            qn[e] = a.q_norm[lane + 64 * e];
+            kn[e] = a.k_norm[lane + 64 * e];
         }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            sc[k] += __shfl_xor(sc[k], 1, 64);
-            sc[k] += __shfl_xor(sc[k], 2, 64);
+        for (int i = 0; i < 16; ++i) {
+            const float2 cs = *(const float2 *)(a.rope_cs + ((size_t)b * a.block + i) * D + 2 * pair);
+            cosr[i] = cs.x;
+            sinr[i] = cs.y;
         }
-        float mx = -INFINITY;
+        for (int vec = wave; vec < nvec; vec += 4) {
+            float x[D / 64];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            bool vis = true;
-            if (!is_block) {
-                const int kp = kpos[k];
+            for (int e = 0; e < D / 64; ++e) x[e] = stage[vec][lane + 64 * e];
+            float cr = 0.0f, sr = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (i == (vec & 15)) {
+                    cr = cosr[i];
+                    sr = sinr[i];
+                }
+            head_norm_rope_reg<D>(x, vec < NQ ? qn : kn, cr, sr, a.eps, lane);
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) stage[vec][lane + 64 * e] = x[e];
+        }
+    }
+    __syncthreads();
+    if (wave >= a.G) return;
+
+    const int hh = wave, q = lane & 15, grp = lane >> 4;
+    // ---- Q^T operand: query q, head elements 32ks + 8grp .. +8, three terms ----
+    bf16x8_t qb[KS][3];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = stage[hh * 16 + q][32 * ks + 8 * grp + e] * a.scale;
+        split8(v, qb[ks]);
+    }
+    // ---- S^T = K Q^T, key tile kt: lane holds keys 16kt + 4grp + i (i < 4) of query q ----
+    f32x4_t st[MAXKT];
+#pragma clang loop unroll(full)
+    for (int kt = 0; kt < MAXKT; ++kt) {
+        st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (kt >= nkt) continue;
+        const int key = 16 * kt + q;  // A-operand row of this lane
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int d0 = 32 * ks + 8 * grp;
+            if (!split_kv) {
+                const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(ksh + key * KROW + d0));
+#pragma unroll
+                for (int t = 0; t < 3; ++t) st[kt] = MFMA_BF16(ka, qb[ks][t], st[kt]);
+            } else {
+                float kv[8];
+                if (is_block) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) kv[e] = stage[NQ + key][d0 + e];
+                } else {
+                    const float4 *kp = (const float4 *)((const float *)Kb + (head_base + s0 + key) * D + d0);
+                    const float4 k0 = kp[0], k1 = kp[1];
+                    kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w;
+                    kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
+                }
+                bf16x8_t ka[3];
+                split8(kv, ka);
+                // the six products with term-order sum <= 2
+                st[kt] = MFMA_BF16(ka[0], qb[ks][0], st[kt]);
+                st[kt] = MFMA_BF16(ka[0], qb[ks][1], st[kt]);
+                st[kt] = MFMA_BF16(ka[1], qb[ks][0], st[kt]);
+                st[kt] = MFMA_BF16(ka[0], qb[ks][2], st[kt]);
+                st[kt] = MFMA_BF16(ka[1], qb[ks][1], st[kt]);
+                st[kt] = MFMA_BF16(ka[2], qb[ks][0], st[kt]);
+            }
+        }
+    }
+    // ---- mask and chunk softmax statistics for query q ----
+    const int qpos = a.n_past[b] + q;
+    float mx = -INFINITY;
+#pragma clang loop unroll(full)
+    for (int kt = 0; kt < MAXKT; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bool vis = kt < nkt;
+            if (vis && !is_block) {
+                const int kp = kpos[16 * kt + 4 * grp + i];
                 const int dlt = qpos - kp;
                 vis = kp >= 0 && dlt >= 0 && dlt < a.W;
             }
-            if (!vis) sc[k] = -INFINITY;
-            mx = fmaxf(mx, sc[k]);
+            if (!vis) st[kt][i] = -INFINITY;
+            mx = fmaxf(mx, st[kt][i]);
         }
-        const float m_new = fmaxf(m_run, mx);
-        if (m_new == -INFINITY) continue;  // nothing visible yet
-        const float alpha = expf(m_run - m_new);
-        float psum = 0.0f;
-#pragma unroll
-        for (int e = 0; e < DE; ++e) o[e] *= alpha;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const float p = expf(sc[k] - m_new);
-            psum += p;
-#pragma unroll
-            for (int e = 0; e < DE; ++e) o[e] += p * Vt[k][dq + 4 * e];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
     }
-    if (live) {
-        const size_t slot = (((size_t)b * a.Hkv + j) * (a.NCH + 1) + c) * NQ + qi;
-        if (dq == 0) {
-            a.ml[slot * 2] = m_run;
-            a.ml[slot * 2 + 1] = l_run;
-        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float lsum = 0.0f;
+#pragma clang loop unroll(full)
+    for (int kt = 0; kt < MAXKT; ++kt)
 #pragma unroll
-        for (int e = 0; e < DE; ++e) a.o[slot * D + dq + 4 * e] = o[e];
+        for (int i = 0; i < 4; ++i) {
+            const float p = (mx == -INFINITY || st[kt][i] == -INFINITY) ? 0.0f : expf(st[kt][i] - mx);
+            st[kt][i] = p;
+            lsum += p;
+        }
+    lsum += __shfl_xor(lsum, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    // ---- O^T = V^T P^T over key pairs of tiles (2ks2, 2ks2 + 1) ----
+    f32x4_t ot[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) ot[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma clang loop unroll(full)
+    for (int ks2 = 0; ks2 < (MAXKT + 1) / 2; ++ks2) {
+        if (ks2 >= nks2) continue;
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = st[2 * ks2][i];
+            pv[4 + i] = 2 * ks2 + 1 < MAXKT ? st[(2 * ks2 + 1) % MAXKT][i] : 0.0f;
+        }
+        bf16x8_t pb[3];
+        split8(pv, pb);
+        const int k0 = 32 * ks2 + 4 * grp, k1 = 32 * ks2 + 16 + 4 * grp;  // the lane group's keys in V^T
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const int d = 16 * dt + q;
+            bf16x8_t va[3];
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                if (t >= nplanes) break;
+                const uint16_t *row = vt + ((size_t)t * D + d) * CHP;
+                const uint2 lo = *(const uint2 *)(row + k0);
+                const uint2 hi = *(const uint2 *)(row + k1);
+                va[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+            }
+            if (!split_kv) {
+#pragma unroll
+                for (int t = 0; t < 3; ++t) ot[dt] = MFMA_BF16(va[0], pb[t], ot[dt]);
+            } else {
+                ot[dt] = MFMA_BF16(va[0], pb[0], ot[dt]);
+                ot[dt] = MFMA_BF16(va[0], pb[1], ot[dt]);
+                ot[dt] = MFMA_BF16(va[1], pb[0], ot[dt]);
+                ot[dt] = MFMA_BF16(va[0], pb[2], ot[dt]);
+                ot[dt] = MFMA_BF16(va[1], pb[1], ot[dt]);
+                ot[dt] = MFMA_BF16(va[2], pb[0], ot[dt]);
+            }
+        }
     }
+    // ---- partial (max, sum, unnormalised output) of query (hh, q) ----
+    const size_t slot = (((size_t)b * a.Hkv + j) * (a.NCH + 1) + c) * NQ + hh * 16 + q;
+    if (grp == 0) {
+        a.ml[slot * 2] = mx;
+        a.ml[slot * 2 + 1] = lsum;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.o[slot * D + 16 * dt + 4 * grp + i] = ot[dt][i];
 }
 
-// Combine kernel: grid (H, B), 256 threads; row i = t/16 of q head h merges the
-// NCH + 1 chunk partials in chunk order and writes the attention output in the
-// activation format of the Wo projection.
+// LDS of the partial kernel: staged q (and block k) [80][D] f32; for a bf16
+// ring the chunk's keys [CH][D+8] bf16; the V^T planes (one bf16 plane of CH
+// keys for a bf16 ring, three planes for f32 values, the block padded to 32
+// keys; every row +4 elements); the chunk's slot positions.
+int attn_vt_elems(int D, int CH, int ring_dtype) {
+    const int ring = (CH + 4) * (ring_dtype == DFLASH_BF16 ? 1 : 3);
+    return (ring > 3 * 36 ? ring : 3 * 36) * D;
+}
+size_t attn_smem_bytes(int D, int CH, int ring_dtype) {
+    const size_t kbytes = ring_dtype == DFLASH_BF16 ? (size_t)CH * (D + 8) * 2 : 0;
+    return (size_t)(64 + 16) * D * 4 + kbytes + (size_t)attn_vt_elems(D, CH, ring_dtype) * 2 + (size_t)CH * 4;
+}
+
+template <int D, int KT>
+static hipError_t set_attn_limit(int bytes) {
+    return hipFuncSetAttribute((const void *)attn_partial_kernel<D, KT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               bytes);
+}
+
+hipError_t attention_set_smem_limit() {
+    const int bytes = 160 * 1024;
+    hipError_t e;
+    if ((e = set_attn_limit<128, 8>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<128, 4>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<128, 2>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<64, 8>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<64, 4>(bytes)) != hipSuccess) return e;
+    return set_attn_limit<64, 2>(bytes);
+}
+
+// Combine kernel: grid (H, B, D / 32), 256 threads. Thread t serves block row
+// t / 16 of q head h and head elements 32 * blockIdx.z + 2 * (t % 16) + {0, 1};
+// it merges the NCH + 1 chunk partials in chunk order and writes the attention
+// output in the activation format of the Wo projection.
 struct CombArgs {
     const float *ml, *o;
     int NCH, G, Hkv, D, block;
@@ -465,39 +699,32 @@ struct CombArgs {
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombArgs a) {
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
-    const int i = tid >> 4, dl = tid & 15;
+    const int i = tid >> 4;
+    const int d = blockIdx.z * 32 + 2 * (tid & 15);
     const int j = h / a.G, hh = h % a.G;
     const int NQ = a.G * 16, qi = hh * 16 + i;
     const size_t base = ((size_t)b * a.Hkv + j) * (a.NCH + 1);
-    float mstar = -INFINITY;
-    for (int c = 0; c <= a.NCH; ++c) mstar = fmaxf(mstar, a.ml[((base + c) * NQ + qi) * 2]);
-    float lsum = 0.0f;
-    for (int c = 0; c <= a.NCH; ++c) {
-        const float mc = a.ml[((base + c) * NQ + qi) * 2];
-        if (mc != -INFINITY) lsum += expf(mc - mstar) * a.ml[((base + c) * NQ + qi) * 2 + 1];
+    const int nc = a.NCH + 1;
+    // one pass with a running maximum; chunk loads are independent of the running state
+    float mstar = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
+#pragma unroll 17
+    for (int c = 0; c < nc; ++c) {
+        const float2 ml = *(const float2 *)(a.ml + ((base + c) * NQ + qi) * 2);
+        const float2 ov = *(const float2 *)(a.o + ((base + c) * NQ + qi) * a.D + d);
+        if (ml.x != -INFINITY) {
+            const float mn = fmaxf(mstar, ml.x);
+            const float alpha = expf(mstar - mn);  // 0 when mstar is -inf
+            const float w = expf(ml.x - mn);
+            lsum = lsum * alpha + w * ml.y;
+            o0 = o0 * alpha + w * ov.x;
+            o1 = o1 * alpha + w * ov.y;
+            mstar = mn;
+        }
     }
     const float inv = 1.0f / lsum;
     const int row = b * a.block + i;
-    for (int d = dl; d < a.D; d += 16) {
-        float acc = 0.0f;
-        for (int c = 0; c <= a.NCH; ++c) {
-            const float mc = a.ml[((base + c) * NQ + qi) * 2];
-            if (mc != -INFINITY) acc += expf(mc - mstar) * a.o[((base + c) * NQ + qi) * a.D + d];
-        }
-        const float v = acc * inv;
-        const int col = h * a.D + d;
-        if (a.act_fmt == ACT_F32) {
-            ((float *)a.act_o)[(size_t)row * a.qdim + col] = v;
-        } else {
-            uint16_t t0, t1, t2;
-            split3(v, t0, t1, t2);
-            uint16_t *p = (uint16_t *)a.act_o;
-            const size_t plane = (size_t)a.act_rows * a.qdim;
-            p[(size_t)row * a.qdim + col] = t0;
-            p[plane + (size_t)row * a.qdim + col] = t1;
-            p[2 * plane + (size_t)row * a.qdim + col] = t2;
-        }
-    }
+    write_act(a.act_o, a.act_fmt, a.act_rows, a.qdim, row, h * a.D + d, o0 * inv);
+    write_act(a.act_o, a.act_fmt, a.act_rows, a.qdim, row, h * a.D + d + 1, o1 * inv);
 }
 
 hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, const int32_t *n_past, int B,
@@ -518,6 +745,8 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.ring_dtype = c->cfg.ring_dtype;
     a.G = c->H / c->Hkv;
     a.NCH = c->NCH;
+    a.CH = c->W / c->NCH;
+    a.vt_elems = attn_vt_elems(c->D, a.CH, c->cfg.ring_dtype);
     a.block = c->cfg.block;
     a.n_past = n_past;
     a.eps = c->cfg.rms_eps;
@@ -525,12 +754,17 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.ml = c->att_ml;
     a.o = c->att_o;
     dim3 grid(c->NCH + 1, c->Hkv, B);
-    if (c->D == 128)
-        hipLaunchKernelGGL(attn_partial_kernel<128>, grid, dim3(256), 0, s, a);
-    else if (c->D == 64)
-        hipLaunchKernelGGL(attn_partial_kernel<64>, grid, dim3(256), 0, s, a);
-    else
-        return hipErrorInvalidValue;
+    const size_t smem = attn_smem_bytes(c->D, a.CH, c->cfg.ring_dtype);
+    const int kt = a.CH / 16;
+#define DFLASH_ATTN_LAUNCH(DD, KK) hipLaunchKernelGGL((attn_partial_kernel<DD, KK>), grid, dim3(256), smem, s, a)
+    if (c->D == 128 && kt == 8) DFLASH_ATTN_LAUNCH(128, 8);
+    else if (c->D == 128 && kt == 4) DFLASH_ATTN_LAUNCH(128, 4);
+    else if (c->D == 128 && kt == 2) DFLASH_ATTN_LAUNCH(128, 2);
+    else if (c->D == 64 && kt == 8) DFLASH_ATTN_LAUNCH(64, 8);
+    else if (c->D == 64 && kt == 4) DFLASH_ATTN_LAUNCH(64, 4);
+    else if (c->D == 64 && kt == 2) DFLASH_ATTN_LAUNCH(64, 2);
+    else return hipErrorInvalidValue;
+#undef DFLASH_ATTN_LAUNCH
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     CombArgs cb;
@@ -545,7 +779,7 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     cb.act_fmt = c->act_fmt;
     cb.act_rows = c->Mmax;
     cb.qdim = c->qdim;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(c->H, B), dim3(256), 0, s, cb);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(c->H, B, c->D / 32), dim3(256), 0, s, cb);
     return hipGetLastError();
 }
 

@@ -54,8 +54,8 @@ __global__ void tile_weights_kernel(const uint8_t *__restrict__ src, int rows, i
     const int k = (int)(idx % chunks) * LANE_ELEMS;
     const int v = tiled_row(r, row_map, dst_row0, pair_half);
     const u32x4 *s = (const u32x4 *)(src + ((size_t)r * K + k) * esize);
-    u32x4 *d = (u32x4 *)(dst + tiled_offset(v, k, KB) * esize);
-    for (int i = 0; i < esize; ++i) d[i] = s[i];  // 16 elements = esize 16-byte words
+    const int epw = 16 / esize;  // 16 elements = esize 16-byte words, each stored with its wavefront neighbours
+    for (int w = 0; w < esize; ++w) *(u32x4 *)(dst + tiled_offset(v, k + w * epw, KB, esize) * esize) = s[w];
 }
 
 hipError_t launch_tile_weights(const void *src, int src_rows, int K, int esize, void *dst, int KB, int row_map,
@@ -110,9 +110,9 @@ hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *code
 template <int WT>
 __device__ __forceinline__ void load_wtile(const void *W, size_t tile_index, int lane, u32x4 (&w)[WTraits<WT>::NV]) {
     constexpr int NV = WTraits<WT>::NV;
-    const u32x4 *p = (const u32x4 *)W + (tile_index * 64 + lane) * NV;
+    const u32x4 *p = (const u32x4 *)W + tile_index * NV * 64 + lane;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) w[v] = p[v];
+    for (int v = 0; v < NV; ++v) w[v] = p[v * 64];
 }
 
 // 16 bf16 values of one lane as two MFMA operands
@@ -156,6 +156,8 @@ struct AFTraits<ACT_BF16> {
     static constexpr int NW = 2;
 };
 
+// Row-major activation planes (the large-M GEMM reads caller inputs and its
+// own row-major staging).
 template <int AF>
 __device__ __forceinline__ void load_act(const void *act, int act_rows, int K, int row, int M, int kb, int lane,
                                          u32x4 (&a)[AFTraits<AF>::NW]) {
@@ -182,6 +184,34 @@ __device__ __forceinline__ void load_act(const void *act, int act_rows, int K, i
         const u32x4 *p = (const u32x4 *)((const uint16_t *)act + (size_t)row * K + col);
         a[0] = p[0];
         a[1] = p[1];
+    }
+}
+
+// Lane-ordered activation planes (act_offset): one k-block of one 16-row tile
+// is 1 KB per plane word, read by one contiguous wavefront load.
+template <int AF>
+__device__ __forceinline__ void load_act_lanes(const void *act, int act_rows, int K, int mt, bool live, int kb,
+                                               int lane, u32x4 (&a)[AFTraits<AF>::NW]) {
+    constexpr int NW = AFTraits<AF>::NW;
+    if (!live) {
+#pragma unroll
+        for (int i = 0; i < NW; ++i) a[i] = u32x4{0, 0, 0, 0};
+        return;
+    }
+    const int KB = K / KBLK;
+    if constexpr (AF == ACT_SPLIT3) {
+        const u32x4 *base = (const u32x4 *)act + ((size_t)mt * KB + kb) * 128 + lane;
+        const size_t plane = (size_t)act_rows * K / 8;  // 16-byte words per plane
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            a[2 * t] = base[t * plane];
+            a[2 * t + 1] = base[t * plane + 64];
+        }
+    } else {
+        static_assert(AF == ACT_F32, "lane-ordered activations are split bf16 or f32");
+        const u32x4 *base = (const u32x4 *)act + ((size_t)mt * KB + kb) * 256 + lane;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) a[v] = base[v * 64];
     }
 }
 
@@ -222,23 +252,6 @@ __device__ __forceinline__ void tile_mfma(const u32x4 (&w)[WTraits<WT>::NV], con
 }
 
 // ---------------------------------------------------------------------------
-// Activation writers (epilogues)
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void write_act(void *act, int fmt, int act_rows, int K, int row, int col, float v) {
-    if (fmt == ACT_F32) {
-        ((float *)act)[(size_t)row * K + col] = v;
-    } else {
-        uint16_t t0, t1, t2;
-        split3(v, t0, t1, t2);
-        uint16_t *p = (uint16_t *)act;
-        const size_t plane = (size_t)act_rows * K;
-        p[(size_t)row * K + col] = t0;
-        p[plane + (size_t)row * K + col] = t1;
-        p[2 * plane + (size_t)row * K + col] = t2;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Split-K weight-streaming kernel for the block rows
 // ---------------------------------------------------------------------------
 // Grid (G = N/64 column groups, S k-splits), 256 threads = 4 wavefronts.
@@ -249,7 +262,7 @@ __device__ __forceinline__ void write_act(void *act, int fmt, int act_rows, int 
 // global memory; the last workgroup of the group to arrive (an agent-scope
 // atomic counter, fenced on both sides) sums the S partials in split order and
 // runs the epilogue, so results do not depend on scheduling.
-template <int WT, int AF, int MT>
+template <int WT, int AF, int MT, int EPI>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     constexpr int NV = WTraits<WT>::NV;
     constexpr int NW = AFTraits<AF>::NW;
@@ -274,7 +287,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             u32x4 av[NW];
-            load_act<AF>(a.act, a.act_rows, a.K, mt * 16 + (lane & 15), M, kb, lane, av);
+            load_act_lanes<AF>(a.act, a.act_rows, a.K, mt, mt * 16 < M, kb, lane, av);
 #pragma unroll
             for (int t = 0; t < 4; ++t) tile_mfma<WT, AF>(w[t], av, acc[mt][t]);
         }
@@ -304,56 +317,92 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 
     float *tflat = &tile[0][0];
     if (a.S > 1) {
+        // Split-K handshake without cache-wide maintenance: partials are written
+        // and read with device-coherent (agent-scope) atomic accesses, each wave
+        // waits for its stores to complete before the workgroup signals, and the
+        // last workgroup of the group to arrive sums the partials in split order.
         float *part = a.partial + ((size_t)s * G + g) * (MP * GROUP_N);
-        for (int e = tid; e < MP * GROUP_N; e += 256) part[e] = tflat[e];
-        __threadfence();
+        for (int e = tid; e < MP * GROUP_N; e += 256)
+            __hip_atomic_store((uint32_t *)(part + e), __float_as_uint(tflat[e]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __syncthreads();
-        if (tid == 0) is_last = (atomicAdd(&a.counters[g], 1) == a.S - 1);
+        if (tid == 0)
+            is_last = __hip_atomic_fetch_add(&a.counters[g], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
         __syncthreads();
         if (!is_last) return;
-        __threadfence();
-        for (int e = tid; e < MP * GROUP_N; e += 256) {
-            float sum = 0.0f;
-            for (int ss = 0; ss < a.S; ++ss) sum += __builtin_nontemporal_load(a.partial + ((size_t)ss * G + g) * (MP * GROUP_N) + e);
-            tflat[e] = sum;
+        constexpr int EPT = MP * GROUP_N / 256;  // tile elements per thread
+        float sum[EPT];
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) sum[k] = 0.0f;
+        for (int s0 = 0; s0 < a.S; s0 += 4) {  // four splits' loads in flight, summed in split order
+            float v[4][EPT];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int k = 0; k < EPT; ++k)
+                    v[u][k] = s0 + u < a.S ? __uint_as_float(__hip_atomic_load(
+                                                 (const uint32_t *)(a.partial + ((size_t)(s0 + u) * G + g) * (MP * GROUP_N) +
+                                                                    tid + 256 * k),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                           : 0.0f;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int k = 0; k < EPT; ++k)
+                    if (s0 + u < a.S) sum[k] += v[u][k];
         }
-        if (tid == 0) a.counters[g] = 0;
+#pragma unroll
+        for (int k = 0; k < EPT; ++k) tflat[tid + 256 * k] = sum[k];
+        if (tid == 0) __hip_atomic_store(&a.counters[g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
     }
 
     // ---- epilogue on the 16*MT x 64 tile ----
     const EpiArgs &e = a.epi;
-    if (tid < MP) {
-        float r = 1.0f;
-        if (e.ss != nullptr && tid < M) {
-            float sum = 0.0f;
-            for (int gg = 0; gg < e.ss_groups; ++gg) sum += e.ss[(size_t)gg * e.ss_stride + tid];
-            r = 1.0f / sqrtf(sum * e.inv_E + e.eps);
-        }
-        rs_s[tid] = r;
+    // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps): 16 threads per row, fixed-order tree
+    for (int m0 = 0; m0 < MP; m0 += 16) {
+        const int m = m0 + (tid >> 4), sub = tid & 15;
+        float part = 0.0f;
+        if (e.ss != nullptr && m < M)
+            for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
+        for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        if (sub == 0) rs_s[m] = (e.ss != nullptr && m < M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
     }
     __syncthreads();
 
-    if (e.kind == EPI_SCALED) {
+    if constexpr (EPI == EPI_SCALED) {
         for (int m = wave; m < M; m += 4) {
             const int n = g * GROUP_N + lane;
             float v = tile[m][lane] * rs_s[m];
             if (e.wscale) v *= e.wscale[n];
             e.out[(size_t)m * e.ld_out + n] = v;
         }
-    } else if (e.kind == EPI_RESID) {
-        for (int m = wave; m < M; m += 4) {
-            const int n = g * GROUP_N + lane;
-            float v = tile[m][lane];
-            if (e.wscale) v *= e.wscale[n];
-            float *xp = e.x + (size_t)m * e.ld_x + n;
-            const float xn = *xp + v;
-            *xp = xn;
-            write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, n, xn * e.wnext[n]);
-            const float sq = wave_sum(xn * xn);
-            if (lane == 0) e.ss_out[(size_t)g * e.ss_stride + m] = sq;
+    } else if constexpr (EPI == EPI_RESID) {
+        constexpr int RPW = MP / 4;  // rows per wave; all residual loads issued first
+        const int n = g * GROUP_N + lane;
+        const float sc = e.wscale ? e.wscale[n] : 1.0f;
+        float xv[RPW];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int m = wave + 4 * r;
+            xv[r] = m < M ? e.x[(size_t)m * e.ld_x + n] : 0.0f;
         }
-    } else if (e.kind == EPI_SWIGLU) {
+        const float wn = e.wnext[n];
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int m = wave + 4 * r;
+            if (m < M) {
+                const float xn = xv[r] + tile[m][lane] * sc;
+                e.x[(size_t)m * e.ld_x + n] = xn;
+                write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, n, xn * wn);
+                const float sq = wave_sum(xn * xn);
+                if (lane == 0) e.ss_out[(size_t)g * e.ss_stride + m] = sq;
+            }
+        }
+    } else if constexpr (EPI == EPI_SWIGLU) {
         for (int m = wave; m < M; m += 4) {
             if (lane < 32) {
                 float gv = tile[m][lane] * rs_s[m];
@@ -383,31 +432,50 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
                 }
             }
             if (lane == 0) {
-                e.am_val[(size_t)g * e.ss_stride + m] = bv;
-                e.am_idx[(size_t)g * e.ss_stride + m] = bi;
+                __hip_atomic_store((uint32_t *)(e.am_val + (size_t)g * e.ss_stride + m), __float_as_uint(bv),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(e.am_idx + (size_t)g * e.ss_stride + m, bi, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             }
         }
-        __threadfence();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __syncthreads();
-        if (tid == 0) is_last = (atomicAdd(e.am_counter, 1) == G - 1);
+        if (tid == 0)
+            is_last = __hip_atomic_fetch_add(e.am_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
         __syncthreads();
         if (!is_last) return;
-        __threadfence();
         __shared__ int best_s[MP];
-        if (tid < M) {
+        for (int m0 = 0; m0 < M; m0 += 16) {
+            const int m = m0 + (tid >> 4), sub = tid & 15;
             float bv = -INFINITY;
             int bi = 0x7fffffff;
-            for (int gg = 0; gg < G; ++gg) {
-                const float v = __builtin_nontemporal_load(e.am_val + (size_t)gg * e.ss_stride + tid);
-                const int i = __builtin_nontemporal_load(e.am_idx + (size_t)gg * e.ss_stride + tid);
-                if (v > bv || (v == bv && i < bi)) {
-                    bv = v;
-                    bi = i;
+            if (m < M)
+                for (int gg = sub; gg < G; gg += 16) {
+                    const float v = __uint_as_float(__hip_atomic_load(
+                        (const uint32_t *)(e.am_val + (size_t)gg * e.ss_stride + m), __ATOMIC_RELAXED,
+                        __HIP_MEMORY_SCOPE_AGENT));
+                    const int i = __hip_atomic_load(e.am_idx + (size_t)gg * e.ss_stride + m, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+                    if (v > bv || (v == bv && i < bi)) {
+                        bv = v;
+                        bi = i;
+                    }
+                }
+            for (int o = 8; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (ov > bv || (ov == bv && oi < bi)) {
+                    bv = ov;
+                    bi = oi;
                 }
             }
-            best_s[tid] = bi;
-            const int b = tid / e.block, i = tid % e.block;
-            if (i > 0) e.drafts[(size_t)b * (e.block - 1) + i - 1] = bi;
+            if (sub == 0 && m < M) {
+                best_s[m] = bi;
+                const int b = m / e.block, i = m % e.block;
+                if (i > 0) e.drafts[(size_t)b * (e.block - 1) + i - 1] = bi;
+            }
         }
         __syncthreads();
         if (e.target != nullptr && tid < M / e.block) {
@@ -416,27 +484,39 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
             while (n < e.block - 1 && best_s[b * e.block + 1 + n] == e.target[(size_t)b * (e.block - 1) + n]) ++n;
             e.n_ok[b] = n;
         }
-        if (tid == 0) *e.am_counter = 0;
+        if (tid == 0) __hip_atomic_store(e.am_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
-template <int WT, int AF>
+template <int WT, int AF, int EPI>
 static hipError_t launch_gemv_mt(int MT, dim3 grid, const GemvArgs &a, hipStream_t s) {
     switch (MT) {
-        case 1: hipLaunchKernelGGL((gemv_kernel<WT, AF, 1>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemv_kernel<WT, AF, 2>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((gemv_kernel<WT, AF, 4>), grid, dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((gemv_kernel<WT, AF, 8>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemv_kernel<WT, AF, 2, EPI>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemv_kernel<WT, AF, 4, EPI>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((gemv_kernel<WT, AF, 8, EPI>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <int WT, int AF>
+static hipError_t launch_gemv_epi(int MT, dim3 grid, const GemvArgs &a, hipStream_t s) {
+    switch (a.epi.kind) {
+        case EPI_SCALED: return launch_gemv_mt<WT, AF, EPI_SCALED>(MT, grid, a, s);
+        case EPI_RESID: return launch_gemv_mt<WT, AF, EPI_RESID>(MT, grid, a, s);
+        case EPI_SWIGLU: return launch_gemv_mt<WT, AF, EPI_SWIGLU>(MT, grid, a, s);
+        case EPI_LOGITS: return launch_gemv_mt<WT, AF, EPI_LOGITS>(MT, grid, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_gemv(int wdtype, int act_fmt, int MT, dim3 grid, const GemvArgs &a, hipStream_t s) {
-    if (wdtype == DFLASH_F32 && act_fmt == ACT_F32) return launch_gemv_mt<DFLASH_F32, ACT_F32>(MT, grid, a, s);
-    if (wdtype == DFLASH_BF16 && act_fmt == ACT_SPLIT3) return launch_gemv_mt<DFLASH_BF16, ACT_SPLIT3>(MT, grid, a, s);
+    if (wdtype == DFLASH_F32 && act_fmt == ACT_F32) return launch_gemv_epi<DFLASH_F32, ACT_F32>(MT, grid, a, s);
+    if (wdtype == DFLASH_BF16 && act_fmt == ACT_SPLIT3)
+        return launch_gemv_epi<DFLASH_BF16, ACT_SPLIT3>(MT, grid, a, s);
     if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_SPLIT3)
-        return launch_gemv_mt<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, grid, a, s);
+        return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, grid, a, s);
     return hipErrorInvalidValue;
 }
 

@@ -222,6 +222,10 @@ class Drafter:
             None if n_ok is None else _dev(n_ok, torch.int32, "n_ok"), s.cuda_stream, C.byref(h)))
         return StepGraph(h.value, [ring_table, id_last, n_past, logits, drafts, target, n_ok, self])
 
+    def replay_stage(self, stage: int, layer: int = 0, stream=None) -> None:
+        """Re-run one weight-streaming stage of the last block step (a single-kernel timing hook)."""
+        check(lib().dflash_replay_stage(self._ctx, stage, layer, _stream(stream)))
+
     def close(self) -> None:
         if getattr(self, "_ctx", None):
             lib().dflash_destroy(self._ctx)

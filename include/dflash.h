@@ -58,7 +58,7 @@ typedef enum {
  * Drafter geometry and storage dtypes.
  *
  * Supported shapes: head_dim 64 or 128; n_head a multiple of n_head_kv with
- * n_head / n_head_kv <= 8; block == 16; n_embd, n_ff, n_vocab,
+ * n_head / n_head_kv <= 4; block == 16; n_embd, n_ff, n_vocab,
  * n_capture * target_hidden, n_head * head_dim and n_head_kv * head_dim
  * multiples of 64; window a multiple of 64 and <= 65536; 1 <= max_batch <= 8.
  */
@@ -190,6 +190,23 @@ void dflash_graph_destroy(dflash_graph *g);
  * nearest even and saturated at +-448; both divisions in IEEE fp32. */
 int dflash_quantize_fp8_rows(const float *w, int32_t rows, int32_t cols, uint8_t *codes, float *scales,
                              void *stream);
+
+/* Stages of the block step that dflash_replay_stage can re-run. */
+typedef enum {
+    DFLASH_STAGE_QKV = 0,     /* fused q/k/v projection of one layer (attention-norm folded in) */
+    DFLASH_STAGE_O = 1,       /* output projection + residual (+ ffn-norm input of the next stage) */
+    DFLASH_STAGE_GATE_UP = 2, /* gate/up projection + SwiGLU */
+    DFLASH_STAGE_DOWN = 3     /* down projection + residual (+ next layer's norm input) */
+} dflash_stage;
+
+/* Re-run one weight-streaming stage of layer `layer` of the last block step
+ * on the activations the workspace holds now, with that step's batch; a
+ * timing hook for a single kernel (the kernel and its launch are the ones the
+ * step uses). DFLASH_STAGE_GATE_UP and DFLASH_STAGE_QKV leave the step's state
+ * consistent; DFLASH_STAGE_O and DFLASH_STAGE_DOWN add into the residual
+ * stream again, so run a full step before reading results. ESTATE before the
+ * first block step. */
+int dflash_replay_stage(dflash_ctx *ctx, int32_t stage, int32_t layer, void *stream);
 
 /* Message of the last failed call on this thread ("" if none). */
 const char *dflash_last_error(void);

@@ -100,6 +100,7 @@ def test_null_arguments_fail_before_any_gpu_work(L):
     assert L.dflash_step_graph_create(None, None, None, None, 1, None, None, None, None, None, C.byref(h)) == _lib.EINVAL
     assert L.dflash_step_graph_launch(None, None) == _lib.EINVAL
     assert L.dflash_quantize_fp8_rows(None, 1, 1, None, None, None) == _lib.EINVAL
+    assert L.dflash_replay_stage(None, 0, 0, None) == _lib.EINVAL
     L.dflash_destroy(None)
     L.dflash_graph_destroy(None)
 

@@ -36,6 +36,10 @@ int hip_fail(hipError_t e, const char *what) {
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// the q/k/v projection streams 128-column groups (8 tiles): one head of 128 per group
+constexpr int QKV_TPG = 8;
+constexpr int QKV_WN = QKV_TPG / TILES_PER_GROUP;
+
 int dtype_bytes(int dt) { return dt == DFLASH_F32 ? 4 : dt == DFLASH_BF16 ? 2 : 1; }
 
 int check_config(const dflash_config *c) {
@@ -52,6 +56,8 @@ int check_config(const dflash_config *c) {
     for (int64_t v : m64)
         if (v <= 0 || v % 64) return fail(DFLASH_EUNSUPPORTED, "dimensions must be positive multiples of 64");
     if (c->window > 65536) return fail(DFLASH_EUNSUPPORTED, "window must be <= 65536");
+    if ((int64_t)(c->n_head + 2 * c->n_head_kv) * c->head_dim % 128)
+        return fail(DFLASH_EUNSUPPORTED, "(n_head + 2 * n_head_kv) * head_dim must be a multiple of 128");
     if (c->max_batch < 1 || c->max_batch > 8) return fail(DFLASH_EUNSUPPORTED, "max_batch must be in 1..8");
     if (c->max_inject < 1) return fail(DFLASH_EINVAL, "max_inject must be >= 1");
     if (c->mask_id < 0 || c->mask_id >= c->n_vocab) return fail(DFLASH_EINVAL, "mask_id out of range");
@@ -65,10 +71,11 @@ int check_config(const dflash_config *c) {
     return DFLASH_OK;
 }
 
-// k-split of a weight-streaming launch: aim for ~768 workgroups (three per
-// CU) with at least 8 k-blocks (two per wave) in each.
+// k-split of a weight-streaming launch: aim for ~1536 workgroups (six per CU,
+// rounded to the nearest split count) with at least 8 k-blocks (two per wave)
+// in each; capped at 16 splits.
 void choose_split(int G, int KB, int &S, int &kbps) {
-    S = std::max(1, std::min((KB + 7) / 8, (768 + G - 1) / G));
+    S = std::max(1, std::min(16, std::min((KB + 7) / 8, (1536 + G / 2) / G)));
     kbps = (KB + S - 1) / S;
     S = (KB + kbps - 1) / kbps;
 }
@@ -138,13 +145,13 @@ size_t carve(dflash_ctx &x, char *base) {
     x.att_o = cv.take<float>(4ull * c.max_batch * c.n_head_kv * (NCH + 1) * G * 16 * D);
     // split-K partials: the largest S * G * Mp * 64 over the step's launches
     const int Mp = 16 * mt_for(Mmax);
-    const int shapes[5][2] = {{nqkv, E}, {E, qdim}, {2 * F, E}, {E, F}, {V, E}};
+    const int shapes[5][3] = {{nqkv, E, QKV_WN}, {E, qdim, 1}, {2 * F, E, 1}, {E, F, 1}, {V, E, 1}};
     size_t pmax = 0;
     int gmax = 0;
     for (auto &sh : shapes) {
-        int Gn = sh[0] / GROUP_N, KB = sh[1] / KBLK, S, kbps;
+        int Gn = sh[0] / (GROUP_N * sh[2]), KB = sh[1] / KBLK, S, kbps;
         choose_split(Gn, KB, S, kbps);
-        pmax = std::max(pmax, (size_t)S * Gn * Mp * GROUP_N);
+        pmax = std::max(pmax, (size_t)S * Gn * Mp * GROUP_N * sh[2]);
         gmax = std::max(gmax, Gn);
     }
     x.partial = cv.take<float>(4 * pmax);
@@ -193,8 +200,9 @@ size_t ring_bytes_of(const dflash_config &c) {
     return 2 * kv + a256(4ull * c.window);
 }
 
-int tile_matrix(const void *src, int rows, int K, int es, void *dst, int row_map, int row0, int half, hipStream_t s) {
-    HIP_TRY(launch_tile_weights(src, rows, K, es, dst, K / KBLK, row_map, row0, half, s), "weight tiling launch");
+int tile_matrix(const void *src, int rows, int K, int es, void *dst, int row_map, int row0, int half, hipStream_t s,
+                int tpg = TILES_PER_GROUP) {
+    HIP_TRY(launch_tile_weights(src, rows, K, es, dst, K / KBLK, row_map, row0, half, tpg, s), "weight tiling launch");
     return DFLASH_OK;
 }
 
@@ -254,9 +262,9 @@ int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
         TRY(tile_scales(lw.s_k, x.kvdim, x.s_kv, 0, r0, 0, s));
         TRY(tile_scales(lw.s_v, x.kvdim, x.s_kv, 0, r0 + x.kvdim, 0, s));
         LayerBufs &b = x.layer[l];
-        TRY(tile_matrix(lw.wq, x.qdim, E, esw, b.qkv, 0, 0, 0, s));
-        TRY(tile_matrix(lw.wk, x.kvdim, E, esw, b.qkv, 0, x.qdim, 0, s));
-        TRY(tile_matrix(lw.wv, x.kvdim, E, esw, b.qkv, 0, x.qdim + x.kvdim, 0, s));
+        TRY(tile_matrix(lw.wq, x.qdim, E, esw, b.qkv, 0, 0, 0, s, QKV_TPG));
+        TRY(tile_matrix(lw.wk, x.kvdim, E, esw, b.qkv, 0, x.qdim, 0, s, QKV_TPG));
+        TRY(tile_matrix(lw.wv, x.kvdim, E, esw, b.qkv, 0, x.qdim + x.kvdim, 0, s, QKV_TPG));
         TRY(tile_scales(lw.s_q, x.qdim, b.s_qkv, 0, 0, 0, s));
         TRY(tile_scales(lw.s_k, x.kvdim, b.s_qkv, 0, x.qdim, 0, s));
         TRY(tile_scales(lw.s_v, x.kvdim, b.s_qkv, 0, x.qdim + x.kvdim, 0, s));
@@ -289,31 +297,41 @@ EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
     return e;
 }
 
-int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, const EpiArgs &epi, hipStream_t s) {
+int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, const EpiArgs &epi, hipStream_t s,
+         int WN = 1) {
     GemvArgs a = {};
     a.W = W;
     a.N = N;
     a.K = K;
     a.act = act;
     a.act_rows = x.Mmax;
-    const int G = N / GROUP_N, KB = K / KBLK;
+    const int G = N / (GROUP_N * WN), KB = K / KBLK;
     choose_split(G, KB, a.S, a.kb_per_split);
     a.partial = x.partial;
     a.counters = x.counters;
     a.epi = epi;
-    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), dim3(G, a.S), a, s), "block-step GEMV launch");
+    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), WN, dim3(G, a.S), a, s), "block-step GEMV launch");
     return DFLASH_OK;
 }
 
+// q/k/v projection with the attention norm folded in; its epilogue RMS-norms
+// and ropes every q and k head (q also scaled by 1/sqrt(D))
 int stage_qkv(const dflash_ctx &x, int l, int M, hipStream_t s) {
     const LayerBufs &b = x.layer[l];
-    EpiArgs e = epi_base(x, EPI_SCALED, M);
+    EpiArgs e = epi_base(x, EPI_QKV, M);
     e.wscale = b.s_qkv;
     e.ss = x.ss_a;
     e.ss_groups = x.G_E;
     e.out = x.qkv_out;
     e.ld_out = x.nqkv;
-    return gemv(x, b.qkv, x.nqkv, x.E, x.act_a, e, s);
+    e.qdim = x.qdim;
+    e.kvdim = x.kvdim;
+    e.D = x.D;
+    e.q_norm = x.q_norm + (size_t)l * x.D;
+    e.k_norm = x.k_norm + (size_t)l * x.D;
+    e.rope_cs = x.rope_cs;
+    e.qscale = 1.0f / sqrtf((float)x.D);
+    return gemv(x, b.qkv, x.nqkv, x.E, x.act_a, e, s, QKV_WN);
 }
 
 int stage_o(const dflash_ctx &x, int l, int M, hipStream_t s) {

@@ -7,7 +7,7 @@
 
 #include <string>
 
-#include "../../include/dflash.h"
+#include "dflash.h"
 
 // ---------------------------------------------------------------------------
 // Tiling of streamed weights
@@ -34,13 +34,14 @@ constexpr int TILES_PER_GROUP = 4;
 constexpr int GROUP_N = TILE_N * TILES_PER_GROUP;  // 64 output columns per group
 constexpr int LANE_ELEMS = 16;
 
-// element offset of weight (n, k) in a tiled matrix with KB = K / 64 k-blocks and es-byte elements
-__host__ __device__ inline size_t tiled_offset(int n, int k, int KB, int es) {
+// element offset of weight (n, k) in a tiled matrix with KB = K / 64 k-blocks, es-byte elements and tpg
+// tiles per column group (4, or 8 for the q/k/v projection whose groups are 128 columns = one head)
+__host__ __device__ inline size_t tiled_offset(int n, int k, int KB, int es, int tpg = TILES_PER_GROUP) {
     const int epw = 16 / es;  // elements per 16-byte word
-    int g = n / GROUP_N, t = (n / TILE_N) % TILES_PER_GROUP, r = n % TILE_N;
+    int g = n / (TILE_N * tpg), t = (n / TILE_N) % tpg, r = n % TILE_N;
     int kb = k / KBLK, c = (k % KBLK) / LANE_ELEMS, j = k % LANE_ELEMS;
     int lane = r + 16 * c, v = j / epw, i = j % epw;
-    return (((((size_t)g * KB + kb) * TILES_PER_GROUP + t) * es + v) * 64 + lane) * epw + i;
+    return (((((size_t)g * KB + kb) * tpg + t) * es + v) * 64 + lane) * epw + i;
 }
 
 // Activation operands of the block-row kernels use the same lane order: for
@@ -158,7 +159,7 @@ __device__ __forceinline__ void write_act(void *act, int fmt, int act_rows, int 
 // ---------------------------------------------------------------------------
 // Epilogues of the split-K weight-streaming kernel
 // ---------------------------------------------------------------------------
-enum EpiKind { EPI_SCALED = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum EpiKind { EPI_SCALED = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_QKV = 4 };
 
 struct EpiArgs {
     int kind;
@@ -181,6 +182,11 @@ struct EpiArgs {
     int act_rows;         // row stride of act_out (Mmax)
     int act_K;
     float *ss_out;        // [G][ss_stride] sums of squares of the updated x
+    // EPI_QKV: per-head RMSNorm + rope of q and k in the projection output
+    int qdim, kvdim, D, block;
+    const float *q_norm, *k_norm;  // this layer's [D]
+    const float *rope_cs;          // [B][block][D/2][2]
+    float qscale;                  // 1/sqrt(D), folded into q
     // EPI_LOGITS: argmax across groups
     float *am_val;
     int *am_idx;
@@ -188,7 +194,6 @@ struct EpiArgs {
     int32_t *drafts;      // [B][block-1]
     const int32_t *target;  // [B][block-1] or null
     int32_t *n_ok;        // [B] or null
-    int block;
 };
 
 struct GemvArgs {
@@ -280,13 +285,13 @@ struct dflash_graph {
 // Launchers (kernels_*.hip)
 // ---------------------------------------------------------------------------
 hipError_t launch_tile_weights(const void *src, int src_rows, int K, int esize, void *dst, int KB, int row_map,
-                               int dst_row0, int pair_half, hipStream_t s);
+                               int dst_row0, int pair_half, int tpg, hipStream_t s);
 hipError_t launch_tile_scales(const float *src, int src_rows, float *dst, int row_map, int dst_row0, int pair_half,
                               hipStream_t s);
 hipError_t launch_vec_to_f32(const void *src, int dtype, int n, float *dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *codes, float *scales, hipStream_t s);
-hipError_t launch_gemv(int wdtype, int act_fmt, int MT, dim3 grid, const GemvArgs &a, hipStream_t s);
+hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, dim3 grid, const GemvArgs &a, hipStream_t s);
 hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s);
 hipError_t launch_split(const float *src, int rows, int K, int ld_src, void *dst, int act_fmt, int act_rows,
                         hipStream_t s);

@@ -311,11 +311,12 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 // ---------------------------------------------------------------------------
 // Non-causal sliding-window GQA attention (dflash-ops card, Method)
 // ---------------------------------------------------------------------------
-// Partial kernel: grid (NCH + 1, Hkv, B), 256 threads = 4 wavefronts. Chunk
+// Partial kernel: grid (NCH + 1, Hkv, B), 512 threads = 8 wavefronts. Chunk
 // c < NCH covers ring slots [c*CH, c*CH + CH); chunk NCH is the block's own 16
-// keys. The G*16 query vectors of kv head j (q heads jG .. jG+G-1, 16 block rows
-// each) are RMS-normed with q_norm, roped at n_past + i and scaled by
-// 1/sqrt(D); wave w handles q head jG + w.
+// keys. The q/k/v projection has already RMS-normed and roped q and the block's
+// k (q also scaled by 1/sqrt(D)). Wave w serves q head jG + (w % 4) for the
+// first (w < 4) or second half of the chunk's key tiles; the two halves merge
+// through LDS.
 //
 // Scores are computed transposed, S^T = K Q^T (keys as MFMA rows, queries as
 // columns), so that each lane holds the scores of one query for 4 keys of every
@@ -328,15 +329,12 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 // A ring key at slot s is visible to block row i when slot_pos[s] >= 0 and
 // 0 <= n_past + i - slot_pos[s] < W; block keys are always visible.
 struct AttnArgs {
-    const float *qkv;
+    const float *qkv;  // [M][nqkv]: q (normed, roped, scaled), k (normed, roped), v
     int nqkv, qdim, kvdim;
-    const float *rope_cs;
-    const float *q_norm, *k_norm;  // this layer's [D]
     void *const *rings;
     int layer, L, Hkv, W, ring_dtype, G, NCH, CH, block;
     int vt_elems;  // bf16 elements of the V^T region in LDS
     const int32_t *n_past;
-    float eps, scale;
     float *ml, *o;
 };
 
@@ -361,14 +359,20 @@ __device__ __forceinline__ void split8(const float (&v)[8], bf16x8_t (&t)[3]) {
     t[2] = __builtin_bit_cast(bf16x8_t, w2);
 }
 
+__device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
+    const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 #define MFMA_BF16(A, B, C) __builtin_amdgcn_mfma_f32_16x16x32_bf16((A), (B), (C), 0, 0, 0)
 
-template <int D, int MAXKT>
-__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+template <int D, int HKT>
+__global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     constexpr int KS = D / 32;   // MFMA k-steps over the head dimension
     constexpr int DT = D / 16;   // 16-wide tiles of the head dimension
     constexpr int KROW = D + 8;  // bf16 elements per staged K row (+8 spreads LDS banks)
-                                 // MAXKT: 16-key tiles per ring chunk (CH = 16 * MAXKT)
+                                 // HKT: 16-key tiles per half chunk (CH = 32 * HKT)
     extern __shared__ float smem[];
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -377,14 +381,13 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const bool bf16_ring = a.ring_dtype == DFLASH_BF16;
     const bool split_kv = is_block || !bf16_ring;  // fp32 keys/values need three terms
     const int nkeys = is_block ? 16 : a.CH;
-    const int nkt = nkeys / 16;            // key tiles
     const int nks2 = (nkeys + 31) / 32;    // k-steps over keys for P V (the block pads 16 keys to 32)
     const int CHP = nks2 * 32 + 4;         // V^T row length: keys padded to 32, +4 to spread LDS banks
     const int nplanes = split_kv ? 3 : 1;
-    float(*stage)[D] = (float(*)[D])smem;                              // [80][D] normed / roped q (and block k)
-    uint16_t *ksh = (uint16_t *)(smem + (64 + 16) * D);                 // [CH][KROW] bf16 ring keys
-    uint16_t *vt = ksh + (bf16_ring ? a.CH * KROW : 0);                 // [planes][D][CHP] V^T in bf16 terms
-    int *kpos = (int *)(vt + a.vt_elems);                               // [CH] positions of the chunk's slots
+    uint16_t *ksh = (uint16_t *)smem;                              // [CH][KROW] bf16 ring keys
+    uint16_t *vt = ksh + (bf16_ring ? a.CH * KROW : 0);            // [planes][D][CHP] V^T in bf16 terms
+    int *kpos = (int *)(vt + a.vt_elems);                          // [CH] positions of the chunk's slots
+    float *xch = (float *)(kpos + a.CH);                           // [4][64][DT*4 + 2] second-half results
 
     const int es = bf16_ring ? 2 : 4;
     const char *rb = (const char *)a.rings[b];
@@ -393,44 +396,23 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     const int32_t *sp = (const int32_t *)(rb + ring_pos_offset(a.L, a.Hkv, a.W, D, es));
     const size_t head_base = ((size_t)a.layer * a.Hkv + j) * a.W;  // slot-row index of slot 0
     const int s0 = c * a.CH;
+    const float *qkvb = a.qkv + (size_t)b * a.block * a.nqkv;     // this sequence's 16 rows
 
-    // ---- raw q (and block k) of this kv head: float4 loads, all issued before any use ----
-    const int nvec = NQ + (is_block ? 16 : 0);
-    {
-        constexpr int V4 = D / 4;
-        constexpr int NB = (80 * V4 + 255) / 256;
-        const int n4 = nvec * V4;
-        float4 buf[NB];
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const int idx = min(tid + 256 * u, n4 - 1);  // clamped: every lane loads, live ones store
-            const int vec = idx / V4, d4 = idx % V4;
-            const size_t m = (size_t)b * a.block + (vec % 16);
-            const size_t col = vec < NQ ? (size_t)(j * a.G + vec / 16) * D : a.qdim + (size_t)j * D;
-            buf[u] = *(const float4 *)(a.qkv + m * a.nqkv + col + 4 * d4);
-        }
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const int idx = tid + 256 * u;
-            if (idx < n4) *(float4 *)&stage[idx / V4][4 * (idx % V4)] = buf[u];
-        }
-    }
     // ---- chunk keys and values into LDS ----
     if (is_block) {
-        for (int idx = tid; idx < 3 * D * CHP; idx += 256) vt[idx] = 0;  // keys 16..31 pad the k-step
+        for (int idx = tid; idx < 3 * D * CHP; idx += 512) vt[idx] = 0;  // keys 16..31 pad the k-step
         __syncthreads();
-        for (int idx = tid; idx < 16 * D; idx += 256) {
+        for (int idx = tid; idx < 16 * D; idx += 512) {
             const int key = idx / D, d = idx % D;
-            const float v = a.qkv[((size_t)b * a.block + key) * a.nqkv + a.qdim + a.kvdim + (size_t)j * D + d];
             uint16_t t0, t1, t2;
-            split3(v, t0, t1, t2);
+            split3(qkvb[(size_t)key * a.nqkv + a.qdim + a.kvdim + (size_t)j * D + d], t0, t1, t2);
             vt[(0 * D + d) * CHP + key] = t0;
             vt[(1 * D + d) * CHP + key] = t1;
             vt[(2 * D + d) * CHP + key] = t2;
         }
     } else if (bf16_ring) {
-        // K rows and V rows: CH*D/8 16-byte words each, in batches of 8 words per thread
-        constexpr int NWORD = (16 * MAXKT * D / 8 + 255) / 256;
+        // K rows and V rows: CH*D/8 16-byte words each, in batches with all loads in flight
+        constexpr int NWORD = (32 * HKT * D / 8 + 511) / 512;
         constexpr int BATCH = NWORD < 4 ? NWORD : 4;
         const int nword = a.CH * D / 8;
         const uint16_t *kg = (const uint16_t *)Kb + (head_base + s0) * D;
@@ -440,13 +422,13 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
             uint4 kbuf[BATCH], vbuf[BATCH];
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int w = min(tid + 256 * (u0 + u), nword - 1);
+                const int w = min(tid + 512 * (u0 + u), nword - 1);  // clamped: every lane loads
                 kbuf[u] = *(const uint4 *)(kg + 8 * (size_t)w);
                 vbuf[u] = *(const uint4 *)(vg + 8 * (size_t)w);
             }
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int w = tid + 256 * (u0 + u);
+                const int w = tid + 512 * (u0 + u);
                 if (w < nword) {
                     const int key = (8 * w) / D, d = (8 * w) % D;
                     *(uint4 *)(ksh + key * KROW + d) = kbuf[u];
@@ -461,7 +443,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         }
     } else {
         // f32 ring: values split into three planes (keys are read from memory and split at use)
-        constexpr int NW4 = (16 * MAXKT * D / 4 + 255) / 256;
+        constexpr int NW4 = (32 * HKT * D / 4 + 511) / 512;
         constexpr int BATCH = NW4 < 8 ? NW4 : 8;
         const int nw4 = a.CH * D / 4;
         const float *vg = (const float *)Vb + (head_base + s0) * D;
@@ -469,10 +451,10 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         for (int u0 = 0; u0 < NW4; u0 += BATCH) {
             float4 buf[BATCH];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) buf[u] = *(const float4 *)(vg + 4 * (size_t)min(tid + 256 * (u0 + u), nw4 - 1));
+            for (int u = 0; u < BATCH; ++u) buf[u] = *(const float4 *)(vg + 4 * (size_t)min(tid + 512 * (u0 + u), nw4 - 1));
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int w = tid + 256 * (u0 + u);
+                const int w = tid + 512 * (u0 + u);
                 if (w < nw4) {
                     const int key = (4 * w) / D, d = (4 * w) % D;
                     const float f[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
@@ -489,159 +471,155 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
         }
     }
     if (!is_block)
-        for (int k = tid; k < a.CH; k += 256) kpos[k] = sp[s0 + k];
+        for (int k = tid; k < a.CH; k += 512) kpos[k] = sp[s0 + k];
     __syncthreads();
-    // ---- per-head RMSNorm + rope of q (and block k); weights and the 16 rows' cos/sin in registers ----
-    {
-        float qn[D / 64], kn[D / 64], cosr[16], sinr[16];
-        const int pair = D == 128 ? lane : (lane & 31);
-#pragma unroll
-        for (int e = 0; e < D / 64; ++e) {
-            qn[e] = a.q_norm[lane + 64 * e];
-            kn[e] = a.k_norm[lane + 64 * e];
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float2 cs = *(const float2 *)(a.rope_cs + ((size_t)b * a.block + i) * D + 2 * pair);
-            cosr[i] = cs.x;
-            sinr[i] = cs.y;
-        }
-        for (int vec = wave; vec < nvec; vec += 4) {
-            float x[D / 64];
-#pragma unroll
-            for (int e = 0; e < D / 64; ++e) x[e] = stage[vec][lane + 64 * e];
-            float cr = 0.0f, sr = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (i == (vec & 15)) {
-                    cr = cosr[i];
-                    sr = sinr[i];
-                }
-            head_norm_rope_reg<D>(x, vec < NQ ? qn : kn, cr, sr, a.eps, lane);
-#pragma unroll
-            for (int e = 0; e < D / 64; ++e) stage[vec][lane + 64 * e] = x[e];
-        }
-    }
-    __syncthreads();
-    if (wave >= a.G) return;
 
-    const int hh = wave, q = lane & 15, grp = lane >> 4;
-    // ---- Q^T operand: query q, head elements 32ks + 8grp .. +8, three terms ----
-    bf16x8_t qb[KS][3];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = stage[hh * 16 + q][32 * ks + 8 * grp + e] * a.scale;
-        split8(v, qb[ks]);
-    }
-    // ---- S^T = K Q^T, key tile kt: lane holds keys 16kt + 4grp + i (i < 4) of query q ----
-    f32x4_t st[MAXKT];
-#pragma clang loop unroll(full)
-    for (int kt = 0; kt < MAXKT; ++kt) {
-        st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        if (kt >= nkt) continue;
-        const int key = 16 * kt + q;  // A-operand row of this lane
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int d0 = 32 * ks + 8 * grp;
-            if (!split_kv) {
-                const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(ksh + key * KROW + d0));
-#pragma unroll
-                for (int t = 0; t < 3; ++t) st[kt] = MFMA_BF16(ka, qb[ks][t], st[kt]);
-            } else {
-                float kv[8];
-                if (is_block) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) kv[e] = stage[NQ + key][d0 + e];
-                } else {
-                    const float4 *kp = (const float4 *)((const float *)Kb + (head_base + s0 + key) * D + d0);
-                    const float4 k0 = kp[0], k1 = kp[1];
-                    kv[0] = k0.x; kv[1] = k0.y; kv[2] = k0.z; kv[3] = k0.w;
-                    kv[4] = k1.x; kv[5] = k1.y; kv[6] = k1.z; kv[7] = k1.w;
-                }
-                bf16x8_t ka[3];
-                split8(kv, ka);
-                // the six products with term-order sum <= 2
-                st[kt] = MFMA_BF16(ka[0], qb[ks][0], st[kt]);
-                st[kt] = MFMA_BF16(ka[0], qb[ks][1], st[kt]);
-                st[kt] = MFMA_BF16(ka[1], qb[ks][0], st[kt]);
-                st[kt] = MFMA_BF16(ka[0], qb[ks][2], st[kt]);
-                st[kt] = MFMA_BF16(ka[1], qb[ks][1], st[kt]);
-                st[kt] = MFMA_BF16(ka[2], qb[ks][0], st[kt]);
-            }
-        }
-    }
-    // ---- mask and chunk softmax statistics for query q ----
-    const int qpos = a.n_past[b] + q;
-    float mx = -INFINITY;
-#pragma clang loop unroll(full)
-    for (int kt = 0; kt < MAXKT; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bool vis = kt < nkt;
-            if (vis && !is_block) {
-                const int kp = kpos[16 * kt + 4 * grp + i];
-                const int dlt = qpos - kp;
-                vis = kp >= 0 && dlt >= 0 && dlt < a.W;
-            }
-            if (!vis) st[kt][i] = -INFINITY;
-            mx = fmaxf(mx, st[kt][i]);
-        }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float lsum = 0.0f;
-#pragma clang loop unroll(full)
-    for (int kt = 0; kt < MAXKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = (mx == -INFINITY || st[kt][i] == -INFINITY) ? 0.0f : expf(st[kt][i] - mx);
-            st[kt][i] = p;
-            lsum += p;
-        }
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-    // ---- O^T = V^T P^T over key pairs of tiles (2ks2, 2ks2 + 1) ----
+    const int hh = wave & 3, half = wave >> 2;
+    const bool active = hh < a.G;
+    const int q = lane & 15, grp = lane >> 4;
+    // key tiles of this wave: [half * HKT, half * HKT + HKT) intersected with the chunk
+    const int kt0 = half * HKT;
+    const int nkt = max(0, min(HKT, nkeys / 16 - kt0));
+    float mx = -INFINITY, lsum = 0.0f;
     f32x4_t ot[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) ot[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (active && nkt > 0) {
+        // ---- Q^T operand: query q, head elements 32ks + 8grp .. +8, three terms ----
+        bf16x8_t qb[KS][3];
+        const float *qrow = qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            float v[8];
+            load8(qrow + 32 * ks + 8 * grp, v);
+            split8(v, qb[ks]);
+        }
+        // ---- S^T = K Q^T, key tile kt: lane holds keys 16(kt0+kt) + 4grp + i (i < 4) of query q ----
+        f32x4_t st[HKT];
 #pragma clang loop unroll(full)
-    for (int ks2 = 0; ks2 < (MAXKT + 1) / 2; ++ks2) {
-        if (ks2 >= nks2) continue;
-        float pv[8];
+        for (int kt = 0; kt < HKT; ++kt) {
+            st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            if (kt >= nkt) continue;
+            const int key = 16 * (kt0 + kt) + q;  // A-operand row of this lane
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pv[i] = st[2 * ks2][i];
-            pv[4 + i] = 2 * ks2 + 1 < MAXKT ? st[(2 * ks2 + 1) % MAXKT][i] : 0.0f;
-        }
-        bf16x8_t pb[3];
-        split8(pv, pb);
-        const int k0 = 32 * ks2 + 4 * grp, k1 = 32 * ks2 + 16 + 4 * grp;  // the lane group's keys in V^T
+            for (int ks = 0; ks < KS; ++ks) {
+                const int d0 = 32 * ks + 8 * grp;
+                if (!split_kv) {
+                    const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, *(const u32x4_t *)(ksh + key * KROW + d0));
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const int d = 16 * dt + q;
-            bf16x8_t va[3];
-#pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                if (t >= nplanes) break;
-                const uint16_t *row = vt + ((size_t)t * D + d) * CHP;
-                const uint2 lo = *(const uint2 *)(row + k0);
-                const uint2 hi = *(const uint2 *)(row + k1);
-                va[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-            }
-            if (!split_kv) {
-#pragma unroll
-                for (int t = 0; t < 3; ++t) ot[dt] = MFMA_BF16(va[0], pb[t], ot[dt]);
-            } else {
-                ot[dt] = MFMA_BF16(va[0], pb[0], ot[dt]);
-                ot[dt] = MFMA_BF16(va[0], pb[1], ot[dt]);
-                ot[dt] = MFMA_BF16(va[1], pb[0], ot[dt]);
-                ot[dt] = MFMA_BF16(va[0], pb[2], ot[dt]);
-                ot[dt] = MFMA_BF16(va[1], pb[1], ot[dt]);
-                ot[dt] = MFMA_BF16(va[2], pb[0], ot[dt]);
+                    for (int t = 0; t < 3; ++t) st[kt] = MFMA_BF16(ka, qb[ks][t], st[kt]);
+                } else {
+                    float kv[8];
+                    if (is_block)
+                        load8(qkvb + (size_t)key * a.nqkv + a.qdim + (size_t)j * D + d0, kv);
+                    else
+                        load8((const float *)Kb + (head_base + s0 + key) * D + d0, kv);
+                    bf16x8_t ka[3];
+                    split8(kv, ka);
+                    // the six products with term-order sum <= 2
+                    st[kt] = MFMA_BF16(ka[0], qb[ks][0], st[kt]);
+                    st[kt] = MFMA_BF16(ka[0], qb[ks][1], st[kt]);
+                    st[kt] = MFMA_BF16(ka[1], qb[ks][0], st[kt]);
+                    st[kt] = MFMA_BF16(ka[0], qb[ks][2], st[kt]);
+                    st[kt] = MFMA_BF16(ka[1], qb[ks][1], st[kt]);
+                    st[kt] = MFMA_BF16(ka[2], qb[ks][0], st[kt]);
+                }
             }
         }
+        // ---- mask and softmax statistics of this wave's keys for query q ----
+        const int qpos = a.n_past[b] + q;
+#pragma clang loop unroll(full)
+        for (int kt = 0; kt < HKT; ++kt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bool vis = kt < nkt;
+                if (vis && !is_block) {
+                    const int kp = kpos[16 * (kt0 + kt) + 4 * grp + i];
+                    const int dlt = qpos - kp;
+                    vis = kp >= 0 && dlt >= 0 && dlt < a.W;
+                }
+                if (!vis) st[kt][i] = -INFINITY;
+                mx = fmaxf(mx, st[kt][i]);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+#pragma clang loop unroll(full)
+        for (int kt = 0; kt < HKT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = (mx == -INFINITY || st[kt][i] == -INFINITY) ? 0.0f : expf(st[kt][i] - mx);
+                st[kt][i] = p;
+                lsum += p;
+            }
+        lsum += __shfl_xor(lsum, 16, 64);
+        lsum += __shfl_xor(lsum, 32, 64);
+        // ---- O^T = V^T P^T over key pairs of tiles (2ks2, 2ks2 + 1) of this half ----
+#pragma clang loop unroll(full)
+        for (int ks2 = 0; ks2 < (HKT + 1) / 2; ++ks2) {
+            if (2 * ks2 >= nkt) continue;
+            float pv[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = st[2 * ks2][i];
+                pv[4 + i] = 2 * ks2 + 1 < HKT ? st[(2 * ks2 + 1) % HKT][i] : 0.0f;
+            }
+            bf16x8_t pb[3];
+            split8(pv, pb);
+            const int kbase = 16 * kt0 + 32 * ks2;
+            const int k0 = kbase + 4 * grp, k1 = kbase + 16 + 4 * grp;  // the lane group's keys in V^T
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int d = 16 * dt + q;
+                bf16x8_t va[3];
+#pragma unroll
+                for (int t = 0; t < 3; ++t) {
+                    if (t >= nplanes) break;
+                    const uint16_t *row = vt + ((size_t)t * D + d) * CHP;
+                    const uint2 lo = *(const uint2 *)(row + k0);
+                    // a half with one key tile has no second tile in the pair: its keys (and P) are zero
+                    const uint2 hi = 2 * ks2 + 1 < HKT ? *(const uint2 *)(row + k1) : make_uint2(0u, 0u);
+                    va[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+                }
+                if (!split_kv) {
+#pragma unroll
+                    for (int t = 0; t < 3; ++t) ot[dt] = MFMA_BF16(va[0], pb[t], ot[dt]);
+                } else {
+                    ot[dt] = MFMA_BF16(va[0], pb[0], ot[dt]);
+                    ot[dt] = MFMA_BF16(va[0], pb[1], ot[dt]);
+                    ot[dt] = MFMA_BF16(va[1], pb[0], ot[dt]);
+                    ot[dt] = MFMA_BF16(va[0], pb[2], ot[dt]);
+                    ot[dt] = MFMA_BF16(va[1], pb[1], ot[dt]);
+                    ot[dt] = MFMA_BF16(va[2], pb[0], ot[dt]);
+                }
+            }
+        }
+    }
+    // ---- merge the second half into the first through LDS ----
+    constexpr int XS = DT * 4 + 2;
+    if (half == 1 && active) {
+        float *xp = xch + ((size_t)hh * 64 + lane) * XS;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xp[dt * 4 + i] = ot[dt][i];
+        xp[DT * 4] = mx;
+        xp[DT * 4 + 1] = lsum;
+    }
+    __syncthreads();
+    if (half == 1 || !active) return;
+    {
+        const float *xp = xch + ((size_t)hh * 64 + lane) * XS;
+        const float m2 = xp[DT * 4], l2 = xp[DT * 4 + 1];
+        const float mn = fmaxf(mx, m2);
+        const float a1 = mn == -INFINITY ? 0.0f : expf(mx - mn);
+        const float a2 = mn == -INFINITY ? 0.0f : expf(m2 - mn);
+        lsum = lsum * a1 + l2 * a2;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ot[dt][i] = ot[dt][i] * a1 + xp[dt * 4 + i] * a2;
+        mx = mn;
     }
     // ---- partial (max, sum, unnormalised output) of query (hh, q) ----
     const size_t slot = (((size_t)b * a.Hkv + j) * (a.NCH + 1) + c) * NQ + hh * 16 + q;
@@ -651,21 +629,21 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a.o[slot * D + 16 * dt + 4 * grp + i] = ot[dt][i];
+        *(float4 *)(a.o + slot * D + 16 * dt + 4 * grp) = make_float4(ot[dt][0], ot[dt][1], ot[dt][2], ot[dt][3]);
 }
 
-// LDS of the partial kernel: staged q (and block k) [80][D] f32; for a bf16
-// ring the chunk's keys [CH][D+8] bf16; the V^T planes (one bf16 plane of CH
-// keys for a bf16 ring, three planes for f32 values, the block padded to 32
-// keys; every row +4 elements); the chunk's slot positions.
+// LDS of the partial kernel: for a bf16 ring the chunk's keys [CH][D+8] bf16;
+// the V^T planes (one bf16 plane of CH keys for a bf16 ring, three planes for
+// f32 values, the block padded to 32 keys; every row +4 elements); the chunk's
+// slot positions; the second-half exchange [4][64][D/16*4 + 2] f32.
 int attn_vt_elems(int D, int CH, int ring_dtype) {
     const int ring = (CH + 4) * (ring_dtype == DFLASH_BF16 ? 1 : 3);
     return (ring > 3 * 36 ? ring : 3 * 36) * D;
 }
 size_t attn_smem_bytes(int D, int CH, int ring_dtype) {
     const size_t kbytes = ring_dtype == DFLASH_BF16 ? (size_t)CH * (D + 8) * 2 : 0;
-    return (size_t)(64 + 16) * D * 4 + kbytes + (size_t)attn_vt_elems(D, CH, ring_dtype) * 2 + (size_t)CH * 4;
+    return kbytes + (size_t)attn_vt_elems(D, CH, ring_dtype) * 2 + (size_t)CH * 4 +
+           (size_t)4 * 64 * (D / 16 * 4 + 2) * 4;
 }
 
 template <int D, int KT>
@@ -677,12 +655,12 @@ static hipError_t set_attn_limit(int bytes) {
 hipError_t attention_set_smem_limit() {
     const int bytes = 160 * 1024;
     hipError_t e;
-    if ((e = set_attn_limit<128, 8>(bytes)) != hipSuccess) return e;
     if ((e = set_attn_limit<128, 4>(bytes)) != hipSuccess) return e;
     if ((e = set_attn_limit<128, 2>(bytes)) != hipSuccess) return e;
-    if ((e = set_attn_limit<64, 8>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<128, 1>(bytes)) != hipSuccess) return e;
     if ((e = set_attn_limit<64, 4>(bytes)) != hipSuccess) return e;
-    return set_attn_limit<64, 2>(bytes);
+    if ((e = set_attn_limit<64, 2>(bytes)) != hipSuccess) return e;
+    return set_attn_limit<64, 1>(bytes);
 }
 
 // Combine kernel: grid (H, B, D / 32), 256 threads. Thread t serves block row
@@ -705,20 +683,27 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombArgs a) {
     const int NQ = a.G * 16, qi = hh * 16 + i;
     const size_t base = ((size_t)b * a.Hkv + j) * (a.NCH + 1);
     const int nc = a.NCH + 1;
-    // one pass with a running maximum; chunk loads are independent of the running state
+    // one pass with a running maximum over batches of 8 chunks whose loads are all in flight together
     float mstar = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
-#pragma unroll 17
-    for (int c = 0; c < nc; ++c) {
-        const float2 ml = *(const float2 *)(a.ml + ((base + c) * NQ + qi) * 2);
-        const float2 ov = *(const float2 *)(a.o + ((base + c) * NQ + qi) * a.D + d);
-        if (ml.x != -INFINITY) {
-            const float mn = fmaxf(mstar, ml.x);
-            const float alpha = expf(mstar - mn);  // 0 when mstar is -inf
-            const float w = expf(ml.x - mn);
-            lsum = lsum * alpha + w * ml.y;
-            o0 = o0 * alpha + w * ov.x;
-            o1 = o1 * alpha + w * ov.y;
-            mstar = mn;
+    for (int c0 = 0; c0 < nc; c0 += 8) {
+        float2 mlb[8], ovb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int cc = min(c0 + u, nc - 1);
+            mlb[u] = *(const float2 *)(a.ml + ((base + cc) * NQ + qi) * 2);
+            ovb[u] = *(const float2 *)(a.o + ((base + cc) * NQ + qi) * a.D + d);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (c0 + u < nc && mlb[u].x != -INFINITY) {
+                const float mn = fmaxf(mstar, mlb[u].x);
+                const float alpha = expf(mstar - mn);  // 0 when mstar is -inf
+                const float w = expf(mlb[u].x - mn);
+                lsum = lsum * alpha + w * mlb[u].y;
+                o0 = o0 * alpha + w * ovb[u].x;
+                o1 = o1 * alpha + w * ovb[u].y;
+                mstar = mn;
+            }
         }
     }
     const float inv = 1.0f / lsum;
@@ -734,9 +719,6 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.nqkv = c->nqkv;
     a.qdim = c->qdim;
     a.kvdim = c->kvdim;
-    a.rope_cs = c->rope_cs;
-    a.q_norm = c->q_norm + (size_t)l * c->D;
-    a.k_norm = c->k_norm + (size_t)l * c->D;
     a.rings = rings;
     a.layer = l;
     a.L = c->L;
@@ -749,20 +731,18 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.vt_elems = attn_vt_elems(c->D, a.CH, c->cfg.ring_dtype);
     a.block = c->cfg.block;
     a.n_past = n_past;
-    a.eps = c->cfg.rms_eps;
-    a.scale = 1.0f / sqrtf((float)c->D);
     a.ml = c->att_ml;
     a.o = c->att_o;
     dim3 grid(c->NCH + 1, c->Hkv, B);
     const size_t smem = attn_smem_bytes(c->D, a.CH, c->cfg.ring_dtype);
-    const int kt = a.CH / 16;
-#define DFLASH_ATTN_LAUNCH(DD, KK) hipLaunchKernelGGL((attn_partial_kernel<DD, KK>), grid, dim3(256), smem, s, a)
-    if (c->D == 128 && kt == 8) DFLASH_ATTN_LAUNCH(128, 8);
-    else if (c->D == 128 && kt == 4) DFLASH_ATTN_LAUNCH(128, 4);
-    else if (c->D == 128 && kt == 2) DFLASH_ATTN_LAUNCH(128, 2);
-    else if (c->D == 64 && kt == 8) DFLASH_ATTN_LAUNCH(64, 8);
-    else if (c->D == 64 && kt == 4) DFLASH_ATTN_LAUNCH(64, 4);
-    else if (c->D == 64 && kt == 2) DFLASH_ATTN_LAUNCH(64, 2);
+    const int hkt = a.CH / 32;
+#define DFLASH_ATTN_LAUNCH(DD, KK) hipLaunchKernelGGL((attn_partial_kernel<DD, KK>), grid, dim3(512), smem, s, a)
+    if (c->D == 128 && hkt == 4) DFLASH_ATTN_LAUNCH(128, 4);
+    else if (c->D == 128 && hkt == 2) DFLASH_ATTN_LAUNCH(128, 2);
+    else if (c->D == 128 && hkt == 1) DFLASH_ATTN_LAUNCH(128, 1);
+    else if (c->D == 64 && hkt == 4) DFLASH_ATTN_LAUNCH(64, 4);
+    else if (c->D == 64 && hkt == 2) DFLASH_ATTN_LAUNCH(64, 2);
+    else if (c->D == 64 && hkt == 1) DFLASH_ATTN_LAUNCH(64, 1);
     else return hipErrorInvalidValue;
 #undef DFLASH_ATTN_LAUNCH
     hipError_t err = hipGetLastError();

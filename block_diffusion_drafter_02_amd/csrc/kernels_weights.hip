@@ -46,7 +46,8 @@ __host__ __device__ inline int tiled_row(int r, int row_map, int dst_row0, int p
 }
 
 __global__ void tile_weights_kernel(const uint8_t *__restrict__ src, int rows, int K, int esize,
-                                    uint8_t *__restrict__ dst, int KB, int row_map, int dst_row0, int pair_half) {
+                                    uint8_t *__restrict__ dst, int KB, int row_map, int dst_row0, int pair_half,
+                                    int tpg) {
     const size_t chunks = (size_t)K / LANE_ELEMS;
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)rows * chunks) return;
@@ -55,15 +56,15 @@ __global__ void tile_weights_kernel(const uint8_t *__restrict__ src, int rows, i
     const int v = tiled_row(r, row_map, dst_row0, pair_half);
     const u32x4 *s = (const u32x4 *)(src + ((size_t)r * K + k) * esize);
     const int epw = 16 / esize;  // 16 elements = esize 16-byte words, each stored with its wavefront neighbours
-    for (int w = 0; w < esize; ++w) *(u32x4 *)(dst + tiled_offset(v, k + w * epw, KB, esize) * esize) = s[w];
+    for (int w = 0; w < esize; ++w) *(u32x4 *)(dst + tiled_offset(v, k + w * epw, KB, esize, tpg) * esize) = s[w];
 }
 
 hipError_t launch_tile_weights(const void *src, int src_rows, int K, int esize, void *dst, int KB, int row_map,
-                               int dst_row0, int pair_half, hipStream_t s) {
+                               int dst_row0, int pair_half, int tpg, hipStream_t s) {
     size_t n = (size_t)src_rows * (K / LANE_ELEMS);
     dim3 grid((unsigned)((n + 255) / 256));
     hipLaunchKernelGGL(tile_weights_kernel, grid, dim3(256), 0, s, (const uint8_t *)src, src_rows, K, esize,
-                       (uint8_t *)dst, KB, row_map, dst_row0, pair_half);
+                       (uint8_t *)dst, KB, row_map, dst_row0, pair_half, tpg);
     return hipGetLastError();
 }
 
@@ -254,22 +255,25 @@ __device__ __forceinline__ void tile_mfma(const u32x4 (&w)[WTraits<WT>::NV], con
 // ---------------------------------------------------------------------------
 // Split-K weight-streaming kernel for the block rows
 // ---------------------------------------------------------------------------
-// Grid (G = N/64 column groups, S k-splits), 256 threads = 4 wavefronts.
-// Workgroup (g, s) owns the 64 output columns of group g and k-blocks
-// [s*kbps, (s+1)*kbps); its waves take every fourth k-block. Each wave keeps
+// Grid (G column groups of 64*WN columns, S k-splits), 256 threads = 4
+// wavefronts: WN along the columns (4 tiles each) and 4/WN along the
+// reduction. Workgroup (g, s) owns group g and k-blocks [s*kbps, (s+1)*kbps);
+// its waves along the reduction take every (4/WN)-th k-block. Each wave keeps
 // MT*4 16x16 accumulators (MT 16-row tiles x 4 column tiles), the waves are
 // summed in a fixed order through LDS, and when S > 1 the partial tile goes to
-// global memory; the last workgroup of the group to arrive (an agent-scope
-// atomic counter, fenced on both sides) sums the S partials in split order and
-// runs the epilogue, so results do not depend on scheduling.
-template <int WT, int AF, int MT, int EPI>
+// global memory; the last workgroup of the group to arrive sums the S partials
+// in split order and runs the epilogue, so results do not depend on scheduling.
+template <int WT, int AF, int MT, int EPI, int WN>
 __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     constexpr int NV = WTraits<WT>::NV;
     constexpr int NW = AFTraits<AF>::NW;
     constexpr int MP = MT * 16;
+    constexpr int GN = GROUP_N * WN;  // columns per group
+    constexpr int WK = 4 / WN;        // waves along the reduction
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % WN, wk = wave / WN;
     const int g = blockIdx.x, s = blockIdx.y;
-    const int G = a.N / GROUP_N, KB = a.K / KBLK;
+    const int G = a.N / GN, KB = a.K / KBLK;
     const int kb0 = s * a.kb_per_split;
     const int kb1 = min(KB, kb0 + a.kb_per_split);
     const int M = a.epi.M;
@@ -280,10 +284,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kb = kb0 + wave; kb < kb1; kb += 4) {
+    for (int kb = kb0 + wk; kb < kb1; kb += WK) {
         u32x4 w[4][NV];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) load_wtile<WT>(a.W, ((size_t)g * KB + kb) * 4 + t, lane, w[t]);
+        for (int t = 0; t < 4; ++t) load_wtile<WT>(a.W, ((size_t)g * KB + kb) * 4 * WN + 4 * wn + t, lane, w[t]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             u32x4 av[NW];
@@ -293,11 +297,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         }
     }
 
-    __shared__ float tile[MP][GROUP_N];
+    __shared__ float tile[MP][GN];
     __shared__ float rs_s[MP];
     __shared__ int is_last;
-    for (int wv = 0; wv < 4; ++wv) {
-        if (wave == wv) {
+    for (int wv = 0; wv < WK; ++wv) {
+        if (wk == wv) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -305,7 +309,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int m = mt * 16 + 4 * (lane >> 4) + i;
-                        const int col = 16 * t + (lane & 15);
+                        const int col = 64 * wn + 16 * t + (lane & 15);
                         if (wv == 0)
                             tile[m][col] = acc[mt][t][i];
                         else
@@ -321,8 +325,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         // and read with device-coherent (agent-scope) atomic accesses, each wave
         // waits for its stores to complete before the workgroup signals, and the
         // last workgroup of the group to arrive sums the partials in split order.
-        float *part = a.partial + ((size_t)s * G + g) * (MP * GROUP_N);
-        for (int e = tid; e < MP * GROUP_N; e += 256)
+        float *part = a.partial + ((size_t)s * G + g) * (MP * GN);
+        for (int e = tid; e < MP * GN; e += 256)
             __hip_atomic_store((uint32_t *)(part + e), __float_as_uint(tflat[e]), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
             is_last = __hip_atomic_fetch_add(&a.counters[g], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
         __syncthreads();
         if (!is_last) return;
-        constexpr int EPT = MP * GROUP_N / 256;  // tile elements per thread
+        constexpr int EPT = MP * GN / 256;  // tile elements per thread
         float sum[EPT];
 #pragma unroll
         for (int k = 0; k < EPT; ++k) sum[k] = 0.0f;
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 #pragma unroll
                 for (int k = 0; k < EPT; ++k)
                     v[u][k] = s0 + u < a.S ? __uint_as_float(__hip_atomic_load(
-                                                 (const uint32_t *)(a.partial + ((size_t)(s0 + u) * G + g) * (MP * GROUP_N) +
+                                                 (const uint32_t *)(a.partial + ((size_t)(s0 + u) * G + g) * (MP * GN) +
                                                                     tid + 256 * k),
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
                                            : 0.0f;
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         __syncthreads();
     }
 
-    // ---- epilogue on the 16*MT x 64 tile ----
+    // ---- epilogue on the 16*MT x GN tile ----
     const EpiArgs &e = a.epi;
     // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps): 16 threads per row, fixed-order tree
     for (int m0 = 0; m0 < MP; m0 += 16) {
@@ -373,7 +377,81 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     }
     __syncthreads();
 
-    if constexpr (EPI == EPI_SCALED) {
+    if constexpr (EPI == EPI_QKV) {
+        // columns of this group: whole heads of q (RMSNorm q_norm, rope, * 1/sqrt(D)), of k (RMSNorm
+        // k_norm, rope) or of v (as is), one wave per (row, head) vector
+        const int D = e.D, hpg = GN / D;  // heads per group
+        // the lane's norm weights and the (cos, sin) of its rope pair for all 16 block rows, loaded once
+        float qn[2], kn[2], cosr[16], sinr[16];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int d = min(lane + 64 * u, D - 1);
+            qn[u] = e.q_norm[d];
+            kn[u] = e.k_norm[d];
+        }
+        const int pair = D == 128 ? lane : (lane & 31);
+        const int b0 = (wave < M * hpg) ? (wave / hpg) / e.block : 0;  // rows of one wave share a sequence
+        for (int i = 0; i < 16; ++i) {
+            const float2 cs = *(const float2 *)(e.rope_cs + ((size_t)b0 * e.block + i) * D + 2 * pair);
+            cosr[i] = cs.x;
+            sinr[i] = cs.y;
+        }
+        for (int vec = wave; vec < M * hpg; vec += 4) {
+            const int m = vec / hpg, hg = vec % hpg;
+            const int c0 = hg * D;            // first column of the head inside the tile
+            const int n0 = g * GN + c0;       // first column of the head in the output
+            const bool is_q = n0 < e.qdim, is_k = !is_q && n0 < e.qdim + e.kvdim;
+            const int b = m / e.block, i = m % e.block;
+            float x[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int d = lane + 64 * u;
+                float v = 0.0f;
+                if (d < D) {
+                    v = tile[m][c0 + d] * rs_s[m];
+                    if (e.wscale) v *= e.wscale[n0 + d];
+                }
+                x[u] = v;
+            }
+            if (is_q || is_k) {
+                float ss = x[0] * x[0] + x[1] * x[1];
+                ss = wave_sum(ss);
+                const float r = 1.0f / sqrtf(ss / (float)D + e.eps);
+                float cn = 0.0f, sn = 0.0f;
+                if (b == b0) {
+#pragma unroll
+                    for (int k = 0; k < 16; ++k)
+                        if (k == i) {
+                            cn = cosr[k];
+                            sn = sinr[k];
+                        }
+                } else {
+                    const float2 cs = *(const float2 *)(e.rope_cs + ((size_t)b * e.block + i) * D + 2 * pair);
+                    cn = cs.x;
+                    sn = cs.y;
+                }
+                const float w0 = is_q ? qn[0] : kn[0], w1 = is_q ? qn[1] : kn[1];
+                if (D == 128) {
+                    const float x1 = x[0] * r * w0, x2 = x[1] * r * w1;
+                    x[0] = x1 * cn - x2 * sn;
+                    x[1] = x1 * sn + x2 * cn;
+                } else {  // D == 64: the pair partner of lane l is lane l ^ 32
+                    const float x1 = x[0] * r * w0;
+                    const float partner = __shfl_xor(x1, 32, 64);
+                    x[0] = lane < 32 ? x1 * cn - partner * sn : partner * sn + x1 * cn;
+                }
+                if (is_q) {
+                    x[0] *= e.qscale;
+                    x[1] *= e.qscale;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int d = lane + 64 * u;
+                if (d < D) e.out[(size_t)m * e.ld_out + n0 + d] = x[u];
+            }
+        }
+    } else if constexpr (EPI == EPI_SCALED) {
         for (int m = wave; m < M; m += 4) {
             const int n = g * GROUP_N + lane;
             float v = tile[m][lane] * rs_s[m];
@@ -488,35 +566,39 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     }
 }
 
-template <int WT, int AF, int EPI>
+template <int WT, int AF, int EPI, int WN>
 static hipError_t launch_gemv_mt(int MT, dim3 grid, const GemvArgs &a, hipStream_t s) {
     switch (MT) {
-        case 1: hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI>), grid, dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemv_kernel<WT, AF, 2, EPI>), grid, dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((gemv_kernel<WT, AF, 4, EPI>), grid, dim3(256), 0, s, a); break;
-        case 8: hipLaunchKernelGGL((gemv_kernel<WT, AF, 8, EPI>), grid, dim3(256), 0, s, a); break;
+        case 1: hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI, WN>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemv_kernel<WT, AF, 2, EPI, WN>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemv_kernel<WT, AF, 4, EPI, WN>), grid, dim3(256), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((gemv_kernel<WT, AF, 8, EPI, WN>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+// The q/k/v projection runs with 128-column groups (WN = 2, whole heads for its
+// epilogue); every other projection with 64-column groups.
 template <int WT, int AF>
-static hipError_t launch_gemv_epi(int MT, dim3 grid, const GemvArgs &a, hipStream_t s) {
+static hipError_t launch_gemv_epi(int MT, int WN, dim3 grid, const GemvArgs &a, hipStream_t s) {
+    if (a.epi.kind == EPI_QKV) return WN == 2 ? launch_gemv_mt<WT, AF, EPI_QKV, 2>(MT, grid, a, s) : hipErrorInvalidValue;
+    if (WN != 1) return hipErrorInvalidValue;
     switch (a.epi.kind) {
-        case EPI_SCALED: return launch_gemv_mt<WT, AF, EPI_SCALED>(MT, grid, a, s);
-        case EPI_RESID: return launch_gemv_mt<WT, AF, EPI_RESID>(MT, grid, a, s);
-        case EPI_SWIGLU: return launch_gemv_mt<WT, AF, EPI_SWIGLU>(MT, grid, a, s);
-        case EPI_LOGITS: return launch_gemv_mt<WT, AF, EPI_LOGITS>(MT, grid, a, s);
+        case EPI_SCALED: return launch_gemv_mt<WT, AF, EPI_SCALED, 1>(MT, grid, a, s);
+        case EPI_RESID: return launch_gemv_mt<WT, AF, EPI_RESID, 1>(MT, grid, a, s);
+        case EPI_SWIGLU: return launch_gemv_mt<WT, AF, EPI_SWIGLU, 1>(MT, grid, a, s);
+        case EPI_LOGITS: return launch_gemv_mt<WT, AF, EPI_LOGITS, 1>(MT, grid, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemv(int wdtype, int act_fmt, int MT, dim3 grid, const GemvArgs &a, hipStream_t s) {
-    if (wdtype == DFLASH_F32 && act_fmt == ACT_F32) return launch_gemv_epi<DFLASH_F32, ACT_F32>(MT, grid, a, s);
+hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, dim3 grid, const GemvArgs &a, hipStream_t s) {
+    if (wdtype == DFLASH_F32 && act_fmt == ACT_F32) return launch_gemv_epi<DFLASH_F32, ACT_F32>(MT, WN, grid, a, s);
     if (wdtype == DFLASH_BF16 && act_fmt == ACT_SPLIT3)
-        return launch_gemv_epi<DFLASH_BF16, ACT_SPLIT3>(MT, grid, a, s);
+        return launch_gemv_epi<DFLASH_BF16, ACT_SPLIT3>(MT, WN, grid, a, s);
     if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_SPLIT3)
-        return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, grid, a, s);
+        return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, WN, grid, a, s);
     return hipErrorInvalidValue;
 }
 

@@ -122,6 +122,8 @@ def main() -> int:
     ap.add_argument("--workload", default="bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=50)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (five times) to calibrate byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -264,6 +266,15 @@ def main() -> int:
                                             step_bytes(shape, wdt, rdt, n_vis[:1])["total"])
     else:
         line["cpu_baseline"] = None
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dr.device).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = n
     graph.close()
     print(json.dumps(line), flush=True)
     return 0

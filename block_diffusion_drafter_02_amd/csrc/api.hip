@@ -480,6 +480,9 @@ int dflash_ring_reset(dflash_ctx *x, void *ring, void *stream) {
     if ((uintptr_t)ring % 256) return fail(DFLASH_EINVAL, "ring must be 256-byte aligned");
     const int es = dtype_bytes(x->cfg.ring_dtype);
     const size_t kv = a256((size_t)x->L * x->Hkv * x->W * x->D * es);
+    // K and V are zeroed too: attention weights a masked slot's value by an exact 0, which only
+    // stays 0 when the value is finite
+    HIP_TRY(launch_fill_i32((int32_t *)ring, 0, 2 * kv / 4, (hipStream_t)stream), "ring reset launch");
     HIP_TRY(launch_fill_i32((int32_t *)((char *)ring + 2 * kv), -1, x->W, (hipStream_t)stream), "ring reset launch");
     return DFLASH_OK;
 }

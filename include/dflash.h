@@ -131,8 +131,10 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
                   void *stream, dflash_ctx **out);
 void dflash_destroy(dflash_ctx *ctx);
 
-/* Mark every slot of `ring` empty (slot_pos[] = -1). K/V contents are left
- * as they are; empty slots are never attended. */
+/* Mark every slot of `ring` empty (slot_pos[] = -1) and zero its K/V
+ * storage. Empty slots get attention weight exactly 0; zeroed storage keeps
+ * their contribution 0 (an arbitrary bit pattern could be NaN). A ring must be
+ * reset once before its first inject. */
 int dflash_ring_reset(dflash_ctx *ctx, void *ring, void *stream);
 
 /* Cross-layer feature fusion (dflash_engine.py page, TargetContextFeatureFuser):

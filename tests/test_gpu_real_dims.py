@@ -1,0 +1,183 @@
+"""GPU parity at the real drafter dimensions (5 layers, n_embd 6656, heads 32/8, head_dim 128, n_ff 19968,
+window 2048, block 16, vocab 8192), in the launch configuration bench.py times (the captured block step with
+the acceptance scan). The oracle computes everything itself from the same seeded inputs: the encoded context,
+the ring and the block step. The batch workload is checked on sampled sequences.
+
+Bars: slot tables, drafts and acceptance counts exact (a draft may differ only where the oracle's top-2 gap is
+within the logit tolerance); logits within the fp32 rounding-growth bar of the step's summation chain (fp32
+storage) or 2e-2 of the oracle logits' standard deviation (bf16 / fp8 storage); sampled ring values within the
+fp32 bar of the injection chain, plus one bf16 ulp for bf16 rings.
+"""
+import numpy as np
+import pytest
+
+from block_diffusion_drafter_02_amd import synth
+from oracle import dflash_oracle as O
+from tests import workload as WL
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+REAL = synth.REAL
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _inject_both(spec, dr, raw, positions, tag, seed=0):
+    """Inject `positions` (in window-sized chunks) into a fresh GPU ring and a fresh oracle ring."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import to_device
+
+    feats = synth.features(spec.shape, len(positions), spec.feature_dtype, seed=seed, tag=tag)
+    ring = dr.new_ring()
+    fdev = to_device(feats, dr.device)
+    WL.gpu_inject(dr, ring, fdev, positions, REAL.window)
+    torch.cuda.synchronize()
+    del fdev
+    cfg, w, oring = WL.oracle_side(spec, raw, feats, positions, REAL.window)
+    return ring, (cfg, w, oring), feats
+
+
+def _graph_step(dr, rings, id_last, n_past, target):
+    """The bench's launch configuration: a captured block step with the acceptance scan."""
+    torch = _torch()
+    B = len(rings)
+    table = dr.ring_table(rings)
+    il = torch.tensor(id_last, dtype=torch.int32, device=dr.device)
+    npst = torch.tensor(n_past, dtype=torch.int32, device=dr.device)
+    logits = torch.empty((16 * B, REAL.n_vocab), dtype=torch.float32, device=dr.device)
+    drafts = torch.empty((B, 15), dtype=torch.int32, device=dr.device)
+    tgt = torch.tensor(target, dtype=torch.int32, device=dr.device)
+    n_ok = torch.empty((B,), dtype=torch.int32, device=dr.device)
+    stream = torch.cuda.Stream()
+    g = dr.capture_step(table, il, npst, logits, drafts, tgt, n_ok, stream=stream)
+    with torch.cuda.stream(stream):
+        g.launch(stream)
+    stream.synchronize()
+    out = logits.cpu().numpy().astype(np.float64), drafts.cpu().numpy(), n_ok.cpu().numpy()
+    g.close()
+    return out
+
+
+def _check_sequence(spec, ref, logits, drafts, n_ok, planted, label):
+    tol = WL.logit_tol(spec, ref)
+    err = np.abs(logits - ref).max()
+    assert err <= tol, f"{label}: logits max-abs {err:.3g} > {tol:.3g}"
+    bad, ties = WL.compare_drafts(ref, drafts, tol)
+    assert not bad, f"{label}: draft mismatches at rows {bad} (near ties {ties})"
+    if not ties:
+        assert int(n_ok) == int(planted), f"{label}: n_ok {n_ok} != planted {planted}"
+    print(f"[{label}] logits max-abs err {err:.3g} (tol {tol:.3g}), near ties {ties}", flush=True)
+
+
+def _sample_ring(dr, ring, oring, spec, slots):
+    K, V, sp = dr.ring_views(ring)
+    np.testing.assert_array_equal(sp.cpu().numpy(), oring.slot_pos.astype(np.int32))
+    for l in (0, REAL.n_layer - 1):
+        Kg = K[l][:, slots].float().cpu().numpy().astype(np.float64)
+        Vg = V[l][:, slots].float().cpu().numpy().astype(np.float64)
+        Ko, Vo = oring.K[l][:, slots], oring.V[l][:, slots]
+        WL.check_ring_values(spec, Kg, Ko, f"ring K layer {l}")
+        WL.check_ring_values(spec, Vg, Vo, f"ring V layer {l}")
+
+
+def _targets(ref_logits_list, st):
+    drafts = np.stack([O.greedy_drafts(r) for r in ref_logits_list])
+    return synth.planted_targets(drafts, st["mismatch"][: len(drafts)], st["filler"][: len(drafts)], REAL.n_vocab)
+
+
+def test_real_bf16_full_ring_headline_step(gpu):
+    """bf16 weights and ring, positions 0..2047 injected at once, n_past 2048."""
+    from block_diffusion_drafter_02_amd.drafter import Drafter
+
+    spec = WL.Spec(REAL, "bf16", "bf16", "bf16")
+    raw = synth.weights(REAL, "bf16", seed=0)
+    dr = Drafter(REAL, raw, "bf16", "bf16", "bf16", max_batch=1, max_inject=REAL.window)
+    ring, (cfg, w, oring), _ = _inject_both(spec, dr, raw, np.arange(2048), "real.bf16.feats")
+    _sample_ring(dr, ring, oring, spec, [0, 1, 777, 2047])
+    st = synth.step_inputs(REAL, 1, seed=11)
+    ref = O.block_forward(cfg, w, oring, O.block_ids(cfg, int(st["id_last"][0])), 2048)
+    tgt = _targets([ref], st)
+    logits, drafts, n_ok = _graph_step(dr, [ring], st["id_last"], [2048], tgt)
+    _check_sequence(spec, ref, logits, drafts[0], n_ok[0], st["mismatch"][0], "bf16 n_past 2048")
+
+
+def test_real_f32_wrapped_ring_step(gpu):
+    """fp32 weights and ring, 2300 positions injected as [0, 2048) then [2048, 2300) so the ring wraps."""
+    from block_diffusion_drafter_02_amd.drafter import Drafter
+
+    spec = WL.Spec(REAL, "f32", "f32", "f32")
+    raw = synth.weights(REAL, "f32", seed=0)
+    dr = Drafter(REAL, raw, "f32", "f32", "f32", max_batch=1, max_inject=REAL.window)
+    ring, (cfg, w, oring), _ = _inject_both(spec, dr, raw, np.arange(2300), "real.f32.feats")
+    assert oring.slot_pos[0] == 2048 and oring.slot_pos[251] == 2299 and oring.slot_pos[252] == 252
+    _sample_ring(dr, ring, oring, spec, [0, 251, 252, 2047])
+    st = synth.step_inputs(REAL, 1, seed=12)
+    ref = O.block_forward(cfg, w, oring, O.block_ids(cfg, int(st["id_last"][0])), 2300)
+    tgt = _targets([ref], st)
+    logits, drafts, n_ok = _graph_step(dr, [ring], st["id_last"], [2300], tgt)
+    _check_sequence(spec, ref, logits, drafts[0], n_ok[0], st["mismatch"][0], "f32 n_past 2300")
+
+
+def test_real_bf16_batch8_sampled_sequences(gpu):
+    """Eight sequences with n_past ~ U[64, 6000] (partial and wrapped rings), rows sequence-major; the oracle
+    checks three of them (the shortest, the longest and one in between)."""
+    from block_diffusion_drafter_02_amd.drafter import Drafter
+
+    spec = WL.Spec(REAL, "bf16", "bf16", "bf16")
+    raw = synth.weights(REAL, "bf16", seed=0)
+    dr = Drafter(REAL, raw, "bf16", "bf16", "bf16", max_batch=8, max_inject=REAL.window)
+    n_pasts = [int(v) for v in synth.batch_n_past(8, seed=0)]
+    order = np.argsort(n_pasts)
+    checked = [int(order[0]), int(order[4]), int(order[-1])]
+    rings, orefs = [], {}
+    for b, n in enumerate(n_pasts):
+        pos = np.arange(max(0, n - REAL.window), n)
+        if b in checked:
+            ring, o, _ = _inject_both(spec, dr, raw, pos, f"real.batch.feats{b}")
+            orefs[b] = o
+        else:
+            from block_diffusion_drafter_02_amd.drafter import to_device
+
+            ring = dr.new_ring()
+            f = to_device(synth.features(REAL, len(pos), "bf16", seed=0, tag=f"real.batch.feats{b}"), dr.device)
+            WL.gpu_inject(dr, ring, f, pos, REAL.window)
+            del f
+        rings.append(ring)
+    st = synth.step_inputs(REAL, 8, seed=13)
+    refs = {b: O.block_forward(o[0], o[1], o[2], O.block_ids(o[0], int(st["id_last"][b])), n_pasts[b])
+            for b, o in orefs.items()}
+    target = np.array(st["filler"], dtype=np.int32)
+    for b, r in refs.items():
+        target[b] = synth.planted_targets(O.greedy_drafts(r)[None], st["mismatch"][b:b + 1], st["filler"][b:b + 1],
+                                          REAL.n_vocab)[0]
+    logits, drafts, n_ok = _graph_step(dr, rings, st["id_last"], n_pasts, target)
+    for b in checked:
+        _check_sequence(spec, refs[b], logits[16 * b:16 * (b + 1)], drafts[b], n_ok[b], st["mismatch"][b],
+                        f"batch seq {b} n_past {n_pasts[b]}")
+
+
+def test_real_fp8_weights_with_bulk_inject(gpu):
+    """FP8 E4M3 layer and lm_head weights (per-row scales), bf16 ring: context 0..2047, then a bulk injection of
+    512 new positions [2048, 2560) before the step at n_past 2560; the quantisation itself is bit-exact."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter, quantize_fp8_rows
+
+    spec = WL.Spec(REAL, "fp8", "bf16", "bf16")
+    raw = synth.weights(REAL, "fp8", seed=0)
+    rows = raw["lm_head"][:256]
+    codes, scales = quantize_fp8_rows(torch.from_numpy(rows).cuda())
+    oc, osc = O.quantize_fp8_rows(rows)
+    np.testing.assert_array_equal(codes.cpu().numpy(), oc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), osc)
+    dr = Drafter(REAL, raw, "fp8", "bf16", "bf16", max_batch=1, max_inject=REAL.window)
+    ring, (cfg, w, oring), _ = _inject_both(spec, dr, raw, np.arange(2560), "real.fp8.feats")
+    _sample_ring(dr, ring, oring, spec, [0, 511, 512, 2047])
+    st = synth.step_inputs(REAL, 1, seed=14)
+    ref = O.block_forward(cfg, w, oring, O.block_ids(cfg, int(st["id_last"][0])), 2560)
+    tgt = _targets([ref], st)
+    logits, drafts, n_ok = _graph_step(dr, [ring], st["id_last"], [2560], tgt)
+    _check_sequence(spec, ref, logits, drafts[0], n_ok[0], st["mismatch"][0], "fp8 n_past 2560")

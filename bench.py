@@ -33,11 +33,13 @@ COUNTERS = os.path.join(ROOT, "profiles", "gate_up_gemv_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "block_diffusion_drafter_02_amd", "csrc", "kernels_weights.hip")
 
 WORKLOADS = {
-    # name: (weight dtype, ring dtype, feature dtype, batch, n_past list or None)
-    "bf16": ("bf16", "bf16", "bf16", 1),
-    "f32": ("f32", "f32", "f32", 1),
-    "bf16-batch8": ("bf16", "bf16", "bf16", 8),
+    # name: (weight dtype, ring dtype, feature dtype, batch, positions injected before every step)
+    "bf16": ("bf16", "bf16", "bf16", 1, 0),
+    "f32": ("f32", "f32", "f32", 1, 0),
+    "bf16-batch8": ("bf16", "bf16", "bf16", 8, 0),
+    "fp8-inject512": ("fp8", "bf16", "bf16", 1, 512),
 }
+FEATURE_POOL = 4  # distinct resident feature blocks cycled by the per-step inject (content does not change cost)
 
 
 def esize(dt: str) -> float:
@@ -62,6 +64,22 @@ def step_bytes(shape, wdt: str, rdt: str, n_vis: list[int]) -> dict:
     return {"weights": w, "ring": ring, "other": norms + embed + logits, "total": w + ring + norms + embed + logits}
 
 
+def inject_bytes(shape, T: int, wdt: str, rdt: str, fdt: str) -> dict:
+    """Algorithmic HBM bytes of encoding and injecting T positions: the features and fc once, the fused
+    wk/wv of all layers once (plus fp8 row scales), h [T, n_embd] f32 written once and read once, the ring
+    K/V entries and slot table written."""
+    E, L, C = shape.n_embd, shape.n_layer, shape.n_capture * shape.target_hidden
+    aux = "f32" if wdt == "f32" else "bf16"
+    kvrows = L * 2 * shape.kv_dim
+    w = C * E * esize(aux) + kvrows * E * esize(wdt) + (kvrows * 4 if wdt == "fp8" else 0)
+    io = T * C * esize(fdt) + 2 * T * E * 4 + T * 4
+    ring = T * kvrows * esize(rdt) + T * 4
+    flops_enc = 2.0 * T * C * E
+    flops_kv = 2.0 * T * E * kvrows
+    return {"weights": w, "io": io, "ring": ring, "total": w + io + ring, "flops_encode": flops_enc,
+            "flops_kv": flops_kv}
+
+
 def visible_slots(n_past: int, window: int, block: int) -> int:
     """Ring slots visible to at least one block row when positions 0..n_past-1 were injected in order."""
     lo = max(0, n_past - window)  # oldest position still held by the ring
@@ -84,9 +102,11 @@ def read_traffic(bytes_per_launch_alg: float):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes):
-    """The oracle, as it stands, for one block step of one sequence at the same dimensions on a synthetic ring
-    with the same fill; returns the rate in the metric's unit (algorithmic GB/s)."""
+def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes, inject_feats=None, min_seconds=10.0,
+                 max_seconds=30.0):
+    """The oracle, as it stands, for block steps of one sequence at the same dimensions on a synthetic ring
+    with the same fill (each preceded by encoding and injecting ``inject_feats`` when given); returns the rate
+    in the metric's unit (algorithmic GB/s)."""
     from oracle import dflash_oracle as O
 
     cfg = O.Config.from_shape(shape, rdt)
@@ -105,13 +125,31 @@ def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
-    t0 = time.perf_counter()
-    O.block_forward(cfg, w, ring, O.block_ids(cfg, 1), n_past)
-    dt = time.perf_counter() - t0
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds_per_step": round(dt, 3),
-            "sample": f"one block step of one sequence (5 layers + lm_head) at the same dimensions and dtypes, "
-                      f"ring filled to n_past={n_past} with synthetic values (content does not change the cost)"}
+    if wdt == "fp8":
+        # the GPU quantises at setup, outside its clock; so does the oracle here
+        for l in range(cfg.n_layer):
+            for name in O.Weights.MATS:
+                w.fp8_codes((l, name))
+        w.fp8_codes("lm_head")
+    np_cur = n_past
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        if inject_feats is not None:
+            T = inject_feats.shape[0]
+            O.inject(cfg, w, ring, O.encode(cfg, w, inject_feats), np.arange(np_cur, np_cur + T))
+            np_cur += T
+        O.block_forward(cfg, w, ring, O.block_ids(cfg, 1 + steps), np_cur)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or dt / steps * (steps + 1) > max_seconds:
+            break
+    per = dt / steps
+    return {"value": round(total_bytes / per / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seconds_per_step": round(per, 3), "steps": steps,
+            "sample": f"{steps} block steps of one sequence (5 layers + lm_head) at the same dimensions and dtypes"
+                      f"{', each after injecting %d positions' % inject_feats.shape[0] if inject_feats is not None else ''}, "
+                      f"ring filled to n_past={n_past} with synthetic values (content does not change the cost); "
+                      f"the rate is this workload's algorithmic bytes per step over the oracle's time per step"}
 
 
 def main() -> int:
@@ -135,7 +173,7 @@ def main() -> int:
     from block_diffusion_drafter_02_amd import _lib, synth
     from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
 
-    wdt, rdt, fdt, B = WORKLOADS[args.workload]
+    wdt, rdt, fdt, B, T_inj = WORKLOADS[args.workload]
     shape = synth.REAL
     t_setup = time.perf_counter()
     print(f"[bench] generating {args.workload} weights", file=sys.stderr, flush=True)
@@ -162,8 +200,17 @@ def main() -> int:
     table = dr.ring_table(rings)
     n_vis = [visible_slots(n, shape.window, shape.block) for n in n_pasts]
     nb = step_bytes(shape, wdt, rdt, n_vis)
-
     K, W = args.steps, args.warmup
+    ib = None
+    if T_inj:
+        # every step first injects T_inj new positions [n_past, n_past + T_inj), then steps at the new n_past
+        ib = inject_bytes(shape, T_inj, wdt, rdt, fdt)
+        pool = [to_device(synth.features(shape, T_inj, fdt, seed=0, tag=f"bench.inject{i}"), dr.device)
+                for i in range(FEATURE_POOL)]
+        h_inj = torch.empty((T_inj, shape.n_embd), dtype=torch.float32, device=dr.device)
+        starts = n_pasts[0] + T_inj * np.arange(W + K + 1, dtype=np.int64)
+        pos_all = torch.from_numpy((starts[:, None] + np.arange(T_inj)[None]).astype(np.int32)).to(dr.device)
+        np_all = torch.from_numpy((starts[1:, None]).astype(np.int32)).to(dr.device)
     ids_all = torch.from_numpy(synth.integers(0, "bench.id_last", (W + K, B), 0, shape.n_vocab)).to(dr.device)
     tgt_all = torch.from_numpy(synth.integers(0, "bench.target", (W + K, B, 15), 0, shape.n_vocab)).to(dr.device)
     il = ids_all[0].clone()
@@ -176,8 +223,15 @@ def main() -> int:
     graph = dr.capture_step(table, il, npst, logits, drafts, target, n_ok, stream=stream)
     setup_s = time.perf_counter() - t_setup
 
+    def inject_step(k):
+        dr.encode(pool[k % FEATURE_POOL], h_inj, stream=stream)
+        dr.inject(rings[0], h_inj, pos_all[k], stream=stream)
+        npst.copy_(np_all[k])
+
     with torch.cuda.stream(stream):
         def step(k):
+            if T_inj:
+                inject_step(k)
             il.copy_(ids_all[k])
             target.copy_(tgt_all[k])
             graph.launch(stream)
@@ -202,7 +256,7 @@ def main() -> int:
         g1.record(stream)
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / K
-        # dominant kernel: the gate/up GEMV of layer 0, launched alone on the same stream
+        # dominant kernel of the block step: the gate/up GEMV of layer 0, launched alone on the same stream
         r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(3):
             dr.replay_stage(_lib.STAGE_GATE_UP, 0, stream)
@@ -212,9 +266,25 @@ def main() -> int:
         r1.record(stream)
         torch.cuda.synchronize()
         gu_ms = r0.elapsed_time(r1) / args.stage_reps
+        inj = None
+        if T_inj:
+            # the per-step injection alone (encode GEMM + norm, then the fused wk/wv GEMM + ring writes) and
+            # the encode alone, on the same stream; the ring is re-filled at positions already written
+            reps = max(5, min(args.stage_reps, 20))
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            for k in range(reps):
+                inject_step(W + K - 1 - (k % 4))
+            e[1].record(stream)
+            for k in range(reps):
+                dr.encode(pool[k % FEATURE_POOL], h_inj, stream=stream)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            inj = {"inject_us": e[0].elapsed_time(e[1]) / reps * 1e3, "encode_us": e[1].elapsed_time(e[2]) / reps * 1e3}
 
     ms = wall * 1e3 / K
-    value = nb["total"] / (ms * 1e-3) / 1e9
+    total = nb["total"] + (ib["total"] if ib else 0)
+    value = total / (ms * 1e-3) / 1e9
     E, F = shape.n_embd, shape.n_ff
     gu_bytes = 2 * F * E * esize(wdt) + 16 * B * E * 4 + 16 * B * F * 4
     if wdt == "fp8":
@@ -236,14 +306,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if wdt == "f32" else "bf16x3-split/f32-accumulate",
+        "dtype": "f32",
         "data": "synthetic (seeded N(0, 1/fan_in) weights, N(0,1) target features, uniform token ids)",
         "config": {
             "workload": f"DFlash drafter block step + acceptance, real dims (5 layers, n_embd 6656, heads 32/8, "
                         f"head_dim 128, n_ff 19968, window 2048, block 16, vocab 8192), {wdt} weights, {rdt} ring, "
                         f"batch {B}, n_past {n_pasts}",
             "batch": B,
-            "algorithmic_bytes_per_step": nb["total"],
+            "algorithmic_bytes_per_step": total,
             "weight_bytes_per_step": nb["weights"],
             "ring_bytes_per_step": nb["ring"],
         },
@@ -260,10 +330,22 @@ def main() -> int:
         },
         "setup_s": round(setup_s, 1),
     }
+    if T_inj:
+        line["config"]["workload"] += f", {T_inj} positions injected before every step"
+        line["config"]["inject_bytes_per_step"] = ib["total"]
+        line["inject"] = {
+            "positions": T_inj,
+            "inject_us": round(inj["inject_us"], 2),
+            "encode_us": round(inj["encode_us"], 2),
+            "encode_tflops": round(ib["flops_encode"] / (inj["encode_us"] * 1e-6) / 1e12, 1),
+            "inject_gbs": round(ib["total"] / (inj["inject_us"] * 1e-6) / 1e9, 1),
+            "block_step_us_est": round(ms * 1e3 - inj["inject_us"], 2),
+        }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(shape, raw, wdt, rdt, n_pasts[0],
-                                            step_bytes(shape, wdt, rdt, n_vis[:1])["total"])
+        line["cpu_baseline"] = cpu_baseline(
+            shape, raw, wdt, rdt, n_pasts[0], step_bytes(shape, wdt, rdt, n_vis[:1])["total"] + (ib["total"] if ib else 0),
+            inject_feats=synth.features(shape, T_inj, fdt, seed=0, tag="bench.inject0") if T_inj else None)
     else:
         line["cpu_baseline"] = None
     if args.calibrate_copy_mib:

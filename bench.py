@@ -160,6 +160,8 @@ def main() -> int:
     ap.add_argument("--workload", default="bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=50)
+    ap.add_argument("--path", default="auto", choices=["auto", "kernels", "persistent"],
+                    help="block-step path (auto: the persistent chain for one sequence)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (five times) to calibrate byte counters")
     args = ap.parse_args()
@@ -183,6 +185,7 @@ def main() -> int:
     else:
         n_pasts = [int(v) for v in synth.batch_n_past(B, seed=0)]
     dr = Drafter(shape, raw, wdt, rdt, fdt, max_batch=B, max_inject=shape.window)
+    dr.set_path({"auto": _lib.PATH_AUTO, "kernels": _lib.PATH_KERNELS, "persistent": _lib.PATH_PERSISTENT}[args.path])
     print("[bench] injecting context", file=sys.stderr, flush=True)
     rings = []
     for b, n in enumerate(n_pasts):
@@ -313,6 +316,7 @@ def main() -> int:
                         f"head_dim 128, n_ff 19968, window 2048, block 16, vocab 8192), {wdt} weights, {rdt} ring, "
                         f"batch {B}, n_past {n_pasts}",
             "batch": B,
+            "path": "persistent" if dr.step_path(B) == _lib.PATH_PERSISTENT else "kernels",
             "algorithmic_bytes_per_step": total,
             "weight_bytes_per_step": nb["weights"],
             "ring_bytes_per_step": nb["ring"],

@@ -17,6 +17,7 @@ DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 
 OK, EINVAL, ERANGE, EUNSUPPORTED, EHIP, ESTATE = 0, -1, -2, -3, -4, -5
 STAGE_QKV, STAGE_O, STAGE_GATE_UP, STAGE_DOWN = 0, 1, 2, 3
+PATH_AUTO, PATH_KERNELS, PATH_PERSISTENT = 0, 1, 2
 
 
 class Config(C.Structure):
@@ -63,6 +64,9 @@ SYMBOLS = {
     "dflash_graph_destroy": (None, [C.c_void_p]),
     "dflash_replay_stage": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
     "dflash_quantize_fp8_rows": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "dflash_set_path": (C.c_int, [C.c_void_p, C.c_int32]),
+    "dflash_step_path": (C.c_int32, [C.c_void_p, C.c_int32]),
+    "dflash_check_device": (C.c_int, [C.c_void_p, C.c_void_p]),
     "dflash_last_error": (C.c_char_p, []),
 }
 

@@ -82,6 +82,29 @@ void choose_split(int G, int KB, int &S, int &kbps) {
 
 int mt_for(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
 
+// Partial slots per column group of a chain phase with G groups of KB k-blocks
+// each. The phase's n = min(workgroups, G*KB) <= PSTEP_MAX_WG workgroups own
+// contiguous runs of at least m = floor(G*KB / n) >= 1 k-blocks, so a group
+// meets at most ceil((KB - 1) / m) + 1 <= min(KB, 2 ceil(n / G)) + 2 of them
+// (m >= G*KB / (2n) when G*KB >= n). prepare_chain checks the exact counts.
+int pchain_pmax(int G, int KB) {
+    const int c = 2 * ((PSTEP_MAX_WG + G - 1) / G);
+    return std::min(KB, c) + 2;
+}
+
+// Largest number of workgroups that share one column group of a chain phase with nwg workgroups (exact).
+int pchain_pieces(int G, int KB, int nwg) {
+    const long long U = (long long)G * KB;
+    const long long n = std::min<long long>(nwg, U);
+    int worst = 0;
+    for (int g = 0; g < G; ++g) {
+        const long long u0 = (long long)g * KB, u1 = u0 + KB - 1;
+        const long long w0 = ((u0 + 1) * n - 1) / U, w1 = ((u1 + 1) * n - 1) / U;
+        worst = std::max(worst, (int)(w1 - w0 + 1));
+    }
+    return worst;
+}
+
 struct Carver {
     char *base;
     size_t off = 0;
@@ -170,6 +193,20 @@ size_t carve(dflash_ctx &x, char *base) {
     if (c.aux_dtype == DFLASH_BF16 && c.feature_dtype == DFLASH_F32) x.enc_act = cv.take<void>(6ull * T * Cin);
     x.inj_act = act_fmt == ACT_SPLIT3 ? cv.take<void>(6ull * T * E) : nullptr;
     x.inj_kv = cv.take<float>(4ull * T * L * 2 * kvdim);
+
+    // persistent chain: partial slots for the most workgroups a launch may have
+    x.x2 = cv.take<float>(4ull * Mmax * E);
+    x.pargs = cv.take<PStepArgs>(sizeof(PStepArgs));
+    size_t ppmax = 0;
+    int pgmax = 0;
+    for (auto &sh : shapes) {
+        const int Gn = sh[0] / (GROUP_N * sh[2]), KBn = sh[1] / KBLK;
+        ppmax = std::max(ppmax, (size_t)Gn * pchain_pmax(Gn, KBn) * 16 * GROUP_N * sh[2]);
+        pgmax = std::max(pgmax, Gn);
+    }
+    x.ppartial = cv.take<float>(4 * ppmax);
+    x.n_psync = 4 + pgmax;
+    x.psync = cv.take<int>(4ull * x.n_psync);
     return cv.off;
 }
 
@@ -235,6 +272,8 @@ int check_weights(const dflash_config &c, const dflash_weights *w) {
     return DFLASH_OK;
 }
 
+int prepare_chain(dflash_ctx &x, hipStream_t s);
+
 int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
     const dflash_config &c = x.cfg;
     const int E = x.E, L = x.L, D = x.D, F = x.F, V = x.V;
@@ -281,7 +320,89 @@ int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
     TRY(tile_scales(w->s_lm_head, V, x.s_lm, 0, 0, 0, s));
     HIP_TRY(launch_fill_i32(x.counters, 0, x.n_counters, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.am_counter, 0, 1, s), "counter reset");
+    HIP_TRY(launch_fill_i32(x.psync, 0, x.n_psync, s), "counter reset");
+    return prepare_chain(x, s);
+}
+
+// Arguments of the persistent chain, kept in the workspace for the life of the context.
+int prepare_chain(dflash_ctx &x, hipStream_t s) {
+    x.pchain_wg = 0;
+    x.path = DFLASH_PATH_AUTO;
+    const int nwg = pchain_grid(&x);
+    if (nwg < 1) return DFLASH_OK;  // the per-launch kernels serve every step
+    int rate_khz = 0;
+    HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, x.device), "wall clock rate query");
+    PStepArgs a = {};
+    a.L = x.L;
+    a.E = x.E;
+    a.F = x.F;
+    a.V = x.V;
+    a.D = x.D;
+    a.nqkv = x.nqkv;
+    a.qdim = x.qdim;
+    a.kvdim = x.kvdim;
+    a.G_E = x.G_E;
+    a.block = x.cfg.block;
+    a.mask_id = x.cfg.mask_id;
+    a.aux_dtype = x.cfg.aux_dtype;
+    a.act_fmt = x.act_fmt;
+    a.act_rows = x.Mmax;
+    a.eps = x.cfg.rms_eps;
+    a.inv_E = 1.0f / (float)x.E;
+    a.qscale = 1.0f / sqrtf((float)x.D);
+    a.tok_embd = x.tok_embd;
+    a.inv_freq = x.inv_freq;
+    a.attn_norm = x.attn_norm;
+    a.ffn_norm = x.ffn_norm;
+    a.q_norm = x.q_norm;
+    a.k_norm = x.k_norm;
+    a.output_norm = x.output_norm;
+    for (int l = 0; l < x.L; ++l) {
+        const LayerBufs &b = x.layer[l];
+        a.layer[l] = PLayer{b.qkv, b.o, b.gu, b.down, b.s_qkv, b.s_o, b.s_gu, b.s_down};
+    }
+    a.lm = x.lm;
+    a.s_lm = x.s_lm;
+    a.x = x.x;
+    a.x2 = x.x2;
+    a.act_a = x.act_a;
+    a.act_f = x.act_f;
+    a.act_d = x.act_d;
+    a.act_o = x.act_o;
+    a.ss_a = x.ss_a;
+    a.ss_f = x.ss_f;
+    a.qkv_out = x.qkv_out;
+    a.rope_cs = x.rope_cs;
+    a.ss_stride = x.Mmax;
+    a.partial = x.ppartial;
+    const int phase_g[5] = {x.nqkv / (GROUP_N * QKV_WN), x.E / GROUP_N, 2 * x.F / GROUP_N, x.E / GROUP_N,
+                            x.V / GROUP_N};
+    const int phase_kb[5] = {x.E / KBLK, x.qdim / KBLK, x.E / KBLK, x.F / KBLK, x.E / KBLK};
+    for (int i = 0; i < 5; ++i) {
+        a.pmax[i] = pchain_pmax(phase_g[i], phase_kb[i]);
+        if (pchain_pieces(phase_g[i], phase_kb[i], nwg) > a.pmax[i])
+            return fail(DFLASH_EHIP, "internal: chain partial slots too few (phase %d)", i);
+    }
+    a.am_val = x.am_val;
+    a.am_idx = x.am_idx;
+    a.bar = (unsigned *)x.psync;
+    a.err = x.psync + 1;
+    a.am_counter = x.psync + 2;
+    a.counters = x.psync + 4;
+    a.spin_ticks = (long long)rate_khz * 1000;  // one second
+    HIP_TRY(hipMemcpyAsync(x.pargs, &a, sizeof a, hipMemcpyHostToDevice, s), "chain argument upload");
+    HIP_TRY(hipStreamSynchronize(s), "chain argument upload");
+    x.pchain_wg = nwg;
     return DFLASH_OK;
+}
+
+// DFLASH_PATH_AUTO takes the per-launch kernels: on MI355X at the real drafter
+// dimensions the persistent chain's 768 resident workgroups stream the weights
+// more slowly than the per-launch grids (the third workgroup of every CU lags,
+// and every phase waits for the slowest), so it stays an explicit choice.
+bool use_chain(const dflash_ctx &x, int B) {
+    if (B != 1 || x.pchain_wg < 1) return false;
+    return x.path == DFLASH_PATH_PERSISTENT;
 }
 
 EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
@@ -393,6 +514,18 @@ int stage_lm(const dflash_ctx &x, int M, float *logits, int32_t *drafts, const i
 int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const int32_t *block_ids,
              const int32_t *n_past, int B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
              hipStream_t s) {
+    if (use_chain(x, B)) {
+        // persistent chain: embed + q/k/v(0); per layer attention, combine, then Wo .. q/k/v(l+1) or lm_head
+        const PStepIO io{id_last, block_ids, n_past, logits, drafts, target, n_ok};
+        HIP_TRY(launch_fill_i32(x.psync, 0, x.n_psync, s), "chain counter reset");
+        HIP_TRY(launch_pchain_head(&x, x.pargs, io, x.pchain_wg, s), "chain launch");
+        for (int l = 0; l < x.L; ++l) {
+            HIP_TRY(launch_attention(&x, l, rings, n_past, B, s), "attention launch");
+            HIP_TRY(launch_pchain_layer(&x, x.pargs, io, l, 1 + 3 * l, x.pchain_wg, s), "chain launch");
+        }
+        x.last_B = B;
+        return DFLASH_OK;
+    }
     const int M = 16 * B;
     HIP_TRY(launch_embed(&x, id_last, block_ids, n_past, B, s), "embed launch");
     for (int l = 0; l < x.L; ++l) {
@@ -632,6 +765,34 @@ int dflash_replay_stage(dflash_ctx *x, int32_t stage, int32_t layer, void *strea
         case DFLASH_STAGE_DOWN: return stage_down(*x, layer, M, s);
         default: return fail(DFLASH_EINVAL, "unknown stage %d", stage);
     }
+}
+
+int dflash_set_path(dflash_ctx *x, int32_t path) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    if (path != DFLASH_PATH_AUTO && path != DFLASH_PATH_KERNELS && path != DFLASH_PATH_PERSISTENT)
+        return fail(DFLASH_EINVAL, "unknown path %d", path);
+    if (path == DFLASH_PATH_PERSISTENT && x->pchain_wg < 1)
+        return fail(DFLASH_EUNSUPPORTED, "the persistent chain is not available for this configuration");
+    x->path = path;
+    return DFLASH_OK;
+}
+
+int32_t dflash_step_path(const dflash_ctx *x, int32_t B) {
+    if (!x) return -1;
+    return use_chain(*x, B) ? DFLASH_PATH_PERSISTENT : DFLASH_PATH_KERNELS;
+}
+
+int dflash_check_device(dflash_ctx *x, void *stream) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+    int err = 0;
+    HIP_TRY(hipMemcpy(&err, x->psync + 1, sizeof err, hipMemcpyDeviceToHost), "device status read");
+    if (err) {
+        HIP_TRY(hipMemset(x->psync + 1, 0, sizeof err), "device status reset");
+        return fail(DFLASH_ESTATE, "a grid barrier of the persistent chain gave up waiting; that step's outputs "
+                                   "are invalid");
+    }
+    return DFLASH_OK;
 }
 
 int dflash_quantize_fp8_rows(const float *w, int32_t rows, int32_t cols, uint8_t *codes, float *scales, void *stream) {

@@ -139,20 +139,36 @@ __device__ __forceinline__ float wave_max(float v) {
 // GEMM of encode / inject reads row-major planes.
 enum ActFmt { ACT_SPLIT3 = 0, ACT_F32 = 1, ACT_BF16 = 2 };
 
+// Device-coherent (agent-scope) stores: written through to memory, so that a
+// workgroup on another XCD reads the value in the same launch after a
+// grid-wide handshake. Used for every activation a block-step kernel produces.
+__device__ __forceinline__ void st_f32(float *p, float v) {
+    __hip_atomic_store((uint32_t *)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_i32(int32_t *p, int32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u16(uint16_t *p, uint16_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_f32(const float *p) {
+    return __uint_as_float(__hip_atomic_load((const uint32_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // Write one activation value in the lane-ordered layout: f32, or the exact
 // three-term bf16 split over three planes of act_rows * K elements.
 __device__ __forceinline__ void write_act(void *act, int fmt, int act_rows, int K, int row, int col, float v) {
     if (fmt == ACT_F32) {
-        ((float *)act)[act_offset(row, col, K, 4)] = v;
+        st_f32((float *)act + act_offset(row, col, K, 4), v);
     } else {
         uint16_t t0, t1, t2;
         split3(v, t0, t1, t2);
         uint16_t *p = (uint16_t *)act;
         const size_t plane = (size_t)act_rows * K;
         const size_t o = act_offset(row, col, K, 2);
-        p[o] = t0;
-        p[plane + o] = t1;
-        p[2 * plane + o] = t2;
+        st_u16(p + o, t0);
+        st_u16(p + plane + o, t1);
+        st_u16(p + 2 * plane + o, t2);
     }
 }
 
@@ -173,8 +189,10 @@ struct EpiArgs {
     // EPI_SCALED / EPI_LOGITS output [M][ld_out]
     float *out;
     int ld_out;
-    // EPI_RESID: residual stream x [M][ld_x] updated in place; next activation
+    // EPI_RESID: residual stream x [M][ld_x], updated in place or written to x_out when that is
+    // set; next activation
     float *x;
+    float *x_out;
     int ld_x;
     const float *wnext;   // next norm weight [E]
     void *act_out;        // next activation (format act_fmt, K = ld_x or F)
@@ -225,6 +243,8 @@ struct LayerBufs {
     float *s_qkv, *s_o, *s_gu, *s_down;  // fp8 scales in tiled column order (or null)
 };
 
+struct PStepArgs;  // persistent chain arguments (below)
+
 struct dflash_ctx {
     dflash_config cfg;
     int device;
@@ -273,7 +293,76 @@ struct dflash_ctx {
     void *enc_act;      // features converted for the fc GEMM (if needed)
     void *inj_act;      // h converted for the kv GEMM (if needed)
     float *inj_kv;      // [max_inject][L*2*kvdim]
+    // persistent chain (one sequence per step)
+    float *x2;          // second residual buffer [Mmax][E]
+    PStepArgs *pargs;   // device copy of the chain arguments
+    float *ppartial;    // stream-K partial tiles
+    int *psync;         // [bar, err, lm argmax counter, pad, group counters...]
+    int n_psync;
+    int pchain_wg;      // workgroups per chain launch (0: chain unavailable)
+    int path;           // DFLASH_PATH_*
 };
+
+// ---------------------------------------------------------------------------
+// Persistent weight-streaming chain (kernels_persistent.hip)
+// ---------------------------------------------------------------------------
+// The block step of one sequence with persistent weight-streaming kernels:
+// embed + q/k/v of layer 0 is one launch; then per layer l the attention and
+// combine kernels, and one launch of Wo, gate/up, down and the q/k/v of layer
+// l + 1 (or the lm_head), whose phases are separated by grid-wide barriers.
+constexpr int PSTEP_MAX_LAYERS = 16;
+constexpr int PSTEP_MAX_WG = 2048;  // workgroups per launch at most (sizes the partial buffer)
+
+struct PLayer {
+    const void *qkv, *o, *gu, *down;          // tiled weights
+    const float *s_qkv, *s_o, *s_gu, *s_down;  // fp8 column scales (tiled order) or null
+};
+
+// Lives in device memory for the life of the context.
+struct PStepArgs {
+    int L, E, F, V, D, nqkv, qdim, kvdim, G_E, block;
+    int mask_id, aux_dtype, act_fmt, act_rows;
+    float eps, inv_E, qscale;
+    const void *tok_embd;
+    const double *inv_freq;
+    const float *attn_norm, *ffn_norm, *q_norm, *k_norm, *output_norm;
+    PLayer layer[PSTEP_MAX_LAYERS];
+    const void *lm;
+    const float *s_lm;
+    // activations (the per-launch path's buffers plus a second residual buffer)
+    float *x, *x2;
+    void *act_a, *act_f, *act_d, *act_o;
+    float *ss_a, *ss_f, *qkv_out, *rope_cs;
+    int ss_stride;
+    float *partial;     // stream-K partial tiles
+    int *counters;      // [max groups], zero between phases
+    int pmax[5];        // partial slots per column group: q/k/v, Wo, gate/up, down, lm_head
+    float *am_val;
+    int *am_idx;
+    int *am_counter;
+    unsigned *bar;      // grid barrier counter, zeroed at the start of every step
+    int *err;           // set when a barrier wait gives up
+    long long spin_ticks;
+};
+
+// Step inputs and outputs of one call (one sequence), passed by value.
+struct PStepIO {
+    const int32_t *id_last, *block_ids, *n_past;
+    float *logits;
+    int32_t *drafts;
+    const int32_t *target;
+    int32_t *n_ok;
+};
+
+// Workgroups per launch of the chain kernels for this configuration (0: not available).
+int pchain_grid(const dflash_ctx *c);
+// Embed + q/k/v of layer 0 (one grid barrier).
+hipError_t launch_pchain_head(const dflash_ctx *c, const PStepArgs *dev_args, const PStepIO &io, int nWG,
+                              hipStream_t s);
+// Wo, gate/up, down of layer l and the q/k/v of layer l + 1 or the lm_head (three grid barriers);
+// bar_base = grid barriers passed earlier in the step.
+hipError_t launch_pchain_layer(const dflash_ctx *c, const PStepArgs *dev_args, const PStepIO &io, int l,
+                               unsigned bar_base, int nWG, hipStream_t s);
 
 struct dflash_graph {
     dflash_ctx *ctx;
@@ -314,3 +403,10 @@ hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, in
 
 // ring layout helpers (host and device)
 __host__ __device__ inline size_t ring_kv_elems(int L, int Hkv, int W, int D) { return (size_t)L * Hkv * W * D; }
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline size_t ring_v_offset(int L, int Hkv, int W, int D, int es) {
+    return align256(ring_kv_elems(L, Hkv, W, D) * es);
+}
+__host__ __device__ inline size_t ring_pos_offset(int L, int Hkv, int W, int D, int es) {
+    return ring_v_offset(L, Hkv, W, D, es) + align256(ring_kv_elems(L, Hkv, W, D) * es);
+}

@@ -7,13 +7,7 @@
 // ---------------------------------------------------------------------------
 // Ring layout: K [L][Hkv][W][D], V [L][Hkv][W][D] (ring dtype), slot_pos [W]
 // ---------------------------------------------------------------------------
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-__host__ __device__ inline size_t ring_v_offset(int L, int Hkv, int W, int D, int es) {
-    return align256(ring_kv_elems(L, Hkv, W, D) * es);
-}
-__host__ __device__ inline size_t ring_pos_offset(int L, int Hkv, int W, int D, int es) {
-    return ring_v_offset(L, Hkv, W, D, es) + align256(ring_kv_elems(L, Hkv, W, D) * es);
-}
+// (helpers ring_v_offset / ring_pos_offset in dflash_internal.h)
 
 __device__ __forceinline__ float ring_load(const void *base, int ring_dtype, size_t i) {
     return ring_dtype == DFLASH_BF16 ? bf16_to_f32(((const uint16_t *)base)[i]) : ((const float *)base)[i];

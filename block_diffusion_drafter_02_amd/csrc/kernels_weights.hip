@@ -8,29 +8,7 @@
 // bf16 and fp8 weights meet activations split exactly into three bf16 terms,
 // so every bf16 x bf16 MFMA product is exact and accumulation is fp32; f32
 // weights use the f32 MFMA.
-#include "dflash_internal.h"
-
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-
-template <int WT>
-struct WTraits;
-template <>
-struct WTraits<DFLASH_F32> {
-    static constexpr int ES = 4;  // bytes per element
-    static constexpr int NV = 4;  // 16-byte words per lane per tile
-};
-template <>
-struct WTraits<DFLASH_BF16> {
-    static constexpr int ES = 2;
-    static constexpr int NV = 2;
-};
-template <>
-struct WTraits<DFLASH_FP8_E4M3> {
-    static constexpr int ES = 1;
-    static constexpr int NV = 1;
-};
+#include "gemv_device.h"
 
 // ---------------------------------------------------------------------------
 // Re-tiling
@@ -106,153 +84,6 @@ hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *code
 }
 
 // ---------------------------------------------------------------------------
-// Operand loading and the per-tile MFMA step
-// ---------------------------------------------------------------------------
-template <int WT>
-__device__ __forceinline__ void load_wtile(const void *W, size_t tile_index, int lane, u32x4 (&w)[WTraits<WT>::NV]) {
-    constexpr int NV = WTraits<WT>::NV;
-    const u32x4 *p = (const u32x4 *)W + tile_index * NV * 64 + lane;
-#pragma unroll
-    for (int v = 0; v < NV; ++v) w[v] = p[v * 64];
-}
-
-// 16 bf16 values of one lane as two MFMA operands
-__device__ __forceinline__ void as_bf16x8x2(const u32x4 (&w)[2], bf16x8 &lo, bf16x8 &hi) {
-    lo = __builtin_bit_cast(bf16x8, w[0]);
-    hi = __builtin_bit_cast(bf16x8, w[1]);
-}
-
-__device__ __forceinline__ void fp8x16_to_bf16x8x2(const u32x4 &w, bf16x8 &lo, bf16x8 &hi) {
-    u32x4 a, b;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        uint32_t x = w[i];
-        a[2 * i] = (uint32_t)e4m3_to_bf16(x & 0xff) | ((uint32_t)e4m3_to_bf16((x >> 8) & 0xff) << 16);
-        a[2 * i + 1] = (uint32_t)e4m3_to_bf16((x >> 16) & 0xff) | ((uint32_t)e4m3_to_bf16(x >> 24) << 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        uint32_t x = w[2 + i];
-        b[2 * i] = (uint32_t)e4m3_to_bf16(x & 0xff) | ((uint32_t)e4m3_to_bf16((x >> 8) & 0xff) << 16);
-        b[2 * i + 1] = (uint32_t)e4m3_to_bf16((x >> 16) & 0xff) | ((uint32_t)e4m3_to_bf16(x >> 24) << 16);
-    }
-    lo = __builtin_bit_cast(bf16x8, a);
-    hi = __builtin_bit_cast(bf16x8, b);
-}
-
-// Activation operand of one lane: row `row`, columns kb*64 + 16*(lane/16) .. +16.
-// NT = number of 16-byte words per lane: SPLIT3 -> 3 terms x 2, F32 -> 4, BF16 -> 2.
-template <int AF>
-struct AFTraits;
-template <>
-struct AFTraits<ACT_SPLIT3> {
-    static constexpr int NW = 6;
-};
-template <>
-struct AFTraits<ACT_F32> {
-    static constexpr int NW = 4;
-};
-template <>
-struct AFTraits<ACT_BF16> {
-    static constexpr int NW = 2;
-};
-
-// Row-major activation planes (the large-M GEMM reads caller inputs and its
-// own row-major staging).
-template <int AF>
-__device__ __forceinline__ void load_act(const void *act, int act_rows, int K, int row, int M, int kb, int lane,
-                                         u32x4 (&a)[AFTraits<AF>::NW]) {
-    constexpr int NW = AFTraits<AF>::NW;
-    if (row >= M) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) a[i] = u32x4{0, 0, 0, 0};
-        return;
-    }
-    const int col = kb * KBLK + LANE_ELEMS * (lane >> 4);
-    if constexpr (AF == ACT_SPLIT3) {
-        const uint16_t *base = (const uint16_t *)act;
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            const u32x4 *p = (const u32x4 *)(base + ((size_t)t * act_rows + row) * K + col);
-            a[2 * t] = p[0];
-            a[2 * t + 1] = p[1];
-        }
-    } else if constexpr (AF == ACT_F32) {
-        const u32x4 *p = (const u32x4 *)((const float *)act + (size_t)row * K + col);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = p[i];
-    } else {
-        const u32x4 *p = (const u32x4 *)((const uint16_t *)act + (size_t)row * K + col);
-        a[0] = p[0];
-        a[1] = p[1];
-    }
-}
-
-// Lane-ordered activation planes (act_offset): one k-block of one 16-row tile
-// is 1 KB per plane word, read by one contiguous wavefront load.
-template <int AF>
-__device__ __forceinline__ void load_act_lanes(const void *act, int act_rows, int K, int mt, bool live, int kb,
-                                               int lane, u32x4 (&a)[AFTraits<AF>::NW]) {
-    constexpr int NW = AFTraits<AF>::NW;
-    if (!live) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) a[i] = u32x4{0, 0, 0, 0};
-        return;
-    }
-    const int KB = K / KBLK;
-    if constexpr (AF == ACT_SPLIT3) {
-        const u32x4 *base = (const u32x4 *)act + ((size_t)mt * KB + kb) * 128 + lane;
-        const size_t plane = (size_t)act_rows * K / 8;  // 16-byte words per plane
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            a[2 * t] = base[t * plane];
-            a[2 * t + 1] = base[t * plane + 64];
-        }
-    } else {
-        static_assert(AF == ACT_F32, "lane-ordered activations are split bf16 or f32");
-        const u32x4 *base = (const u32x4 *)act + ((size_t)mt * KB + kb) * 256 + lane;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) a[v] = base[v * 64];
-    }
-}
-
-// acc += A(16 rows x 64 k) * W(16 cols x 64 k)^T for one tile
-template <int WT, int AF>
-__device__ __forceinline__ void tile_mfma(const u32x4 (&w)[WTraits<WT>::NV], const u32x4 (&a)[AFTraits<AF>::NW],
-                                          f32x4 &acc) {
-    if constexpr (WT == DFLASH_F32) {
-        static_assert(AF == ACT_F32, "f32 weights take f32 activations");
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float av = __uint_as_float(a[v][j]);
-                float wv = __uint_as_float(w[v][j]);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, wv, acc, 0, 0, 0);
-            }
-        }
-    } else {
-        bf16x8 wlo, whi;
-        if constexpr (WT == DFLASH_BF16)
-            as_bf16x8x2(w, wlo, whi);
-        else
-            fp8x16_to_bf16x8x2(w[0], wlo, whi);
-        if constexpr (AF == ACT_SPLIT3) {
-#pragma unroll
-            for (int t = 0; t < 3; ++t) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[2 * t]), wlo, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[2 * t + 1]), whi, acc, 0, 0,
-                                                              0);
-            }
-        } else {
-            static_assert(AF == ACT_BF16, "bf16 weights take split or bf16 activations");
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[0]), wlo, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[1]), whi, acc, 0, 0, 0);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // Split-K weight-streaming kernel for the block rows
 // ---------------------------------------------------------------------------
 // Grid (G column groups of 64*WN columns, S k-splits), 256 threads = 4
@@ -297,273 +128,18 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
         }
     }
 
-    __shared__ float tile[MP][GN];
+    __shared__ float tile[MP * GN];
     __shared__ float rs_s[MP];
-    __shared__ int is_last;
-    for (int wv = 0; wv < WK; ++wv) {
-        if (wk == wv) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int m = mt * 16 + 4 * (lane >> 4) + i;
-                        const int col = 64 * wn + 16 * t + (lane & 15);
-                        if (wv == 0)
-                            tile[m][col] = acc[mt][t][i];
-                        else
-                            tile[m][col] += acc[mt][t][i];
-                    }
-        }
-        __syncthreads();
-    }
-
-    float *tflat = &tile[0][0];
+    __shared__ int best_s[MP];
+    __shared__ int flag_s;
+    reduce_waves<MT, WN>(acc, tile, wn, wk, lane);
     if (a.S > 1) {
-        // Split-K handshake without cache-wide maintenance: partials are written
-        // and read with device-coherent (agent-scope) atomic accesses, each wave
-        // waits for its stores to complete before the workgroup signals, and the
-        // last workgroup of the group to arrive sums the partials in split order.
-        float *part = a.partial + ((size_t)s * G + g) * (MP * GN);
-        for (int e = tid; e < MP * GN; e += 256)
-            __hip_atomic_store((uint32_t *)(part + e), __float_as_uint(tflat[e]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __syncthreads();
-        if (tid == 0)
-            is_last = __hip_atomic_fetch_add(&a.counters[g], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.S - 1;
-        __syncthreads();
-        if (!is_last) return;
-        constexpr int EPT = MP * GN / 256;  // tile elements per thread
-        float sum[EPT];
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) sum[k] = 0.0f;
-        for (int s0 = 0; s0 < a.S; s0 += 4) {  // four splits' loads in flight, summed in split order
-            float v[4][EPT];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int k = 0; k < EPT; ++k)
-                    v[u][k] = s0 + u < a.S ? __uint_as_float(__hip_atomic_load(
-                                                 (const uint32_t *)(a.partial + ((size_t)(s0 + u) * G + g) * (MP * GN) +
-                                                                    tid + 256 * k),
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                                           : 0.0f;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int k = 0; k < EPT; ++k)
-                    if (s0 + u < a.S) sum[k] += v[u][k];
-        }
-#pragma unroll
-        for (int k = 0; k < EPT; ++k) tflat[tid + 256 * k] = sum[k];
-        if (tid == 0) __hip_atomic_store(&a.counters[g], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
+        constexpr int TE = MP * GN;
+        if (!splitk_last<TE / 256>(tile, a.partial + ((size_t)s * G + g) * TE, a.partial + (size_t)g * TE,
+                                   (size_t)G * TE, a.S, &a.counters[g], &flag_s))
+            return;
     }
-
-    // ---- epilogue on the 16*MT x GN tile ----
-    const EpiArgs &e = a.epi;
-    // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps): 16 threads per row, fixed-order tree
-    for (int m0 = 0; m0 < MP; m0 += 16) {
-        const int m = m0 + (tid >> 4), sub = tid & 15;
-        float part = 0.0f;
-        if (e.ss != nullptr && m < M)
-            for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
-        for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-        if (sub == 0) rs_s[m] = (e.ss != nullptr && m < M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
-    }
-    __syncthreads();
-
-    if constexpr (EPI == EPI_QKV) {
-        // columns of this group: whole heads of q (RMSNorm q_norm, rope, * 1/sqrt(D)), of k (RMSNorm
-        // k_norm, rope) or of v (as is), one wave per (row, head) vector
-        const int D = e.D, hpg = GN / D;  // heads per group
-        // the lane's norm weights and the (cos, sin) of its rope pair for all 16 block rows, loaded once
-        float qn[2], kn[2], cosr[16], sinr[16];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int d = min(lane + 64 * u, D - 1);
-            qn[u] = e.q_norm[d];
-            kn[u] = e.k_norm[d];
-        }
-        const int pair = D == 128 ? lane : (lane & 31);
-        const int b0 = (wave < M * hpg) ? (wave / hpg) / e.block : 0;  // rows of one wave share a sequence
-        for (int i = 0; i < 16; ++i) {
-            const float2 cs = *(const float2 *)(e.rope_cs + ((size_t)b0 * e.block + i) * D + 2 * pair);
-            cosr[i] = cs.x;
-            sinr[i] = cs.y;
-        }
-        for (int vec = wave; vec < M * hpg; vec += 4) {
-            const int m = vec / hpg, hg = vec % hpg;
-            const int c0 = hg * D;            // first column of the head inside the tile
-            const int n0 = g * GN + c0;       // first column of the head in the output
-            const bool is_q = n0 < e.qdim, is_k = !is_q && n0 < e.qdim + e.kvdim;
-            const int b = m / e.block, i = m % e.block;
-            float x[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int d = lane + 64 * u;
-                float v = 0.0f;
-                if (d < D) {
-                    v = tile[m][c0 + d] * rs_s[m];
-                    if (e.wscale) v *= e.wscale[n0 + d];
-                }
-                x[u] = v;
-            }
-            if (is_q || is_k) {
-                float ss = x[0] * x[0] + x[1] * x[1];
-                ss = wave_sum(ss);
-                const float r = 1.0f / sqrtf(ss / (float)D + e.eps);
-                float cn = 0.0f, sn = 0.0f;
-                if (b == b0) {
-#pragma unroll
-                    for (int k = 0; k < 16; ++k)
-                        if (k == i) {
-                            cn = cosr[k];
-                            sn = sinr[k];
-                        }
-                } else {
-                    const float2 cs = *(const float2 *)(e.rope_cs + ((size_t)b * e.block + i) * D + 2 * pair);
-                    cn = cs.x;
-                    sn = cs.y;
-                }
-                const float w0 = is_q ? qn[0] : kn[0], w1 = is_q ? qn[1] : kn[1];
-                if (D == 128) {
-                    const float x1 = x[0] * r * w0, x2 = x[1] * r * w1;
-                    x[0] = x1 * cn - x2 * sn;
-                    x[1] = x1 * sn + x2 * cn;
-                } else {  // D == 64: the pair partner of lane l is lane l ^ 32
-                    const float x1 = x[0] * r * w0;
-                    const float partner = __shfl_xor(x1, 32, 64);
-                    x[0] = lane < 32 ? x1 * cn - partner * sn : partner * sn + x1 * cn;
-                }
-                if (is_q) {
-                    x[0] *= e.qscale;
-                    x[1] *= e.qscale;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int d = lane + 64 * u;
-                if (d < D) e.out[(size_t)m * e.ld_out + n0 + d] = x[u];
-            }
-        }
-    } else if constexpr (EPI == EPI_SCALED) {
-        for (int m = wave; m < M; m += 4) {
-            const int n = g * GROUP_N + lane;
-            float v = tile[m][lane] * rs_s[m];
-            if (e.wscale) v *= e.wscale[n];
-            e.out[(size_t)m * e.ld_out + n] = v;
-        }
-    } else if constexpr (EPI == EPI_RESID) {
-        constexpr int RPW = MP / 4;  // rows per wave; all residual loads issued first
-        const int n = g * GROUP_N + lane;
-        const float sc = e.wscale ? e.wscale[n] : 1.0f;
-        float xv[RPW];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const int m = wave + 4 * r;
-            xv[r] = m < M ? e.x[(size_t)m * e.ld_x + n] : 0.0f;
-        }
-        const float wn = e.wnext[n];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const int m = wave + 4 * r;
-            if (m < M) {
-                const float xn = xv[r] + tile[m][lane] * sc;
-                e.x[(size_t)m * e.ld_x + n] = xn;
-                write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, n, xn * wn);
-                const float sq = wave_sum(xn * xn);
-                if (lane == 0) e.ss_out[(size_t)g * e.ss_stride + m] = sq;
-            }
-        }
-    } else if constexpr (EPI == EPI_SWIGLU) {
-        for (int m = wave; m < M; m += 4) {
-            if (lane < 32) {
-                float gv = tile[m][lane] * rs_s[m];
-                float uv = tile[m][lane + 32] * rs_s[m];
-                if (e.wscale) {
-                    gv *= e.wscale[g * GROUP_N + lane];
-                    uv *= e.wscale[g * GROUP_N + 32 + lane];
-                }
-                const float act = gv / (1.0f + expf(-gv)) * uv;
-                write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, g * 32 + lane, act);
-            }
-        }
-    } else {  // EPI_LOGITS
-        for (int m = wave; m < M; m += 4) {
-            const int n = g * GROUP_N + lane;
-            float v = tile[m][lane] * rs_s[m];
-            if (e.wscale) v *= e.wscale[n];
-            e.out[(size_t)m * e.ld_out + n] = v;
-            float bv = v;
-            int bi = n;
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if (lane == 0) {
-                __hip_atomic_store((uint32_t *)(e.am_val + (size_t)g * e.ss_stride + m), __float_as_uint(bv),
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(e.am_idx + (size_t)g * e.ss_stride + m, bi, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __syncthreads();
-        if (tid == 0)
-            is_last = __hip_atomic_fetch_add(e.am_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
-        __syncthreads();
-        if (!is_last) return;
-        __shared__ int best_s[MP];
-        for (int m0 = 0; m0 < M; m0 += 16) {
-            const int m = m0 + (tid >> 4), sub = tid & 15;
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            if (m < M)
-                for (int gg = sub; gg < G; gg += 16) {
-                    const float v = __uint_as_float(__hip_atomic_load(
-                        (const uint32_t *)(e.am_val + (size_t)gg * e.ss_stride + m), __ATOMIC_RELAXED,
-                        __HIP_MEMORY_SCOPE_AGENT));
-                    const int i = __hip_atomic_load(e.am_idx + (size_t)gg * e.ss_stride + m, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-                    if (v > bv || (v == bv && i < bi)) {
-                        bv = v;
-                        bi = i;
-                    }
-                }
-            for (int o = 8; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if (sub == 0 && m < M) {
-                best_s[m] = bi;
-                const int b = m / e.block, i = m % e.block;
-                if (i > 0) e.drafts[(size_t)b * (e.block - 1) + i - 1] = bi;
-            }
-        }
-        __syncthreads();
-        if (e.target != nullptr && tid < M / e.block) {
-            const int b = tid;
-            int n = 0;
-            while (n < e.block - 1 && best_s[b * e.block + 1 + n] == e.target[(size_t)b * (e.block - 1) + n]) ++n;
-            e.n_ok[b] = n;
-        }
-        if (tid == 0) __hip_atomic_store(e.am_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    gemv_epilogue<EPI, MT, WN>(a.epi, g, G, tile, rs_s, &flag_s, best_s);
 }
 
 template <int WT, int AF, int EPI, int WN>

@@ -222,6 +222,17 @@ class Drafter:
             None if n_ok is None else _dev(n_ok, torch.int32, "n_ok"), s.cuda_stream, C.byref(h)))
         return StepGraph(h.value, [ring_table, id_last, n_past, logits, drafts, target, n_ok, self])
 
+    def set_path(self, path: int) -> None:
+        """Route later block steps: _lib.PATH_AUTO, PATH_KERNELS or PATH_PERSISTENT."""
+        check(lib().dflash_set_path(self._ctx, path))
+
+    def step_path(self, B: int = 1) -> int:
+        return int(lib().dflash_step_path(self._ctx, B))
+
+    def check_device(self, stream=None) -> None:
+        """Raise if a persistent-path step gave up at a grid barrier since the last check."""
+        check(lib().dflash_check_device(self._ctx, _stream(stream)))
+
     def replay_stage(self, stage: int, layer: int = 0, stream=None) -> None:
         """Re-run one weight-streaming stage of the last block step (a single-kernel timing hook)."""
         check(lib().dflash_replay_stage(self._ctx, stage, layer, _stream(stream)))

@@ -193,6 +193,33 @@ void dflash_graph_destroy(dflash_graph *g);
 int dflash_quantize_fp8_rows(const float *w, int32_t rows, int32_t cols, uint8_t *codes, float *scales,
                              void *stream);
 
+/* How a block step runs. DFLASH_PATH_KERNELS: one kernel per projection,
+ * attention and combine (about six per layer). DFLASH_PATH_PERSISTENT: for a
+ * single sequence (B == 1), the weight-streaming projections of a layer run
+ * as one launch of a persistent kernel sized to the GPU (Wo, gate/up, down and
+ * the next layer's q/k/v or the lm_head), with grid-wide barriers between
+ * them; attention and combine stay separate kernels. Both paths compute the
+ * same operations with the same operand splits; their reductions split at
+ * different points, so results agree to fp32 rounding. DFLASH_PATH_AUTO (the
+ * default) takes the faster path measured for this library, currently the
+ * per-launch kernels. */
+typedef enum { DFLASH_PATH_AUTO = 0, DFLASH_PATH_KERNELS = 1, DFLASH_PATH_PERSISTENT = 2 } dflash_path;
+
+/* Choose the path of later block steps (and of graphs captured later).
+ * EUNSUPPORTED for DFLASH_PATH_PERSISTENT when the persistent kernel does not
+ * fit this configuration or device. */
+int dflash_set_path(dflash_ctx *ctx, int32_t path);
+
+/* The path (DFLASH_PATH_KERNELS or DFLASH_PATH_PERSISTENT) a block step of B
+ * sequences takes now; -1 for a NULL ctx. */
+int32_t dflash_step_path(const dflash_ctx *ctx, int32_t B);
+
+/* Synchronise `stream` and report whether a persistent-path step gave up at
+ * a grid barrier since the last check (a barrier waits at most one second,
+ * e.g. when other work holds compute units): ESTATE if so, after which the
+ * flag is cleared; that step's outputs are invalid. OK otherwise. */
+int dflash_check_device(dflash_ctx *ctx, void *stream);
+
 /* Stages of the block step that dflash_replay_stage can re-run. */
 typedef enum {
     DFLASH_STAGE_QKV = 0,     /* fused q/k/v projection of one layer (attention-norm folded in) */
@@ -203,8 +230,8 @@ typedef enum {
 
 /* Re-run one weight-streaming stage of layer `layer` of the last block step
  * on the activations the workspace holds now, with that step's batch; a
- * timing hook for a single kernel (the kernel and its launch are the ones the
- * step uses). DFLASH_STAGE_GATE_UP and DFLASH_STAGE_QKV leave the step's state
+ * timing hook for a single kernel (the per-launch kernel of that stage, as
+ * DFLASH_PATH_KERNELS runs it). DFLASH_STAGE_GATE_UP and DFLASH_STAGE_QKV leave the step's state
  * consistent; DFLASH_STAGE_O and DFLASH_STAGE_DOWN add into the residual
  * stream again, so run a full step before reading results. ESTATE before the
  * first block step. */

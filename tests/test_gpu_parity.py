@@ -88,12 +88,18 @@ def _spec_id(s):
     return f"{'tiny' if s.shape is synth.TINY else 'medium'}-{s.weight_dtype}-{s.ring_dtype}"
 
 
+PATHS = {"kernels": 1, "persistent": 2}  # DFLASH_PATH_KERNELS, DFLASH_PATH_PERSISTENT
+
+
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("spec", SPECS, ids=_spec_id)
-def test_encode_inject_and_block_step_match_oracle(gpu, spec):
+def test_encode_inject_and_block_step_match_oracle(gpu, spec, path):
     torch = _torch()
     n_ctx = spec.shape.window + 16  # the ring wraps: the first 16 slots are overwritten
     dr, ring, fdev, (ocfg, ow, oring), raw, feats = _build(spec, n_ctx)
-    print(f"[case] {_spec_id(spec)} n_ctx={n_ctx}", flush=True)
+    dr.set_path(PATHS[path])
+    assert dr.step_path(1) == PATHS[path]
+    print(f"[case] {_spec_id(spec)} {path} n_ctx={n_ctx}", flush=True)
     # encode of the last chunk against the oracle's encode of the same rows
     last = slice(n_ctx - 16, n_ctx)
     h = dr.encode(fdev[last]).cpu().numpy().astype(np.float64)
@@ -102,6 +108,7 @@ def test_encode_inject_and_block_step_match_oracle(gpu, spec):
     _check_ring(dr, ring, oring, spec)
     st = synth.step_inputs(spec.shape, 1, seed=3)
     logits, drafts = _step(dr, [ring], st["id_last"], [n_ctx])
+    dr.check_device()
     ref = O.block_forward(ocfg, ow, oring, O.block_ids(ocfg, int(st["id_last"][0])), n_ctx)
     tol = _check_logits(spec, ref, logits)
     bad, ties = WL.compare_drafts(ref, drafts[0], tol)
@@ -218,10 +225,13 @@ def test_block_attention_is_non_causal(gpu):
     _check_logits(spec, ref2, l2.astype(np.float64))
 
 
-def test_graph_replay_is_bitwise_equal_to_eager_with_interleaved_traffic(gpu):
+@pytest.mark.parametrize("path", list(PATHS))
+def test_graph_replay_is_bitwise_equal_to_eager_with_interleaved_traffic(gpu, path):
     torch = _torch()
     spec = WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16")
     dr, ring, fdev, _, raw, feats = _build(spec, 300)
+    dr.set_path(PATHS[path])
+    print(f"[case] graph {path}", flush=True)
     table = dr.ring_table([ring])
     il = torch.tensor([5], dtype=torch.int32, device=dr.device)
     npst = torch.tensor([300], dtype=torch.int32, device=dr.device)
@@ -257,6 +267,28 @@ def test_graph_replay_is_bitwise_equal_to_eager_with_interleaved_traffic(gpu):
     torch.cuda.synchronize()
     assert torch.equal(logits, ref9)
     g.close()
+    dr.check_device()
+
+
+@pytest.mark.parametrize("spec", [WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16"), WL.Spec(WL.MEDIUM, "f32", "f32", "f32"),
+                                  WL.Spec(WL.MEDIUM, "fp8", "bf16", "bf16")], ids=_spec_id)
+def test_persistent_and_per_launch_paths_agree(gpu, spec):
+    """The two paths run the same operations and differ only in where their reductions split: logits agree
+    to the fp32 bar, drafts exactly (up to near ties)."""
+    torch = _torch()
+    dr, ring, fdev, _, raw, feats = _build(spec, 300)
+    outs = {}
+    for path in PATHS:
+        dr.set_path(PATHS[path])
+        print(f"[case] paths {_spec_id(spec)} {path}", flush=True)
+        outs[path] = _step(dr, [ring], [77], [300])
+        dr.check_device()
+    (lk, dk), (lp, dp) = outs["kernels"], outs["persistent"]
+    scale = max(1.0, float(np.std(lk)))
+    tol = 16 * WL.U32 * np.sqrt(WL.step_chain(spec.shape)) * scale
+    assert np.abs(lp - lk).max() <= tol, np.abs(lp - lk).max()
+    bad, ties = WL.compare_drafts(lk, dp[0], tol)
+    assert not bad, (bad, ties)
 
 
 def test_fp8_quantisation_is_bit_exact(gpu):

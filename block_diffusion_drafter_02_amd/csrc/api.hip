@@ -36,9 +36,10 @@ int hip_fail(hipError_t e, const char *what) {
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// the q/k/v projection streams 128-column groups (8 tiles): one head of 128 per group
-constexpr int QKV_TPG = 8;
-constexpr int QKV_WN = QKV_TPG / TILES_PER_GROUP;
+// the q/k/v projection streams 64-column groups like every other projection
+// (its per-head RMSNorm and rope run in the attention kernel)
+constexpr int QKV_TPG = TILES_PER_GROUP;
+constexpr int QKV_WN = 1;
 
 int dtype_bytes(int dt) { return dt == DFLASH_F32 ? 4 : dt == DFLASH_BF16 ? 2 : 1; }
 
@@ -56,8 +57,6 @@ int check_config(const dflash_config *c) {
     for (int64_t v : m64)
         if (v <= 0 || v % 64) return fail(DFLASH_EUNSUPPORTED, "dimensions must be positive multiples of 64");
     if (c->window > 65536) return fail(DFLASH_EUNSUPPORTED, "window must be <= 65536");
-    if ((int64_t)(c->n_head + 2 * c->n_head_kv) * c->head_dim % 128)
-        return fail(DFLASH_EUNSUPPORTED, "(n_head + 2 * n_head_kv) * head_dim must be a multiple of 128");
     if (c->max_batch < 1 || c->max_batch > 8) return fail(DFLASH_EUNSUPPORTED, "max_batch must be in 1..8");
     if (c->max_inject < 1) return fail(DFLASH_EINVAL, "max_inject must be >= 1");
     if (c->mask_id < 0 || c->mask_id >= c->n_vocab) return fail(DFLASH_EINVAL, "mask_id out of range");
@@ -435,23 +434,16 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     return DFLASH_OK;
 }
 
-// q/k/v projection with the attention norm folded in; its epilogue RMS-norms
-// and ropes every q and k head (q also scaled by 1/sqrt(D))
+// q/k/v projection with the attention norm folded in (the attention kernel
+// RMS-norms and ropes the q and k heads)
 int stage_qkv(const dflash_ctx &x, int l, int M, hipStream_t s) {
     const LayerBufs &b = x.layer[l];
-    EpiArgs e = epi_base(x, EPI_QKV, M);
+    EpiArgs e = epi_base(x, EPI_SCALED, M);
     e.wscale = b.s_qkv;
     e.ss = x.ss_a;
     e.ss_groups = x.G_E;
     e.out = x.qkv_out;
     e.ld_out = x.nqkv;
-    e.qdim = x.qdim;
-    e.kvdim = x.kvdim;
-    e.D = x.D;
-    e.q_norm = x.q_norm + (size_t)l * x.D;
-    e.k_norm = x.k_norm + (size_t)l * x.D;
-    e.rope_cs = x.rope_cs;
-    e.qscale = 1.0f / sqrtf((float)x.D);
     return gemv(x, b.qkv, x.nqkv, x.E, x.act_a, e, s, QKV_WN);
 }
 

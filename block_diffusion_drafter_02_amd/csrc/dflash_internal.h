@@ -175,7 +175,7 @@ __device__ __forceinline__ void write_act(void *act, int fmt, int act_rows, int 
 // ---------------------------------------------------------------------------
 // Epilogues of the split-K weight-streaming kernel
 // ---------------------------------------------------------------------------
-enum EpiKind { EPI_SCALED = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_QKV = 4 };
+enum EpiKind { EPI_SCALED = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
 struct EpiArgs {
     int kind;
@@ -200,11 +200,7 @@ struct EpiArgs {
     int act_rows;         // row stride of act_out (Mmax)
     int act_K;
     float *ss_out;        // [G][ss_stride] sums of squares of the updated x
-    // EPI_QKV: per-head RMSNorm + rope of q and k in the projection output
-    int qdim, kvdim, D, block;
-    const float *q_norm, *k_norm;  // this layer's [D]
-    const float *rope_cs;          // [B][block][D/2][2]
-    float qscale;                  // 1/sqrt(D), folded into q
+    int block;  // rows per sequence
     // EPI_LOGITS: argmax across groups
     float *am_val;
     int *am_idx;

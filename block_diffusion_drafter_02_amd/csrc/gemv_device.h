@@ -277,81 +277,7 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
     }
     __syncthreads();
 
-    if constexpr (EPI == EPI_QKV) {
-        // columns of this group: whole heads of q (RMSNorm q_norm, rope, * 1/sqrt(D)), of k (RMSNorm
-        // k_norm, rope) or of v (as is), one wave per (row, head) vector
-        const int D = e.D, hpg = GN / D;  // heads per group
-        // the lane's norm weights and the (cos, sin) of its rope pair for all 16 block rows, loaded once
-        float qn[2], kn[2], cosr[16], sinr[16];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int d = min(lane + 64 * u, D - 1);
-            qn[u] = e.q_norm[d];
-            kn[u] = e.k_norm[d];
-        }
-        const int pair = D == 128 ? lane : (lane & 31);
-        const int b0 = (wave < M * hpg) ? (wave / hpg) / e.block : 0;  // rows of one wave share a sequence
-        for (int i = 0; i < 16; ++i) {
-            const float2 cs = *(const float2 *)(e.rope_cs + ((size_t)b0 * e.block + i) * D + 2 * pair);
-            cosr[i] = cs.x;
-            sinr[i] = cs.y;
-        }
-        for (int vec = wave; vec < M * hpg; vec += 4) {
-            const int m = vec / hpg, hg = vec % hpg;
-            const int c0 = hg * D;            // first column of the head inside the tile
-            const int n0 = g * GN + c0;       // first column of the head in the output
-            const bool is_q = n0 < e.qdim, is_k = !is_q && n0 < e.qdim + e.kvdim;
-            const int b = m / e.block, i = m % e.block;
-            float x[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int d = lane + 64 * u;
-                float v = 0.0f;
-                if (d < D) {
-                    v = tile[m * GN + c0 + d] * rs_s[m];
-                    if (e.wscale) v *= e.wscale[n0 + d];
-                }
-                x[u] = v;
-            }
-            if (is_q || is_k) {
-                float ss = x[0] * x[0] + x[1] * x[1];
-                ss = wave_sum(ss);
-                const float r = 1.0f / sqrtf(ss / (float)D + e.eps);
-                float cn = 0.0f, sn = 0.0f;
-                if (b == b0) {
-#pragma unroll
-                    for (int k = 0; k < 16; ++k)
-                        if (k == i) {
-                            cn = cosr[k];
-                            sn = sinr[k];
-                        }
-                } else {
-                    const float2 cs = *(const float2 *)(e.rope_cs + ((size_t)b * e.block + i) * D + 2 * pair);
-                    cn = cs.x;
-                    sn = cs.y;
-                }
-                const float w0 = is_q ? qn[0] : kn[0], w1 = is_q ? qn[1] : kn[1];
-                if (D == 128) {
-                    const float x1 = x[0] * r * w0, x2 = x[1] * r * w1;
-                    x[0] = x1 * cn - x2 * sn;
-                    x[1] = x1 * sn + x2 * cn;
-                } else {  // D == 64: the pair partner of lane l is lane l ^ 32
-                    const float x1 = x[0] * r * w0;
-                    const float partner = __shfl_xor(x1, 32, 64);
-                    x[0] = lane < 32 ? x1 * cn - partner * sn : partner * sn + x1 * cn;
-                }
-                if (is_q) {
-                    x[0] *= e.qscale;
-                    x[1] *= e.qscale;
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int d = lane + 64 * u;
-                if (d < D) st_f32(e.out + (size_t)m * e.ld_out + n0 + d, x[u]);
-            }
-        }
-    } else if constexpr (EPI == EPI_SCALED) {
+    if constexpr (EPI == EPI_SCALED) {
         for (int m = wave; m < M; m += 4) {
             const int n = g * GROUP_N + lane;
             float v = tile[m * GN + lane] * rs_s[m];

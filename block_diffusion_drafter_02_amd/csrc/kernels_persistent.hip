@@ -198,25 +198,18 @@ __device__ __forceinline__ EpiArgs epi_base(const PStepArgs &a, int kind) {
     return e;
 }
 
-// q/k/v of layer l with the attention norm folded in; per-head RMSNorm and rope of q and k, q * 1/sqrt(D)
+// q/k/v of layer l with the attention norm folded in (the attention kernel norms and ropes q and k)
 template <int WT, int AF>
 __device__ __forceinline__ void phase_qkv(const PStepArgs &a, int l, int wg, int nWG, char *lds,
                                           const u32x4 (&pf)[4][WTraits<WT>::NV], bool pok) {
-    EpiArgs e = epi_base(a, EPI_QKV);
+    EpiArgs e = epi_base(a, EPI_SCALED);
     e.wscale = a.layer[l].s_qkv;
     e.ss = a.ss_a;
     e.ss_groups = a.G_E;
     e.out = a.qkv_out;
     e.ld_out = a.nqkv;
-    e.qdim = a.qdim;
-    e.kvdim = a.kvdim;
-    e.D = a.D;
-    e.q_norm = a.q_norm + (size_t)l * a.D;
-    e.k_norm = a.k_norm + (size_t)l * a.D;
-    e.rope_cs = a.rope_cs;
-    e.qscale = a.qscale;
-    sk_gemv<WT, AF, EPI_QKV, 2>(a.layer[l].qkv, a.nqkv, a.E, a.act_a, a.act_rows, e, a.partial, a.pmax[0], a.counters,
-                                wg, nWG, lds, pf, pok);
+    sk_gemv<WT, AF, EPI_SCALED, 1>(a.layer[l].qkv, a.nqkv, a.E, a.act_a, a.act_rows, e, a.partial, a.pmax[0],
+                                   a.counters, wg, nWG, lds, pf, pok);
 }
 
 }  // namespace
@@ -224,7 +217,7 @@ __device__ __forceinline__ void phase_qkv(const PStepArgs &a, int l, int wg, int
 // Embedding and rope table, then the q/k/v projection of layer 0.
 template <int WT, int AF>
 __device__ __forceinline__ void chain_head(const PStepArgs *__restrict__ ap, const PStepIO &io) {
-    __shared__ __attribute__((aligned(16))) char lds[4 * (16 * 128 + 16 + 16 + 4)];
+    __shared__ __attribute__((aligned(16))) char lds[4 * (16 * 64 + 16 + 16 + 4)];
     __shared__ int bar_flag;
     constexpr int NV = WTraits<WT>::NV;
     const PStepArgs &a = *ap;
@@ -234,7 +227,7 @@ __device__ __forceinline__ void chain_head(const PStepArgs *__restrict__ ap, con
     for (int g = wg; g < a.G_E; g += nWG) embed_group(a, io, g);
     if (wg == nWG - 1) rope_table(a, io);
     stores_done();
-    sk_prefetch<WT, 2>(a.layer[0].qkv, a.nqkv, a.E, wg, nWG, pf, pok);
+    sk_prefetch<WT, 1>(a.layer[0].qkv, a.nqkv, a.E, wg, nWG, pf, pok);
     if (!grid_wait(a, (unsigned)nWG, &bar_flag)) return;
     phase_qkv<WT, AF>(a, 0, wg, nWG, lds, pf, pok);
 }
@@ -246,7 +239,7 @@ __device__ __forceinline__ void chain_head(const PStepArgs *__restrict__ ap, con
 template <int WT, int AF, bool LAST>
 __device__ __forceinline__ void chain_layer(const PStepArgs *__restrict__ ap, const PStepIO &io, int l,
                                             unsigned bar_base) {
-    __shared__ __attribute__((aligned(16))) char lds[4 * (16 * 128 + 16 + 16 + 4)];
+    __shared__ __attribute__((aligned(16))) char lds[4 * (16 * 64 + 16 + 16 + 4)];
     __shared__ int bar_flag;
     constexpr int NV = WTraits<WT>::NV;
     const PStepArgs &a = *ap;
@@ -301,7 +294,7 @@ __device__ __forceinline__ void chain_layer(const PStepArgs *__restrict__ ap, co
     if (LAST)
         sk_prefetch<WT, 1>(a.lm, a.V, a.E, wg, nWG, pf, pok);
     else
-        sk_prefetch<WT, 2>(a.layer[l + 1].qkv, a.nqkv, a.E, wg, nWG, pf, pok);
+        sk_prefetch<WT, 1>(a.layer[l + 1].qkv, a.nqkv, a.E, wg, nWG, pf, pok);
     if (!grid_wait(a, ++nb * (unsigned)nWG, &bar_flag)) return;
     if (LAST) {  // output norm folded in; lm_head, argmax of rows 1..15, acceptance scan
         EpiArgs e = epi_base(a, EPI_LOGITS);

@@ -307,8 +307,9 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 // ---------------------------------------------------------------------------
 // Partial kernel: grid (NCH + 1, Hkv, B), 512 threads = 8 wavefronts. Chunk
 // c < NCH covers ring slots [c*CH, c*CH + CH); chunk NCH is the block's own 16
-// keys. The q/k/v projection has already RMS-normed and roped q and the block's
-// k (q also scaled by 1/sqrt(D)). Wave w serves q head jG + (w % 4) for the
+// keys. Every wave RMS-norms (q_norm) and ropes its q head at positions
+// n_past + i and scales it by 1/sqrt(D); the block chunk does the same for the
+// block's k (k_norm, no scale). Wave w serves q head jG + (w % 4) for the
 // first (w < 4) or second half of the chunk's key tiles; the two halves merge
 // through LDS.
 //
@@ -323,14 +324,51 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 // A ring key at slot s is visible to block row i when slot_pos[s] >= 0 and
 // 0 <= n_past + i - slot_pos[s] < W; block keys are always visible.
 struct AttnArgs {
-    const float *qkv;  // [M][nqkv]: q (normed, roped, scaled), k (normed, roped), v
+    const float *qkv;  // [M][nqkv]: the raw q/k/v projection of the block rows
     int nqkv, qdim, kvdim;
     void *const *rings;
     int layer, L, Hkv, W, ring_dtype, G, NCH, CH, block;
     int vt_elems;  // bf16 elements of the V^T region in LDS
     const int32_t *n_past;
     float *ml, *o;
+    // per-head RMSNorm (q_norm / k_norm of this layer) and NEOX rope of q and of the block's k
+    const float *q_norm, *k_norm;  // [D]
+    const float *rope_cs;          // [B][block][D/2][2] (cos, sin) at position n_past + i
+    float eps, qscale;             // qscale = 1/sqrt(D), folded into q
 };
+
+// Per-head RMSNorm, norm weight and NEOX rope of one head vector of query or
+// key row `row` of sequence b, held as v[ks][e] = element 32ks + 8grp + e by
+// the four lanes grp = 0..3 that share a row (lane bits 4 and 5): the sum of
+// squares is reduced over those lanes, and the rope partner d + D/2 of
+// element d sits in the same lane at ks + KS/2.
+template <int D>
+__device__ __forceinline__ void head_norm_rope_lanes(float (&v)[D / 32][8], const float *w, const float *rope_cs,
+                                                     int b, int block, int row, float eps, float scale, int grp) {
+    constexpr int KS = D / 32;
+    float ss = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[ks][e] * v[ks][e];
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float r = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[ks][e] = v[ks][e] * r * w[32 * ks + 8 * grp + e];
+    const float *cs = rope_cs + ((size_t)b * block + row) * D;  // D/2 (cos, sin) pairs
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float2 c = *(const float2 *)(cs + 2 * (32 * ks + 8 * grp + e));
+            const float x1 = v[ks][e], x2 = v[ks + KS / 2][e];
+            v[ks][e] = (x1 * c.x - x2 * c.y) * scale;
+            v[ks + KS / 2][e] = (x1 * c.y + x2 * c.x) * scale;
+        }
+}
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
@@ -479,14 +517,24 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) ot[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (active && nkt > 0) {
-        // ---- Q^T operand: query q, head elements 32ks + 8grp .. +8, three terms ----
+        // ---- Q^T operand: query q, head elements 32ks + 8grp .. +8 (normed, roped, scaled), three terms ----
         bf16x8_t qb[KS][3];
-        const float *qrow = qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D;
+        {
+            const float *qrow = qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D;
+            float qv[KS][8];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            float v[8];
-            load8(qrow + 32 * ks + 8 * grp, v);
-            split8(v, qb[ks]);
+            for (int ks = 0; ks < KS; ++ks) load8(qrow + 32 * ks + 8 * grp, qv[ks]);
+            head_norm_rope_lanes<D>(qv, a.q_norm, a.rope_cs, b, a.block, q, a.eps, a.qscale, grp);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) split8(qv[ks], qb[ks]);
+        }
+        // the block's key q of this kv head (normed, roped), for the block chunk
+        float kblk[KS][8];
+        if (is_block) {
+            const float *krow = qkvb + (size_t)q * a.nqkv + a.qdim + (size_t)j * D;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) load8(krow + 32 * ks + 8 * grp, kblk[ks]);
+            head_norm_rope_lanes<D>(kblk, a.k_norm, a.rope_cs, b, a.block, q, a.eps, 1.0f, grp);
         }
         // ---- S^T = K Q^T, key tile kt: lane holds keys 16(kt0+kt) + 4grp + i (i < 4) of query q ----
         f32x4_t st[HKT];
@@ -504,10 +552,12 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
                     for (int t = 0; t < 3; ++t) st[kt] = MFMA_BF16(ka, qb[ks][t], st[kt]);
                 } else {
                     float kv[8];
-                    if (is_block)
-                        load8(qkvb + (size_t)key * a.nqkv + a.qdim + (size_t)j * D + d0, kv);
-                    else
+                    if (is_block) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) kv[e] = kblk[ks][e];  // key == q: the block has one key tile
+                    } else {
                         load8((const float *)Kb + (head_base + s0 + key) * D + d0, kv);
+                    }
                     bf16x8_t ka[3];
                     split8(kv, ka);
                     // the six products with term-order sum <= 2
@@ -710,6 +760,11 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
                             hipStream_t s) {
     AttnArgs a;
     a.qkv = c->qkv_out;
+    a.q_norm = c->q_norm + (size_t)l * c->D;
+    a.k_norm = c->k_norm + (size_t)l * c->D;
+    a.rope_cs = c->rope_cs;
+    a.eps = c->cfg.rms_eps;
+    a.qscale = 1.0f / sqrtf((float)c->D);
     a.nqkv = c->nqkv;
     a.qdim = c->qdim;
     a.kvdim = c->kvdim;

@@ -154,11 +154,9 @@ static hipError_t launch_gemv_mt(int MT, dim3 grid, const GemvArgs &a, hipStream
     return hipGetLastError();
 }
 
-// The q/k/v projection runs with 128-column groups (WN = 2, whole heads for its
-// epilogue); every other projection with 64-column groups.
+// Every projection streams 64-column groups (WN = 1).
 template <int WT, int AF>
 static hipError_t launch_gemv_epi(int MT, int WN, dim3 grid, const GemvArgs &a, hipStream_t s) {
-    if (a.epi.kind == EPI_QKV) return WN == 2 ? launch_gemv_mt<WT, AF, EPI_QKV, 2>(MT, grid, a, s) : hipErrorInvalidValue;
     if (WN != 1) return hipErrorInvalidValue;
     switch (a.epi.kind) {
         case EPI_SCALED: return launch_gemv_mt<WT, AF, EPI_SCALED, 1>(MT, grid, a, s);

@@ -46,19 +46,19 @@ __device__ __forceinline__ void as_bf16x8x2(const u32x4 (&w)[2], bf16x8 &lo, bf1
     hi = __builtin_bit_cast(bf16x8, w[1]);
 }
 
+// 16 E4M3FN codes of one lane (byte j of word i = element 4i + j) as two bf16x8
+// operands. The hardware conversion is exact (every E4M3 value is a bf16
+// value); it decodes two codes per instruction.
 __device__ __forceinline__ void fp8x16_to_bf16x8x2(const u32x4 &w, bf16x8 &lo, bf16x8 &hi) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     u32x4 a, b;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        uint32_t x = w[i];
-        a[2 * i] = (uint32_t)e4m3_to_bf16(x & 0xff) | ((uint32_t)e4m3_to_bf16((x >> 8) & 0xff) << 16);
-        a[2 * i + 1] = (uint32_t)e4m3_to_bf16((x >> 16) & 0xff) | ((uint32_t)e4m3_to_bf16(x >> 24) << 16);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        uint32_t x = w[2 + i];
-        b[2 * i] = (uint32_t)e4m3_to_bf16(x & 0xff) | ((uint32_t)e4m3_to_bf16((x >> 8) & 0xff) << 16);
-        b[2 * i + 1] = (uint32_t)e4m3_to_bf16((x >> 16) & 0xff) | ((uint32_t)e4m3_to_bf16(x >> 24) << 16);
+        a[2 * i] = __builtin_bit_cast(uint32_t, (bf16x2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+        a[2 * i + 1] = __builtin_bit_cast(uint32_t, (bf16x2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+        b[2 * i] = __builtin_bit_cast(uint32_t, (bf16x2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, false));
+        b[2 * i + 1] =
+            __builtin_bit_cast(uint32_t, (bf16x2)__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[2 + i], 1.0f, true));
     }
     lo = __builtin_bit_cast(bf16x8, a);
     hi = __builtin_bit_cast(bf16x8, b);

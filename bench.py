@@ -161,7 +161,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--path", default="auto", choices=["auto", "kernels", "persistent"],
-                    help="block-step path (auto: the persistent chain for one sequence)")
+                    help="block-step path (auto: the per-launch kernels; persistent: the opt-in persistent chain)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (five times) to calibrate byte counters")
     args = ap.parse_args()

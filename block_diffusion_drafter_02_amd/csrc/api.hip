@@ -81,6 +81,28 @@ void choose_split(int G, int KB, int &S, int &kbps) {
 
 int mt_for(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
 
+// k-splits of a batched block-row projection (gemm_kernel over all 16*B rows,
+// 256 columns per workgroup): about 512 workgroups, at least 8 k-blocks per
+// split. Depends only on N and K.
+void batch_split(int N, int K, int &S, int &kbps) {
+    const int KB = K / KBLK, tiles = (N / GROUP_N + 3) / 4;  // 256-column workgroup tiles
+    S = std::max(1, std::min((512 + tiles - 1) / tiles, std::max(1, KB / 8)));
+    kbps = (KB + S - 1) / S;
+    S = (KB + kbps - 1) / kbps;
+}
+
+// k-splits of an encode / inject GEMM: enough workgroups (128 x 256 tiles) to
+// fill the GPU about twice, at least 16 k-blocks per split, and the S partial
+// [M][N] products must fit the [rows_cap][N] output buffer.
+void gemm_split(GemmArgs &g, int rows_cap) {
+    const int KB = g.K / KBLK, tiles = ((g.N / GROUP_N + 3) / 4) * ((g.M + 127) / 128);  // 128 x 256 tiles
+    int S = std::max(1, (512 + tiles - 1) / tiles);
+    S = std::min(S, std::max(1, KB / 16));
+    S = std::min(S, std::max(1, rows_cap / g.M));
+    g.kbps = (KB + S - 1) / S;
+    g.S = (KB + g.kbps - 1) / g.kbps;
+}
+
 // Partial slots per column group of a chain phase with G groups of KB k-blocks
 // each. The phase's n = min(workgroups, G*KB) <= PSTEP_MAX_WG workgroups own
 // contiguous runs of at least m = floor(G*KB / n) >= 1 k-blocks, so a group
@@ -206,6 +228,17 @@ size_t carve(dflash_ctx &x, char *base) {
     x.ppartial = cv.take<float>(4 * ppmax);
     x.n_psync = 4 + pgmax;
     x.psync = cv.take<int>(4ull * x.n_psync);
+    // split partials of the batched projections (16*B rows, B > 1)
+    x.bpartial = nullptr;
+    if (c.max_batch > 1) {
+        size_t bmax = 0;
+        for (auto &sh : shapes) {
+            int S, kbps;
+            batch_split(sh[0], sh[1], S, kbps);
+            bmax = std::max(bmax, (size_t)S * Mmax * sh[0]);
+        }
+        x.bpartial = cv.take<float>(4 * bmax);
+    }
     return cv.off;
 }
 
@@ -419,6 +452,21 @@ EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
 
 int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, const EpiArgs &epi, hipStream_t s,
          int WN = 1) {
+    if (epi.M > 16 && x.bpartial) {
+        // several sequences: an MFMA GEMM over all rows writes split partials, then the epilogue kernel
+        GemmArgs g = {};
+        g.W = W;
+        g.N = N;
+        g.K = K;
+        g.M = epi.M;
+        g.act = act;
+        g.act_rows = x.Mmax;
+        g.out = x.bpartial;
+        batch_split(N, K, g.S, g.kbps);
+        HIP_TRY(launch_gemm(x.cfg.weight_dtype, x.act_fmt, g, s, true), "batched projection launch");
+        HIP_TRY(launch_batch_epi(x.bpartial, g.S, g.M, N, epi, s), "batched epilogue launch");
+        return DFLASH_OK;
+    }
     GemvArgs a = {};
     a.W = W;
     a.N = N;
@@ -585,9 +633,10 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
         return hip_fail(e, "hipGetDevice");
     }
     e = attention_set_smem_limit();
+    if (e == hipSuccess) e = gemm_set_smem_limit();
     if (e != hipSuccess) {
         delete x;
-        return hip_fail(e, "hipFuncSetAttribute (attention LDS)");
+        return hip_fail(e, "hipFuncSetAttribute (attention / GEMM LDS)");
     }
     int r = prepare(*x, w, (hipStream_t)stream);
     if (r != DFLASH_OK) {
@@ -644,8 +693,9 @@ int dflash_encode(dflash_ctx *x, const void *feats, int32_t T, float *h, void *s
     g.act = act;
     g.act_rows = act_rows;
     g.out = x->enc_y;
+    gemm_split(g, c.max_inject);
     HIP_TRY(launch_gemm(c.aux_dtype, fmt, g, s), "encode GEMM launch");
-    HIP_TRY(launch_rmsnorm_rows(x->enc_y, T, x->E, x->hidden_norm, c.rms_eps, h, s), "encode norm launch");
+    HIP_TRY(launch_rmsnorm_rows(x->enc_y, g.S, T, x->E, x->hidden_norm, c.rms_eps, h, s), "encode norm launch");
     return DFLASH_OK;
 }
 
@@ -671,8 +721,9 @@ int dflash_inject(dflash_ctx *x, void *ring, const float *h, const int32_t *pos,
     g.act = act;
     g.act_rows = act_rows;
     g.out = x->inj_kv;
+    gemm_split(g, x->cfg.max_inject);
     HIP_TRY(launch_gemm(x->cfg.weight_dtype, x->act_fmt, g, s), "inject GEMM launch");
-    HIP_TRY(launch_inject(x, ring, pos, T, s), "inject launch");
+    HIP_TRY(launch_inject(x, ring, pos, T, g.S, s), "inject launch");
     return DFLASH_OK;
 }
 

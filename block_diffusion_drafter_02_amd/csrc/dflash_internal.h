@@ -62,12 +62,8 @@ __host__ __device__ inline size_t act_offset(int m, int k, int K, int es) {
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // float -> bfloat16, round to nearest even (finite inputs; NaN stays NaN)
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// Round to nearest even (the hardware conversion; NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Exact three-term split v = t0 + t1 + t2 with each term a bfloat16. Each
 // subtraction is exact (Sterbenz: the operands agree to within a factor of
@@ -79,6 +75,20 @@ __device__ __forceinline__ void split3(float v, uint16_t &t0, uint16_t &t1, uint
     t1 = f32_to_bf16(r);
     r = r - bf16_to_f32(t1);
     t2 = f32_to_bf16(r);
+}
+
+// The same split of two values at once, each term packed as (a | b << 16):
+// one packed conversion per term.
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t &w0, uint32_t &w1, uint32_t &w2) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    const bf16x2_t h0 = bf16x2_t{(__bf16)a, (__bf16)b};
+    const float ra = a - (float)h0[0], rb = b - (float)h0[1];
+    const bf16x2_t h1 = bf16x2_t{(__bf16)ra, (__bf16)rb};
+    const float sa = ra - (float)h1[0], sb = rb - (float)h1[1];
+    const bf16x2_t h2 = bf16x2_t{(__bf16)sa, (__bf16)sb};
+    w0 = __builtin_bit_cast(uint32_t, h0);
+    w1 = __builtin_bit_cast(uint32_t, h1);
+    w2 = __builtin_bit_cast(uint32_t, h2);
 }
 
 // E4M3FN code -> bfloat16 bits (exact: 3 mantissa bits and exponents
@@ -228,7 +238,8 @@ struct GemmArgs {
     int N, K, M;
     const void *act;
     int act_rows;   // row stride between terms (for ACT_SPLIT3)
-    float *out;     // [M][N] f32
+    float *out;     // [S][M][N] f32: split s sums k-blocks [s * kbps, (s + 1) * kbps)
+    int S, kbps;
 };
 
 // ---------------------------------------------------------------------------
@@ -295,6 +306,7 @@ struct dflash_ctx {
     float *ppartial;    // stream-K partial tiles
     int *psync;         // [bar, err, lm argmax counter, pad, group counters...]
     int n_psync;
+    float *bpartial;    // split partials of the batched projections (null when max_batch == 1)
     int pchain_wg;      // workgroups per chain launch (0: chain unavailable)
     int path;           // DFLASH_PATH_*
 };
@@ -377,12 +389,14 @@ hipError_t launch_vec_to_f32(const void *src, int dtype, int n, float *dst, hipS
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *codes, float *scales, hipStream_t s);
 hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, dim3 grid, const GemvArgs &a, hipStream_t s);
-hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s);
+hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s, bool lanes = false);
+hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, hipStream_t s);
+hipError_t gemm_set_smem_limit();
 hipError_t launch_split(const float *src, int rows, int K, int ld_src, void *dst, int act_fmt, int act_rows,
                         hipStream_t s);
 hipError_t launch_bf16_to_f32(const uint16_t *src, size_t n, float *dst, hipStream_t s);
-hipError_t launch_rmsnorm_rows(const float *y, int T, int E, const float *w, float eps, float *h, hipStream_t s);
-hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, int T, hipStream_t s);
+hipError_t launch_rmsnorm_rows(const float *y, int S, int T, int E, const float *w, float eps, float *h, hipStream_t s);
+hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, int T, int S, hipStream_t s);
 hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32_t *block_ids, const int32_t *n_past,
                         int B, hipStream_t s);
 hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, const int32_t *n_past, int B,

@@ -85,22 +85,30 @@ hipError_t launch_split(const float *src, int rows, int K, int ld_src, void *dst
 // ---------------------------------------------------------------------------
 // Encode: h = y * rsqrt(mean(y^2) + eps) * w   (one workgroup per row)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *y, int E, const float *w, float eps, float *h) {
+// y holds S k-split partials [S][T][E], summed here in split order first.
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *y, int S, int T, int E, const float *w,
+                                                           float eps, float *h) {
     const int t = blockIdx.x;
-    const float *yr = y + (size_t)t * E;
+    float *hr = h + (size_t)t * E;
     float ss = 0.0f;
-    for (int c = threadIdx.x; c < E; c += 256) ss += yr[c] * yr[c];
+    for (int c = threadIdx.x; c < E; c += 256) {
+        float v = y[(size_t)t * E + c];
+        for (int sp = 1; sp < S; ++sp) v += y[((size_t)sp * T + t) * E + c];
+        hr[c] = v;
+        ss += v * v;
+    }
     ss = wave_sum(ss);
     __shared__ float red[4];
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float r = 1.0f / sqrtf(tot / (float)E + eps);
-    for (int c = threadIdx.x; c < E; c += 256) h[(size_t)t * E + c] = yr[c] * r * w[c];
+    for (int c = threadIdx.x; c < E; c += 256) hr[c] = hr[c] * r * w[c];
 }
 
-hipError_t launch_rmsnorm_rows(const float *y, int T, int E, const float *w, float eps, float *h, hipStream_t s) {
-    hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(T), dim3(256), 0, s, y, E, w, eps, h);
+hipError_t launch_rmsnorm_rows(const float *y, int S, int T, int E, const float *w, float eps, float *h,
+                               hipStream_t s) {
+    hipLaunchKernelGGL(rmsnorm_rows_kernel, dim3(T), dim3(256), 0, s, y, S, T, E, w, eps, h);
     return hipGetLastError();
 }
 
@@ -133,28 +141,6 @@ __device__ __forceinline__ void head_norm_rope(float (&x)[D / 64], const float *
     }
 }
 
-// Same with the lane's norm weights (nw[e] = w[lane + 64e]) and cos/sin
-// (c = cos, s = sin of the lane's pair) already in registers.
-template <int D>
-__device__ __forceinline__ void head_norm_rope_reg(float (&x)[D / 64], const float (&nw)[D / 64], float c, float s,
-                                                   float eps, int lane) {
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) ss += x[e] * x[e];
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)D + eps);
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) x[e] = x[e] * r * nw[e];
-    if constexpr (D == 128) {
-        const float x1 = x[0], x2 = x[1];
-        x[0] = x1 * c - x2 * s;
-        x[1] = x1 * s + x2 * c;
-    } else {
-        const float partner = __shfl_xor(x[0], 32, 64);
-        x[0] = lane < 32 ? x[0] * c - partner * s : partner * s + x[0] * c;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Inject (dflash-ops card, Method; Requirements and limits)
 // ---------------------------------------------------------------------------
@@ -162,7 +148,8 @@ __device__ __forceinline__ void head_norm_rope_reg(float (&x)[D / 64], const flo
 // each kvdim wide. Wave w handles kv heads w, w+4, ... The rope angle is
 // pos * inv_freq[f] in fp64 and its sine and cosine are taken in fp64.
 template <int D>
-__global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ kv, int L, int Hkv, int W,
+// kv holds S k-split partials [S][T][L*2*Hkv*D] of the projection, summed here in split order.
+__global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ kv, int S, int T, int L, int Hkv, int W,
                                                      const int32_t *__restrict__ pos,
                                                      const double *__restrict__ inv_freq,
                                                      const float *__restrict__ k_norm_all, float eps, void *ring,
@@ -183,6 +170,7 @@ __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ k
     const int es = ring_dtype == DFLASH_BF16 ? 2 : 4;
     const size_t kvdim = (size_t)Hkv * D;
     const float *row = kv + (size_t)t * L * 2 * kvdim + (size_t)l * 2 * kvdim;
+    const size_t split = (size_t)T * L * 2 * kvdim;  // floats between partials
     char *rb = (char *)ring;
     void *Kb = rb;
     void *Vb = rb + ring_v_offset(L, Hkv, W, D, es);
@@ -193,6 +181,10 @@ __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ k
         for (int e = 0; e < D / 64; ++e) {
             x[e] = row[(size_t)j * D + lane + 64 * e];
             v[e] = row[kvdim + (size_t)j * D + lane + 64 * e];
+            for (int sp = 1; sp < S; ++sp) {
+                x[e] += row[sp * split + (size_t)j * D + lane + 64 * e];
+                v[e] += row[sp * split + kvdim + (size_t)j * D + lane + 64 * e];
+            }
         }
         head_norm_rope<D>(x, kn, cs, eps, lane);
         const size_t base = (((size_t)l * Hkv + j) * W + slot) * D;
@@ -208,14 +200,14 @@ __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ k
     }
 }
 
-hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, int T, hipStream_t s) {
+hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, int T, int S, hipStream_t s) {
     dim3 grid(T, c->L);
     const float eps = c->cfg.rms_eps;
     if (c->D == 128)
-        hipLaunchKernelGGL(inject_kernel<128>, grid, dim3(256), 0, s, c->inj_kv, c->L, c->Hkv, c->W, pos, c->inv_freq,
+        hipLaunchKernelGGL(inject_kernel<128>, grid, dim3(256), 0, s, c->inj_kv, S, T, c->L, c->Hkv, c->W, pos, c->inv_freq,
                            c->k_norm, eps, ring, c->cfg.ring_dtype);
     else if (c->D == 64)
-        hipLaunchKernelGGL(inject_kernel<64>, grid, dim3(256), 0, s, c->inj_kv, c->L, c->Hkv, c->W, pos, c->inv_freq,
+        hipLaunchKernelGGL(inject_kernel<64>, grid, dim3(256), 0, s, c->inj_kv, S, T, c->L, c->Hkv, c->W, pos, c->inv_freq,
                            c->k_norm, eps, ring, c->cfg.ring_dtype);
     else
         return hipErrorInvalidValue;
@@ -337,36 +329,64 @@ struct AttnArgs {
     float eps, qscale;             // qscale = 1/sqrt(D), folded into q
 };
 
-// Per-head RMSNorm, norm weight and NEOX rope of one head vector of query or
-// key row `row` of sequence b, held as v[ks][e] = element 32ks + 8grp + e by
-// the four lanes grp = 0..3 that share a row (lane bits 4 and 5): the sum of
-// squares is reduced over those lanes, and the rope partner d + D/2 of
-// element d sits in the same lane at ks + KS/2.
+// One head vector of query or key row `row` of sequence b, held as
+// v[ks][e] = element 32ks + 8grp + e by the four lanes grp = 0..3 that share a
+// row (lane bits 4 and 5), with the lane's norm weights and rope (cos, sin)
+// pairs. The rope partner d + D/2 of element d sits in the same lane at
+// ks + KS/2. Loaded in one go so that the loads overlap the chunk's K/V loads.
 template <int D>
-__device__ __forceinline__ void head_norm_rope_lanes(float (&v)[D / 32][8], const float *w, const float *rope_cs,
-                                                     int b, int block, int row, float eps, float scale, int grp) {
+struct HeadRow {
+    float v[D / 32][8], w[D / 32][8], cs[D / 64][16];
+};
+
+template <int D>
+__device__ __forceinline__ void head_load(HeadRow<D> &h, const float *src, const float *w, const float *rope_cs,
+                                          int b, int block, int row, int grp) {
+    constexpr int KS = D / 32;
+    const float *cs = rope_cs + ((size_t)b * block + row) * D;  // D/2 (cos, sin) pairs
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const float4 a0 = *(const float4 *)(src + 32 * ks + 8 * grp), a1 = *(const float4 *)(src + 32 * ks + 8 * grp + 4);
+        const float4 w0 = *(const float4 *)(w + 32 * ks + 8 * grp), w1 = *(const float4 *)(w + 32 * ks + 8 * grp + 4);
+        h.v[ks][0] = a0.x; h.v[ks][1] = a0.y; h.v[ks][2] = a0.z; h.v[ks][3] = a0.w;
+        h.v[ks][4] = a1.x; h.v[ks][5] = a1.y; h.v[ks][6] = a1.z; h.v[ks][7] = a1.w;
+        h.w[ks][0] = w0.x; h.w[ks][1] = w0.y; h.w[ks][2] = w0.z; h.w[ks][3] = w0.w;
+        h.w[ks][4] = w1.x; h.w[ks][5] = w1.y; h.w[ks][6] = w1.z; h.w[ks][7] = w1.w;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float4 c = *(const float4 *)(cs + 2 * (32 * ks + 8 * grp) + 4 * u);
+            h.cs[ks][4 * u] = c.x; h.cs[ks][4 * u + 1] = c.y; h.cs[ks][4 * u + 2] = c.z; h.cs[ks][4 * u + 3] = c.w;
+        }
+}
+
+// Per-head RMSNorm (sum of squares reduced over the four lanes of the row),
+// norm weight, NEOX rope and a scale, in place on h.v.
+template <int D>
+__device__ __forceinline__ void head_norm_rope_row(HeadRow<D> &h, float eps, float scale) {
     constexpr int KS = D / 32;
     float ss = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += v[ks][e] * v[ks][e];
+        for (int e = 0; e < 8; ++e) ss += h.v[ks][e] * h.v[ks][e];
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float r = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[ks][e] = v[ks][e] * r * w[32 * ks + 8 * grp + e];
-    const float *cs = rope_cs + ((size_t)b * block + row) * D;  // D/2 (cos, sin) pairs
+        for (int e = 0; e < 8; ++e) h.v[ks][e] = h.v[ks][e] * r * h.w[ks][e];
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float2 c = *(const float2 *)(cs + 2 * (32 * ks + 8 * grp + e));
-            const float x1 = v[ks][e], x2 = v[ks + KS / 2][e];
-            v[ks][e] = (x1 * c.x - x2 * c.y) * scale;
-            v[ks + KS / 2][e] = (x1 * c.y + x2 * c.x) * scale;
+            const float cx = h.cs[ks][2 * e], sy = h.cs[ks][2 * e + 1];
+            const float x1 = h.v[ks][e], x2 = h.v[ks + KS / 2][e];
+            h.v[ks][e] = (x1 * cx - x2 * sy) * scale;
+            h.v[ks + KS / 2][e] = (x1 * sy + x2 * cx) * scale;
         }
 }
 
@@ -379,12 +399,11 @@ __device__ __forceinline__ void split8(const float (&v)[8], bf16x8_t (&t)[3]) {
     u32x4_t w0, w1, w2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint16_t a0, a1, a2, b0, b1, b2;
-        split3(v[2 * i], a0, a1, a2);
-        split3(v[2 * i + 1], b0, b1, b2);
-        w0[i] = (uint32_t)a0 | ((uint32_t)b0 << 16);
-        w1[i] = (uint32_t)a1 | ((uint32_t)b1 << 16);
-        w2[i] = (uint32_t)a2 | ((uint32_t)b2 << 16);
+        uint32_t x0, x1, x2;
+        split3_pair(v[2 * i], v[2 * i + 1], x0, x1, x2);
+        w0[i] = x0;
+        w1[i] = x1;
+        w2[i] = x2;
     }
     t[0] = __builtin_bit_cast(bf16x8_t, w0);
     t[1] = __builtin_bit_cast(bf16x8_t, w1);
@@ -429,6 +448,22 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     const size_t head_base = ((size_t)a.layer * a.Hkv + j) * a.W;  // slot-row index of slot 0
     const int s0 = c * a.CH;
     const float *qkvb = a.qkv + (size_t)b * a.block * a.nqkv;     // this sequence's 16 rows
+    const int hh = wave & 3, half = wave >> 2;
+    const bool active = hh < a.G;
+    const int q = lane & 15, grp = lane >> 4;
+
+    // ---- loads that do not depend on the chunk, issued ahead of it: the query
+    // position, this wave's query row (and the block's key row) with their norm
+    // weights and rope pairs, and the chunk's slot positions ----
+    const int qpos = a.n_past[b] + q;
+    HeadRow<D> hq, hk;
+    if (active) {
+        head_load<D>(hq, qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D, a.q_norm, a.rope_cs, b, a.block, q,
+                     grp);
+        if (is_block) head_load<D>(hk, qkvb + (size_t)q * a.nqkv + a.qdim + (size_t)j * D, a.k_norm, a.rope_cs, b,
+                                   a.block, q, grp);
+    }
+    const int kp_reg = (!is_block && tid < a.CH) ? sp[s0 + tid] : 0;
 
     // ---- chunk keys and values into LDS ----
     if (is_block) {
@@ -502,13 +537,9 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
             }
         }
     }
-    if (!is_block)
-        for (int k = tid; k < a.CH; k += 512) kpos[k] = sp[s0 + k];
+    if (!is_block && tid < a.CH) kpos[tid] = kp_reg;
     __syncthreads();
 
-    const int hh = wave & 3, half = wave >> 2;
-    const bool active = hh < a.G;
-    const int q = lane & 15, grp = lane >> 4;
     // key tiles of this wave: [half * HKT, half * HKT + HKT) intersected with the chunk
     const int kt0 = half * HKT;
     const int nkt = max(0, min(HKT, nkeys / 16 - kt0));
@@ -519,23 +550,11 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     if (active && nkt > 0) {
         // ---- Q^T operand: query q, head elements 32ks + 8grp .. +8 (normed, roped, scaled), three terms ----
         bf16x8_t qb[KS][3];
-        {
-            const float *qrow = qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D;
-            float qv[KS][8];
+        head_norm_rope_row<D>(hq, a.eps, a.qscale);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) load8(qrow + 32 * ks + 8 * grp, qv[ks]);
-            head_norm_rope_lanes<D>(qv, a.q_norm, a.rope_cs, b, a.block, q, a.eps, a.qscale, grp);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) split8(qv[ks], qb[ks]);
-        }
+        for (int ks = 0; ks < KS; ++ks) split8(hq.v[ks], qb[ks]);
         // the block's key q of this kv head (normed, roped), for the block chunk
-        float kblk[KS][8];
-        if (is_block) {
-            const float *krow = qkvb + (size_t)q * a.nqkv + a.qdim + (size_t)j * D;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) load8(krow + 32 * ks + 8 * grp, kblk[ks]);
-            head_norm_rope_lanes<D>(kblk, a.k_norm, a.rope_cs, b, a.block, q, a.eps, 1.0f, grp);
-        }
+        if (is_block) head_norm_rope_row<D>(hk, a.eps, 1.0f);
         // ---- S^T = K Q^T, key tile kt: lane holds keys 16(kt0+kt) + 4grp + i (i < 4) of query q ----
         f32x4_t st[HKT];
 #pragma clang loop unroll(full)
@@ -554,7 +573,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
                     float kv[8];
                     if (is_block) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) kv[e] = kblk[ks][e];  // key == q: the block has one key tile
+                        for (int e = 0; e < 8; ++e) kv[e] = hk.v[ks][e];  // key == q: the block has one key tile
                     } else {
                         load8((const float *)Kb + (head_base + s0 + key) * D + d0, kv);
                     }
@@ -571,7 +590,6 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
             }
         }
         // ---- mask and softmax statistics of this wave's keys for query q ----
-        const int qpos = a.n_past[b] + q;
 #pragma clang loop unroll(full)
         for (int kt = 0; kt < HKT; ++kt) {
 #pragma unroll

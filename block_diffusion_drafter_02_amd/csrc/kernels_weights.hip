@@ -177,59 +177,302 @@ hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, dim3 grid, const
 }
 
 // ---------------------------------------------------------------------------
-// Large-M GEMM (encode's fc, inject's fused K/V projection)
+// Large-M GEMM (encode's fc, inject's fused K/V projection): out[M][N] =
+// act[M][K] . W[N][K]^T (* per-column scale), f32 out, row-major activations
+// (one bf16 plane, three bf16 planes of an exact split, or f32).
 // ---------------------------------------------------------------------------
-// Grid (N/64 column groups, ceil(M/64) row blocks), 256 threads. Wave w of
-// block (g, mb) computes rows mb*64 + 16w .. +16 against the 64 columns of
-// group g over the whole reduction; the four waves read the same weight
-// tiles, so three of the four reads hit the caches.
-template <int WT, int AF>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-    constexpr int NV = WTraits<WT>::NV;
-    constexpr int NW = AFTraits<AF>::NW;
+// Workgroup tile 128 rows x 256 columns (four column groups) x one k-split
+// (grid z), 8 wavefronts of 64 rows x 64 columns each; split s writes its
+// partial product to out + s*M*N and the consumer sums the splits in order.
+// Per k-block the workgroup stages the activation rows and the four groups'
+// weight tiles in LDS once (activation rows padded against bank conflicts;
+// weight tiles copied in their lane order) and every wave reads its operands
+// from there; the next k-block is loaded into registers while the current one
+// is multiplied. Column groups past N are masked.
+template <int AF>
+struct GemmA;
+template <>
+struct GemmA<ACT_BF16> {
+    static constexpr int TERMS = 1, ES = 2, ROWB = 144;  // 64 bf16 + 8 pad per row
+};
+template <>
+struct GemmA<ACT_SPLIT3> {
+    static constexpr int TERMS = 3, ES = 2, ROWB = 144;
+};
+template <>
+struct GemmA<ACT_F32> {
+    static constexpr int TERMS = 1, ES = 4, ROWB = 272;  // 64 f32 + 4 pad per row
+};
+
+constexpr int GEMM_BM = 128, GEMM_GROUPS = 4, GEMM_THREADS = 512;
+
+// ALANES: the activations are in the block rows' lane-ordered layout (act_offset;
+// planes of act_rows rows) instead of row-major; a 16-row k-block tile of a plane
+// is then one contiguous run of 64-lane words, staged to LDS in the same order.
+template <int WT, int AF, bool ALANES>
+struct GemmShape {
+    static constexpr int NV = WTraits<WT>::NV;
+    static constexpr int TERMS = GemmA<AF>::TERMS, ES = GemmA<AF>::ES, ROWB = GemmA<AF>::ROWB;
+    static constexpr int WPR = 64 * ES / 16;                     // 16-byte words per row of a k-block
+    static constexpr int A_WORDS = TERMS * GEMM_BM * WPR;        // per k-block
+    static constexpr int A_PT = A_WORDS / GEMM_THREADS;          // per thread
+    static constexpr int B_GROUP = 4 * NV * 64;                  // words of one group's k-block
+    static constexpr int B_WORDS = GEMM_GROUPS * B_GROUP;
+    static constexpr int B_PT = B_WORDS / GEMM_THREADS;
+    static constexpr int A_LDS = ALANES ? A_WORDS * 16 : TERMS * GEMM_BM * ROWB;
+    static constexpr int LDS = A_LDS + B_WORDS * 16;
+    static constexpr int LW = ES == 2 ? 2 : 4;                   // lane-ordered words per lane per tile
+};
+
+template <int WT, int AF, bool ALANES>
+__global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
+    using Sh = GemmShape<WT, AF, ALANES>;
+    constexpr int NV = Sh::NV, NW = AFTraits<AF>::NW, TERMS = Sh::TERMS, ES = Sh::ES, ROWB = Sh::ROWB;
+    constexpr int BM = GEMM_BM, WPR = Sh::WPR, A_PT = Sh::A_PT, B_GROUP = Sh::B_GROUP, B_PT = Sh::B_PT;
+    constexpr int LW = Sh::LW;
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    char *A_s = lds;
+    u32x4 *B_s = (u32x4 *)(lds + Sh::A_LDS);
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = blockIdx.x;
-    const int m0 = blockIdx.y * 64 + wave * 16;
+    const int wr = wave >> 2, wc = wave & 3;  // rows 64wr.., column group g0 + wc
+    const int G = a.N / GROUP_N;
+    const int g0 = blockIdx.x * GEMM_GROUPS, r0 = blockIdx.y * BM, sp = blockIdx.z;
     const int KB = a.K / KBLK;
-    f32x4 acc[4];
+    const int kb0 = sp * a.kbps, kb1 = min(KB, kb0 + a.kbps);
+    float *out = a.out + (size_t)sp * a.M * a.N;
+    const bool wave_live = g0 + wc < G;
+
+    u32x4 sa[A_PT], sb[B_PT];
+    auto load_stage = [&](int kb) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (m0 < a.M) {
-        for (int kb = 0; kb < KB; ++kb) {
-            u32x4 w[4][NV];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) load_wtile<WT>(a.W, ((size_t)g * KB + kb) * 4 + t, lane, w[t]);
-            u32x4 av[NW];
-            load_act<AF>(a.act, a.act_rows, a.K, m0 + (lane & 15), a.M, kb, lane, av);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) tile_mfma<WT, AF>(w[t], av, acc[t]);
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + 4 * (lane >> 4) + i;
-            const int n = g * GROUP_N + 16 * t + (lane & 15);
-            if (m < a.M) {
-                float v = acc[t][i];
-                if (a.wscale) v *= a.wscale[n];
-                a.out[(size_t)m * a.N + n] = v;
+        for (int i = 0; i < A_PT; ++i) {
+            const int w = tid + GEMM_THREADS * i;
+            if constexpr (ALANES) {
+                // w = ((t * 8 + mt) * LW + v) * 64 + lane_word
+                const int t = w / (8 * LW * 64), mt = (w / (LW * 64)) % 8, rest = w % (LW * 64);
+                const int mtg = r0 / 16 + mt;
+                if (mtg * 16 < a.M)
+                    sa[i] = *((const u32x4 *)a.act + (size_t)t * a.act_rows * a.K / (16 / ES) +
+                              ((size_t)mtg * KB + kb) * LW * 64 + rest);
+                else
+                    sa[i] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                const int t = w / (BM * WPR), rem = w % (BM * WPR), row = rem / WPR, cw = rem % WPR;
+                const int m = r0 + row;
+                if (m < a.M)
+                    sa[i] = *(const u32x4 *)((const char *)a.act +
+                                             (((size_t)t * a.act_rows + m) * a.K + (size_t)kb * KBLK) * ES +
+                                             (size_t)cw * 16);
+                else
+                    sa[i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i) {
+            const int w = tid + GEMM_THREADS * i;
+            const int gi = w / B_GROUP, rest = w % B_GROUP;
+            if (g0 + gi < G)
+                sb[i] = ((const u32x4 *)a.W)[((size_t)(g0 + gi) * KB + kb) * B_GROUP + rest];
+            else
+                sb[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto store_stage = [&]() {
+#pragma unroll
+        for (int i = 0; i < A_PT; ++i) {
+            const int w = tid + GEMM_THREADS * i;
+            if constexpr (ALANES) {
+                ((u32x4 *)A_s)[w] = sa[i];
+            } else {
+                const int t = w / (BM * WPR), rem = w % (BM * WPR), row = rem / WPR, cw = rem % WPR;
+                *(u32x4 *)(A_s + (t * BM + row) * ROWB + cw * 16) = sa[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_PT; ++i) B_s[tid + GEMM_THREADS * i] = sb[i];
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_stage(kb0);
+    store_stage();
+    __syncthreads();
+    for (int kb = kb0; kb < kb1; ++kb) {
+        if (kb + 1 < kb1) load_stage(kb + 1);
+        if (wave_live) {
+            u32x4 w[4][NV];
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) w[t][v] = B_s[wc * B_GROUP + (t * NV + v) * 64 + lane];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const int mt = wr * 4 + rt;
+                u32x4 av[NW];
+                if constexpr (ALANES) {
+#pragma unroll
+                    for (int t = 0; t < TERMS; ++t)
+#pragma unroll
+                        for (int v = 0; v < LW; ++v)
+                            av[t * LW + v] = ((const u32x4 *)A_s)[((t * 8 + mt) * LW + v) * 64 + lane];
+                } else if constexpr (AF == ACT_F32) {
+                    const int row = mt * 16 + (lane & 15);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) av[v] = *(const u32x4 *)(A_s + row * ROWB + (lane >> 4) * 64 + v * 16);
+                } else {
+                    const int row = mt * 16 + (lane & 15);
+#pragma unroll
+                    for (int t = 0; t < TERMS; ++t)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            av[2 * t + h] = *(const u32x4 *)(A_s + (t * BM + row) * ROWB + (lane >> 4) * 32 + h * 16);
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) tile_mfma<WT, AF>(w[t], av, acc[rt][t]);
+            }
+        }
+        __syncthreads();
+        if (kb + 1 < kb1) {
+            store_stage();
+            __syncthreads();
+        }
+    }
+    if (!wave_live) return;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = r0 + wr * 64 + rt * 16 + 4 * (lane >> 4) + i;
+                const int n = (g0 + wc) * GROUP_N + 16 * t + (lane & 15);
+                if (m < a.M) {
+                    float v = acc[rt][t][i];
+                    if (a.wscale) v *= a.wscale[n];
+                    out[(size_t)m * a.N + n] = v;
+                }
+            }
 }
 
-hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s) {
-    dim3 grid(a.N / GROUP_N, (a.M + 63) / 64);
+template <int WT, int AF, bool ALANES>
+static hipError_t gemm_go(const GemmArgs &a, hipStream_t s) {
+    using Sh = GemmShape<WT, AF, ALANES>;
+    dim3 grid((a.N / GROUP_N + GEMM_GROUPS - 1) / GEMM_GROUPS, (a.M + GEMM_BM - 1) / GEMM_BM, a.S);
+    hipLaunchKernelGGL((gemm_kernel<WT, AF, ALANES>), grid, dim3(GEMM_THREADS), Sh::LDS, s, a);
+    return hipGetLastError();
+}
+
+template <int WT, int AF, bool ALANES>
+static hipError_t gemm_attr() {
+    return hipFuncSetAttribute((const void *)gemm_kernel<WT, AF, ALANES>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               GemmShape<WT, AF, ALANES>::LDS);
+}
+
+hipError_t gemm_set_smem_limit() {
+    hipError_t e;
+    if ((e = gemm_attr<DFLASH_F32, ACT_F32, false>()) != hipSuccess) return e;
+    if ((e = gemm_attr<DFLASH_F32, ACT_F32, true>()) != hipSuccess) return e;
+    if ((e = gemm_attr<DFLASH_BF16, ACT_BF16, false>()) != hipSuccess) return e;
+    if ((e = gemm_attr<DFLASH_BF16, ACT_SPLIT3, false>()) != hipSuccess) return e;
+    if ((e = gemm_attr<DFLASH_BF16, ACT_SPLIT3, true>()) != hipSuccess) return e;
+    if ((e = gemm_attr<DFLASH_FP8_E4M3, ACT_SPLIT3, false>()) != hipSuccess) return e;
+    return gemm_attr<DFLASH_FP8_E4M3, ACT_SPLIT3, true>();
+}
+
+hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s, bool lanes) {
+    if (a.S < 1 || a.kbps < 1 || (a.S - 1) * a.kbps >= a.K / KBLK) return hipErrorInvalidValue;
     if (wdtype == DFLASH_F32 && act_fmt == ACT_F32)
-        hipLaunchKernelGGL((gemm_kernel<DFLASH_F32, ACT_F32>), grid, dim3(256), 0, s, a);
-    else if (wdtype == DFLASH_BF16 && act_fmt == ACT_BF16)
-        hipLaunchKernelGGL((gemm_kernel<DFLASH_BF16, ACT_BF16>), grid, dim3(256), 0, s, a);
-    else if (wdtype == DFLASH_BF16 && act_fmt == ACT_SPLIT3)
-        hipLaunchKernelGGL((gemm_kernel<DFLASH_BF16, ACT_SPLIT3>), grid, dim3(256), 0, s, a);
-    else if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_SPLIT3)
-        hipLaunchKernelGGL((gemm_kernel<DFLASH_FP8_E4M3, ACT_SPLIT3>), grid, dim3(256), 0, s, a);
-    else
-        return hipErrorInvalidValue;
+        return lanes ? gemm_go<DFLASH_F32, ACT_F32, true>(a, s) : gemm_go<DFLASH_F32, ACT_F32, false>(a, s);
+    if (wdtype == DFLASH_BF16 && act_fmt == ACT_BF16 && !lanes) return gemm_go<DFLASH_BF16, ACT_BF16, false>(a, s);
+    if (wdtype == DFLASH_BF16 && act_fmt == ACT_SPLIT3)
+        return lanes ? gemm_go<DFLASH_BF16, ACT_SPLIT3, true>(a, s) : gemm_go<DFLASH_BF16, ACT_SPLIT3, false>(a, s);
+    if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_SPLIT3)
+        return lanes ? gemm_go<DFLASH_FP8_E4M3, ACT_SPLIT3, true>(a, s)
+                     : gemm_go<DFLASH_FP8_E4M3, ACT_SPLIT3, false>(a, s);
+    return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue of a batched projection computed by gemm_kernel. Workgroup
+// (g, y) owns column group g and rows [16*MT*y, 16*MT*(y+1)): it sums the S
+// k-split partials [S][M][N] of that tile in split order (loads of eight
+// splits in flight at a time) into LDS and runs the fused epilogue of the
+// block-row kernels on it, with the row-indexed pointers moved to its first
+// row. The logits epilogue takes every row in one workgroup per group
+// (MT = 8, M <= 128), since its last arriver reduces the argmax of all rows.
+// ---------------------------------------------------------------------------
+template <int EPI, int MT>
+__global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S, int M, int N, EpiArgs e) {
+    constexpr int MP = 16 * MT, PT = MP * GROUP_N / 4 / 256;  // float4 per thread per split
+    constexpr int UNR = MT >= 8 ? 2 : 8;                               // splits in flight
+    __shared__ __attribute__((aligned(16))) float tile[MP * GROUP_N];
+    __shared__ float rs_s[MP];
+    __shared__ int best_s[MP];
+    __shared__ int flag_s;
+    const int g = blockIdx.x, G = N / GROUP_N, row0 = blockIdx.y * MP, tid = threadIdx.x;
+    const int rows = min(MP, M - row0);
+    f32x4 acc[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float *base = part + (size_t)row0 * N + (size_t)g * GROUP_N;
+    for (int s0 = 0; s0 < S; s0 += UNR) {
+        f32x4 v[UNR][PT];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int j = 0; j < PT; ++j) {
+                const int idx = tid + 256 * j, m = idx / (GROUP_N / 4), c4 = idx % (GROUP_N / 4);
+                v[u][j] = (s0 + u < S && m < rows)
+                              ? *(const f32x4 *)(base + ((size_t)(s0 + u) * M + m) * N + c4 * 4)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+#pragma unroll
+            for (int j = 0; j < PT; ++j)
+                if (s0 + u < S) acc[j] += v[u][j];
+    }
+#pragma unroll
+    for (int j = 0; j < PT; ++j) *(f32x4 *)(tile + 4 * (tid + 256 * j)) = acc[j];
+    __syncthreads();
+    EpiArgs el = e;
+    el.M = rows;
+    if (row0 > 0) {
+        const size_t es = e.act_fmt == ACT_F32 ? 4 : 2;
+        if (el.ss) el.ss += row0;
+        if (el.out) el.out += (size_t)row0 * e.ld_out;
+        if (el.x) el.x += (size_t)row0 * e.ld_x;
+        if (el.x_out) el.x_out += (size_t)row0 * e.ld_x;
+        if (el.ss_out) el.ss_out += row0;
+        if (el.act_out) el.act_out = (char *)el.act_out + (size_t)row0 * e.act_K * es;
+    }
+    gemv_epilogue<EPI, MT, 1>(el, g, G, tile, rs_s, &flag_s, best_s);
+}
+
+hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, hipStream_t s) {
+    if (M < 1 || M % 16 != 0 || S < 1) return hipErrorInvalidValue;
+    const dim3 rows_grid(N / GROUP_N, M / 16);
+    switch (e.kind) {
+        case EPI_SCALED:
+            hipLaunchKernelGGL((batch_epi_kernel<EPI_SCALED, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e);
+            break;
+        case EPI_RESID:
+            hipLaunchKernelGGL((batch_epi_kernel<EPI_RESID, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e);
+            break;
+        case EPI_SWIGLU:
+            hipLaunchKernelGGL((batch_epi_kernel<EPI_SWIGLU, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e);
+            break;
+        case EPI_LOGITS:
+            if (M > 128) return hipErrorInvalidValue;
+            hipLaunchKernelGGL((batch_epi_kernel<EPI_LOGITS, 8>), dim3(N / GROUP_N), dim3(256), 0, s, part, S, M, N,
+                               e);
+            break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }

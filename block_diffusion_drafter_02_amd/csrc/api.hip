@@ -474,11 +474,22 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     a.act = act;
     a.act_rows = x.Mmax;
     const int G = N / (GROUP_N * WN), KB = K / KBLK;
+    int nwv = 4;
     choose_split(G, KB, a.S, a.kb_per_split);
+    if (mt_for(epi.M) == 1 && WN == 1 && 2 * G <= x.cus) {
+        // few column groups: one 16-wave workgroup per compute unit, as many
+        // k-splits as fit (the tail then has one split-K handshake at most)
+        nwv = 16;
+        const int cap = (int)std::min<size_t>(x.partial_floats / ((size_t)G * 16 * GROUP_N), 64);
+        const int S = std::max(1, std::min(std::min(x.cus / G, KB / 8), cap));
+        a.kb_per_split = (KB + S - 1) / S;
+        a.S = (KB + a.kb_per_split - 1) / a.kb_per_split;
+    }
     a.partial = x.partial;
     a.counters = x.counters;
     a.epi = epi;
-    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), WN, dim3(G, a.S), a, s), "block-step GEMV launch");
+    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), WN, nwv, dim3(G, a.S), a, s),
+            "block-step GEMV launch");
     return DFLASH_OK;
 }
 
@@ -628,9 +639,10 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
     x->ws_bytes = workspace_bytes;
     x->tok_embd = w->tok_embd;
     hipError_t e = hipGetDevice(&x->device);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&x->cus, hipDeviceAttributeMultiprocessorCount, x->device);
     if (e != hipSuccess) {
         delete x;
-        return hip_fail(e, "hipGetDevice");
+        return hip_fail(e, "hipGetDevice / compute unit count");
     }
     e = attention_set_smem_limit();
     if (e == hipSuccess) e = gemm_set_smem_limit();

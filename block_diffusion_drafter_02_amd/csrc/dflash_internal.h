@@ -258,6 +258,7 @@ struct dflash_ctx {
     int E, H, Hkv, D, F, W, L, V, C, qdim, kvdim, nqkv, Mmax, G_E, NCH;
     int act_fmt;       // activation format of the step GEMVs
     int last_B;        // batch of the last block step (0 before the first)
+    int cus;           // compute units of the device
     size_t wbytes_el;  // bytes per streamed weight element (4, 2, 1)
     char *ws;
     size_t ws_bytes;
@@ -388,7 +389,8 @@ hipError_t launch_tile_scales(const float *src, int src_rows, float *dst, int ro
 hipError_t launch_vec_to_f32(const void *src, int dtype, int n, float *dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *codes, float *scales, hipStream_t s);
-hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, dim3 grid, const GemvArgs &a, hipStream_t s);
+hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, dim3 grid, const GemvArgs &a,
+                       hipStream_t s);
 hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s, bool lanes = false);
 hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, hipStream_t s);
 hipError_t gemm_set_smem_limit();

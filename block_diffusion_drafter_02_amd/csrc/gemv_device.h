@@ -226,7 +226,7 @@ __device__ __forceinline__ bool splitk_last(float *tile, float *mine, const floa
         *flag_s = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
     __syncthreads();
     if (!*flag_s) return false;
-    constexpr int UB = EPT <= 8 ? 8 : (EPT <= 16 ? 4 : 2);  // partials whose loads are in flight together
+    constexpr int UB = EPT <= 4 ? 16 : (EPT <= 8 ? 8 : (EPT <= 16 ? 4 : 2));  // partials in flight together
     float sum[EPT];
 #pragma unroll
     for (int k = 0; k < EPT; ++k) sum[k] = 0.0f;
@@ -260,41 +260,103 @@ __device__ __forceinline__ bool splitk_last(float *tile, float *mine, const floa
 // All outputs are written with device-coherent stores, so a consumer in the
 // same launch (the persistent kernel) reads them after a grid barrier.
 // LDS: tile (MP*GN floats), rs_s (MP floats), flag_s (1 int), best_s (MP ints).
-template <int EPI, int MT, int WN>
-__device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, float *tile, float *rs_s, int *flag_s, int *best_s) {
+// Operands of the epilogue of a one-tile (MT = 1) group that do not depend on
+// the product: the partial sums of squares of this thread's row, the residual
+// rows, the next norm weight and the fp8 column scales. A kernel loads them
+// before its weight stream so that their latency is hidden; for MT > 1 the
+// epilogue loads them itself.
+struct EpiPre {
+    static constexpr int SSN = 8;  // ss partials per thread (ss_groups <= 16 * SSN)
+    float ss[SSN];
+    float x[4];
+    float sc, sc2, wn;
+    bool ss_ok;
+};
+
+template <int EPI, int MT>
+__device__ __forceinline__ void epi_prefetch(const EpiArgs &e, int g, EpiPre &p) {
+    if constexpr (MT != 1) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int M = e.M;
+    if constexpr (EPI != EPI_RESID) {
+        const int m = tid >> 4, sub = tid & 15;
+        p.ss_ok = e.ss_groups <= 16 * EpiPre::SSN;
+#pragma unroll
+        for (int j = 0; j < EpiPre::SSN; ++j) {
+            const int gg = sub + 16 * j;
+            p.ss[j] = (e.ss != nullptr && m < M && gg < e.ss_groups) ? e.ss[(size_t)gg * e.ss_stride + m] : 0.0f;
+        }
+    }
+    if constexpr (EPI == EPI_SWIGLU) {
+        p.sc = e.wscale && lane < 32 ? e.wscale[g * GROUP_N + lane] : 1.0f;
+        p.sc2 = e.wscale && lane < 32 ? e.wscale[g * GROUP_N + 32 + lane] : 1.0f;
+    } else {
+        p.sc = e.wscale ? e.wscale[g * GROUP_N + lane] : 1.0f;
+    }
+    if constexpr (EPI == EPI_RESID) {
+        const int n = g * GROUP_N + lane;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = wave + 4 * r;
+            p.x[r] = m < M ? e.x[(size_t)m * e.ld_x + n] : 0.0f;
+        }
+        p.wn = e.wnext[n];
+    }
+}
+
+template <int EPI, int MT, int WN, bool PF = false>  // PF: operands prefetched by epi_prefetch (MT = 1)
+__device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, float *tile, float *rs_s, int *flag_s,
+                                              int *best_s, const EpiPre &pre = EpiPre{}) {
+    static_assert(!PF || MT == 1, "prefetched epilogue operands cover one row tile");
     constexpr int MP = MT * 16;
     constexpr int GN = GROUP_N * WN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int M = e.M;
-    // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps): 16 threads per row, fixed-order tree
-    for (int m0 = 0; m0 < MP; m0 += 16) {
-        const int m = m0 + (tid >> 4), sub = tid & 15;
-        float part = 0.0f;
-        if (e.ss != nullptr && m < M)
-            for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
-        for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-        if (sub == 0) rs_s[m] = (e.ss != nullptr && m < M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
+    // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps): 16 threads per row, each summing
+    // groups sub, sub + 16, ... in order, then a fixed-order tree
+    if (EPI != EPI_RESID || !PF) {
+        for (int m0 = 0; m0 < MP; m0 += 16) {
+            const int m = m0 + (tid >> 4), sub = tid & 15;
+            float part = 0.0f;
+            if (PF && pre.ss_ok) {
+#pragma unroll
+                for (int j = 0; j < EpiPre::SSN; ++j) part += pre.ss[j];
+            } else if (e.ss != nullptr && m < M) {
+                for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
+            }
+            for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+            if (sub == 0) rs_s[m] = (e.ss != nullptr && m < M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     if constexpr (EPI == EPI_SCALED) {
+        const float sc = PF ? pre.sc : (e.wscale ? e.wscale[g * GROUP_N + lane] : 1.0f);
         for (int m = wave; m < M; m += 4) {
             const int n = g * GROUP_N + lane;
             float v = tile[m * GN + lane] * rs_s[m];
-            if (e.wscale) v *= e.wscale[n];
+            if (e.wscale) v *= sc;
             st_f32(e.out + (size_t)m * e.ld_out + n, v);
         }
     } else if constexpr (EPI == EPI_RESID) {
         constexpr int RPW = MP / 4;  // rows per wave; all residual loads issued first
         const int n = g * GROUP_N + lane;
-        const float sc = e.wscale ? e.wscale[n] : 1.0f;
+        float sc, wn;
         float xv[RPW];
+        if constexpr (PF) {
+            sc = pre.sc;
+            wn = pre.wn;
 #pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const int m = wave + 4 * r;
-            xv[r] = m < M ? e.x[(size_t)m * e.ld_x + n] : 0.0f;
+            for (int r = 0; r < RPW; ++r) xv[r] = pre.x[r];
+        } else {
+            sc = e.wscale ? e.wscale[n] : 1.0f;
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int m = wave + 4 * r;
+                xv[r] = m < M ? e.x[(size_t)m * e.ld_x + n] : 0.0f;
+            }
+            wn = e.wnext[n];
         }
-        const float wn = e.wnext[n];
         float *xo = e.x_out ? e.x_out : e.x;
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
@@ -308,23 +370,26 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
             }
         }
     } else if constexpr (EPI == EPI_SWIGLU) {
+        const float sg = PF ? pre.sc : (e.wscale && lane < 32 ? e.wscale[g * GROUP_N + lane] : 1.0f);
+        const float su = PF ? pre.sc2 : (e.wscale && lane < 32 ? e.wscale[g * GROUP_N + 32 + lane] : 1.0f);
         for (int m = wave; m < M; m += 4) {
             if (lane < 32) {
                 float gv = tile[m * GN + lane] * rs_s[m];
                 float uv = tile[m * GN + lane + 32] * rs_s[m];
                 if (e.wscale) {
-                    gv *= e.wscale[g * GROUP_N + lane];
-                    uv *= e.wscale[g * GROUP_N + 32 + lane];
+                    gv *= sg;
+                    uv *= su;
                 }
                 const float act = gv / (1.0f + expf(-gv)) * uv;
                 write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, g * 32 + lane, act);
             }
         }
     } else {  // EPI_LOGITS
+        const float sc = PF ? pre.sc : (e.wscale ? e.wscale[g * GROUP_N + lane] : 1.0f);
         for (int m = wave; m < M; m += 4) {
             const int n = g * GROUP_N + lane;
             float v = tile[m * GN + lane] * rs_s[m];
-            if (e.wscale) v *= e.wscale[n];
+            if (e.wscale) v *= sc;
             st_f32(e.out + (size_t)m * e.ld_out + n, v);
             float bv = v;
             int bi = n;

@@ -745,18 +745,19 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombArgs a) {
     const int NQ = a.G * 16, qi = hh * 16 + i;
     const size_t base = ((size_t)b * a.Hkv + j) * (a.NCH + 1);
     const int nc = a.NCH + 1;
-    // one pass with a running maximum over batches of 8 chunks whose loads are all in flight together
+    // one pass with a running maximum over batches of 24 chunks whose loads are all in flight together
+    constexpr int UNR = 24;
     float mstar = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int c0 = 0; c0 < nc; c0 += 8) {
-        float2 mlb[8], ovb[8];
+    for (int c0 = 0; c0 < nc; c0 += UNR) {
+        float2 mlb[UNR], ovb[UNR];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < UNR; ++u) {
             const int cc = min(c0 + u, nc - 1);
             mlb[u] = *(const float2 *)(a.ml + ((base + cc) * NQ + qi) * 2);
             ovb[u] = *(const float2 *)(a.o + ((base + cc) * NQ + qi) * a.D + d);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < UNR; ++u) {
             if (c0 + u < nc && mlb[u].x != -INFINITY) {
                 const float mn = fmaxf(mstar, mlb[u].x);
                 const float alpha = expf(mstar - mn);  // 0 when mstar is -inf

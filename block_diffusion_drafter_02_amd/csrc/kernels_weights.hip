@@ -94,13 +94,19 @@ hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *code
 // summed in a fixed order through LDS, and when S > 1 the partial tile goes to
 // global memory; the last workgroup of the group to arrive sums the S partials
 // in split order and runs the epilogue, so results do not depend on scheduling.
-template <int WT, int AF, int MT, int EPI, int WN>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
+//
+// NWV = 16 (one 16-row tile, WN = 1) widens the workgroup to 16 wavefronts
+// along the reduction, so that a group needs fewer k-splits (often none): the
+// waves are summed through LDS in a fixed order, then the first four waves
+// carry on as above.
+template <int WT, int AF, int MT, int EPI, int WN, int NWV = 4>
+__global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
+    static_assert(NWV == 4 || (NWV == 16 && MT == 1 && WN == 1), "wide workgroups take one tile group");
     constexpr int NV = WTraits<WT>::NV;
     constexpr int NW = AFTraits<AF>::NW;
     constexpr int MP = MT * 16;
     constexpr int GN = GROUP_N * WN;  // columns per group
-    constexpr int WK = 4 / WN;        // waves along the reduction
+    constexpr int WK = NWV / WN;      // waves along the reduction
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % WN, wk = wave / WN;
     const int g = blockIdx.x, s = blockIdx.y;
@@ -132,7 +138,36 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
     __shared__ float rs_s[MP];
     __shared__ int best_s[MP];
     __shared__ int flag_s;
-    reduce_waves<MT, WN>(acc, tile, wn, wk, lane);
+    if constexpr (NWV == 16) {
+        // waves 0-7 store, waves 8-15 add into wave w-8's slot, then thread t
+        // sums element t over the eight slots in slot order
+        __shared__ float red[8][16 * GROUP_N];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if ((wk >> 3) == half) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * (lane >> 4) + i, col = 16 * t + (lane & 15);
+                        float *r = &red[wk & 7][m * GROUP_N + col];
+                        if (half == 0)
+                            *r = acc[0][t][i];
+                        else
+                            *r += acc[0][t][i];
+                    }
+            }
+            __syncthreads();
+        }
+        float v = red[0][tid];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) v += red[i][tid];
+        tile[tid] = v;
+        __syncthreads();
+        if (tid >= 256) return;  // the split-K handshake and the epilogue run on four waves
+    } else {
+        reduce_waves<MT, WN>(acc, tile, wn, wk, lane);
+    }
     if (a.S > 1) {
         constexpr int TE = MP * GN;
         if (!splitk_last<TE / 256>(tile, a.partial + ((size_t)s * G + g) * TE, a.partial + (size_t)g * TE,
@@ -143,7 +178,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
 }
 
 template <int WT, int AF, int EPI, int WN>
-static hipError_t launch_gemv_mt(int MT, dim3 grid, const GemvArgs &a, hipStream_t s) {
+static hipError_t launch_gemv_mt(int MT, int NWV, dim3 grid, const GemvArgs &a, hipStream_t s) {
+    if (NWV == 16) {
+        if (MT != 1 || WN != 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI, 1, 16>), grid, dim3(1024), 0, s, a);
+        return hipGetLastError();
+    }
+    if (NWV != 4) return hipErrorInvalidValue;
     switch (MT) {
         case 1: hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI, WN>), grid, dim3(256), 0, s, a); break;
         case 2: hipLaunchKernelGGL((gemv_kernel<WT, AF, 2, EPI, WN>), grid, dim3(256), 0, s, a); break;
@@ -156,23 +197,25 @@ static hipError_t launch_gemv_mt(int MT, dim3 grid, const GemvArgs &a, hipStream
 
 // Every projection streams 64-column groups (WN = 1).
 template <int WT, int AF>
-static hipError_t launch_gemv_epi(int MT, int WN, dim3 grid, const GemvArgs &a, hipStream_t s) {
+static hipError_t launch_gemv_epi(int MT, int WN, int NWV, dim3 grid, const GemvArgs &a, hipStream_t s) {
     if (WN != 1) return hipErrorInvalidValue;
     switch (a.epi.kind) {
-        case EPI_SCALED: return launch_gemv_mt<WT, AF, EPI_SCALED, 1>(MT, grid, a, s);
-        case EPI_RESID: return launch_gemv_mt<WT, AF, EPI_RESID, 1>(MT, grid, a, s);
-        case EPI_SWIGLU: return launch_gemv_mt<WT, AF, EPI_SWIGLU, 1>(MT, grid, a, s);
-        case EPI_LOGITS: return launch_gemv_mt<WT, AF, EPI_LOGITS, 1>(MT, grid, a, s);
+        case EPI_SCALED: return launch_gemv_mt<WT, AF, EPI_SCALED, 1>(MT, NWV, grid, a, s);
+        case EPI_RESID: return launch_gemv_mt<WT, AF, EPI_RESID, 1>(MT, NWV, grid, a, s);
+        case EPI_SWIGLU: return launch_gemv_mt<WT, AF, EPI_SWIGLU, 1>(MT, NWV, grid, a, s);
+        case EPI_LOGITS: return launch_gemv_mt<WT, AF, EPI_LOGITS, 1>(MT, NWV, grid, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, dim3 grid, const GemvArgs &a, hipStream_t s) {
-    if (wdtype == DFLASH_F32 && act_fmt == ACT_F32) return launch_gemv_epi<DFLASH_F32, ACT_F32>(MT, WN, grid, a, s);
+hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, dim3 grid, const GemvArgs &a,
+                       hipStream_t s) {
+    if (wdtype == DFLASH_F32 && act_fmt == ACT_F32)
+        return launch_gemv_epi<DFLASH_F32, ACT_F32>(MT, WN, NWV, grid, a, s);
     if (wdtype == DFLASH_BF16 && act_fmt == ACT_SPLIT3)
-        return launch_gemv_epi<DFLASH_BF16, ACT_SPLIT3>(MT, WN, grid, a, s);
+        return launch_gemv_epi<DFLASH_BF16, ACT_SPLIT3>(MT, WN, NWV, grid, a, s);
     if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_SPLIT3)
-        return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, WN, grid, a, s);
+        return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, WN, NWV, grid, a, s);
     return hipErrorInvalidValue;
 }
 
@@ -416,6 +459,19 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
     __shared__ int flag_s;
     const int g = blockIdx.x, G = N / GROUP_N, row0 = blockIdx.y * MP, tid = threadIdx.x;
     const int rows = min(MP, M - row0);
+    EpiArgs el = e;
+    el.M = rows;
+    if (row0 > 0) {
+        const size_t es = e.act_fmt == ACT_F32 ? 4 : 2;
+        if (el.ss) el.ss += row0;
+        if (el.out) el.out += (size_t)row0 * e.ld_out;
+        if (el.x) el.x += (size_t)row0 * e.ld_x;
+        if (el.x_out) el.x_out += (size_t)row0 * e.ld_x;
+        if (el.ss_out) el.ss_out += row0;
+        if (el.act_out) el.act_out = (char *)el.act_out + (size_t)row0 * e.act_K * es;
+    }
+    EpiPre pre;
+    epi_prefetch<EPI, MT>(el, g, pre);
     f32x4 acc[PT];
 #pragma unroll
     for (int j = 0; j < PT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -440,18 +496,7 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
 #pragma unroll
     for (int j = 0; j < PT; ++j) *(f32x4 *)(tile + 4 * (tid + 256 * j)) = acc[j];
     __syncthreads();
-    EpiArgs el = e;
-    el.M = rows;
-    if (row0 > 0) {
-        const size_t es = e.act_fmt == ACT_F32 ? 4 : 2;
-        if (el.ss) el.ss += row0;
-        if (el.out) el.out += (size_t)row0 * e.ld_out;
-        if (el.x) el.x += (size_t)row0 * e.ld_x;
-        if (el.x_out) el.x_out += (size_t)row0 * e.ld_x;
-        if (el.ss_out) el.ss_out += row0;
-        if (el.act_out) el.act_out = (char *)el.act_out + (size_t)row0 * e.act_K * es;
-    }
-    gemv_epilogue<EPI, MT, 1>(el, g, G, tile, rs_s, &flag_s, best_s);
+    gemv_epilogue<EPI, MT, 1, MT == 1>(el, g, G, tile, rs_s, &flag_s, best_s, pre);
 }
 
 hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, hipStream_t s) {

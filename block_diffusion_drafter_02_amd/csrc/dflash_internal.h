@@ -405,8 +405,8 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
                             hipStream_t s);
 hipError_t attention_set_smem_limit();
 // ring slots per attention chunk (one workgroup per chunk and kv head): 128
-// (or 64) for a bf16 ring, 32 for an f32 ring (its values take three planes
-// of LDS)
+// (64 when the window is not a multiple of 128) for a bf16 ring, 32 for an
+// f32 ring (its values take three planes of LDS)
 inline int attn_chunk(int ring_dtype, int W) {
     if (ring_dtype != DFLASH_BF16) return 32;
     return W % 128 == 0 ? 128 : 64;

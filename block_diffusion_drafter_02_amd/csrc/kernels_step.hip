@@ -331,62 +331,54 @@ struct AttnArgs {
 
 // One head vector of query or key row `row` of sequence b, held as
 // v[ks][e] = element 32ks + 8grp + e by the four lanes grp = 0..3 that share a
-// row (lane bits 4 and 5), with the lane's norm weights and rope (cos, sin)
-// pairs. The rope partner d + D/2 of element d sits in the same lane at
-// ks + KS/2. Loaded in one go so that the loads overlap the chunk's K/V loads.
+// row (lane bits 4 and 5). The rope partner d + D/2 of element d sits in the
+// same lane at ks + KS/2.
 template <int D>
-struct HeadRow {
-    float v[D / 32][8], w[D / 32][8], cs[D / 64][16];
-};
-
-template <int D>
-__device__ __forceinline__ void head_load(HeadRow<D> &h, const float *src, const float *w, const float *rope_cs,
-                                          int b, int block, int row, int grp) {
+__device__ __forceinline__ void head_load(float (&v)[D / 32][8], const float *src, int grp) {
     constexpr int KS = D / 32;
-    const float *cs = rope_cs + ((size_t)b * block + row) * D;  // D/2 (cos, sin) pairs
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const float4 a0 = *(const float4 *)(src + 32 * ks + 8 * grp), a1 = *(const float4 *)(src + 32 * ks + 8 * grp + 4);
-        const float4 w0 = *(const float4 *)(w + 32 * ks + 8 * grp), w1 = *(const float4 *)(w + 32 * ks + 8 * grp + 4);
-        h.v[ks][0] = a0.x; h.v[ks][1] = a0.y; h.v[ks][2] = a0.z; h.v[ks][3] = a0.w;
-        h.v[ks][4] = a1.x; h.v[ks][5] = a1.y; h.v[ks][6] = a1.z; h.v[ks][7] = a1.w;
-        h.w[ks][0] = w0.x; h.w[ks][1] = w0.y; h.w[ks][2] = w0.z; h.w[ks][3] = w0.w;
-        h.w[ks][4] = w1.x; h.w[ks][5] = w1.y; h.w[ks][6] = w1.z; h.w[ks][7] = w1.w;
+        v[ks][0] = a0.x; v[ks][1] = a0.y; v[ks][2] = a0.z; v[ks][3] = a0.w;
+        v[ks][4] = a1.x; v[ks][5] = a1.y; v[ks][6] = a1.z; v[ks][7] = a1.w;
     }
-#pragma unroll
-    for (int ks = 0; ks < KS / 2; ++ks)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float4 c = *(const float4 *)(cs + 2 * (32 * ks + 8 * grp) + 4 * u);
-            h.cs[ks][4 * u] = c.x; h.cs[ks][4 * u + 1] = c.y; h.cs[ks][4 * u + 2] = c.z; h.cs[ks][4 * u + 3] = c.w;
-        }
 }
 
 // Per-head RMSNorm (sum of squares reduced over the four lanes of the row),
-// norm weight, NEOX rope and a scale, in place on h.v.
+// norm weight w[D], NEOX rope with the row's (cos, sin) pairs cs[D/2][2] and a
+// scale, in place; w and cs are read from LDS (16-byte aligned).
 template <int D>
-__device__ __forceinline__ void head_norm_rope_row(HeadRow<D> &h, float eps, float scale) {
+__device__ __forceinline__ void head_norm_rope_row(float (&v)[D / 32][8], const float *w, const float *cs, int grp,
+                                                   float eps, float scale) {
     constexpr int KS = D / 32;
     float ss = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += h.v[ks][e] * h.v[ks][e];
+        for (int e = 0; e < 8; ++e) ss += v[ks][e] * v[ks][e];
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float r = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
+        const float4 w0 = *(const float4 *)(w + 32 * ks + 8 * grp), w1 = *(const float4 *)(w + 32 * ks + 8 * grp + 4);
+        const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) h.v[ks][e] = h.v[ks][e] * r * h.w[ks][e];
+        for (int e = 0; e < 8; ++e) v[ks][e] = v[ks][e] * r * wv[e];
+    }
 #pragma unroll
     for (int ks = 0; ks < KS / 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float cx = h.cs[ks][2 * e], sy = h.cs[ks][2 * e + 1];
-            const float x1 = h.v[ks][e], x2 = h.v[ks + KS / 2][e];
-            h.v[ks][e] = (x1 * cx - x2 * sy) * scale;
-            h.v[ks + KS / 2][e] = (x1 * sy + x2 * cx) * scale;
+        for (int e2 = 0; e2 < 4; ++e2) {
+            const float4 c = *(const float4 *)(cs + 2 * (32 * ks + 8 * grp) + 4 * e2);  // pairs 2 e2, 2 e2 + 1
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int e = 2 * e2 + h;
+                const float cx = h ? c.z : c.x, sy = h ? c.w : c.y;
+                const float x1 = v[ks][e], x2 = v[ks + KS / 2][e];
+                v[ks][e] = (x1 * cx - x2 * sy) * scale;
+                v[ks + KS / 2][e] = (x1 * sy + x2 * cx) * scale;
+            }
         }
 }
 
@@ -439,6 +431,8 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     uint16_t *vt = ksh + (bf16_ring ? a.CH * KROW : 0);            // [planes][D][CHP] V^T in bf16 terms
     int *kpos = (int *)(vt + a.vt_elems);                          // [CH] positions of the chunk's slots
     float *xch = (float *)(kpos + a.CH);                           // [4][64][DT*4 + 2] second-half results
+    float *wsh = xch + 4 * 64 * (DT * 4 + 2);                       // [2][D] q_norm, k_norm
+    float *csh = wsh + 2 * D;                                       // [block][D + 4] rope (cos, sin) pairs
 
     const int es = bf16_ring ? 2 : 4;
     const char *rb = (const char *)a.rings[b];
@@ -453,17 +447,20 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     const int q = lane & 15, grp = lane >> 4;
 
     // ---- loads that do not depend on the chunk, issued ahead of it: the query
-    // position, this wave's query row (and the block's key row) with their norm
-    // weights and rope pairs, and the chunk's slot positions ----
+    // position, this wave's query row (and the block's key row), the chunk's slot
+    // positions, and (staged to LDS with the chunk) the two norm weight vectors
+    // and the block rows' rope pairs ----
     const int qpos = a.n_past[b] + q;
-    HeadRow<D> hq, hk;
+    float qv[KS][8], kbv[KS][8];
     if (active) {
-        head_load<D>(hq, qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D, a.q_norm, a.rope_cs, b, a.block, q,
-                     grp);
-        if (is_block) head_load<D>(hk, qkvb + (size_t)q * a.nqkv + a.qdim + (size_t)j * D, a.k_norm, a.rope_cs, b,
-                                   a.block, q, grp);
+        head_load<D>(qv, qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D, grp);
+        if (is_block) head_load<D>(kbv, qkvb + (size_t)q * a.nqkv + a.qdim + (size_t)j * D, grp);
     }
     const int kp_reg = (!is_block && tid < a.CH) ? sp[s0 + tid] : 0;
+    const int ncs4 = a.block * D / 4;  // float4 words of the rope table rows (at most 512)
+    float4 cs_reg = make_float4(0.f, 0.f, 0.f, 0.f), w_reg = cs_reg;
+    if (tid < ncs4) cs_reg = *(const float4 *)(a.rope_cs + (size_t)b * a.block * D + 4 * tid);
+    if (tid < D / 2) w_reg = *(const float4 *)((tid < D / 4 ? a.q_norm : a.k_norm) + 4 * (tid % (D / 4)));
 
     // ---- chunk keys and values into LDS ----
     if (is_block) {
@@ -538,6 +535,8 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
         }
     }
     if (!is_block && tid < a.CH) kpos[tid] = kp_reg;
+    if (tid < ncs4) *(float4 *)(csh + (4 * tid / D) * (D + 4) + 4 * tid % D) = cs_reg;  // rows padded against bank conflicts
+    if (tid < D / 2) *(float4 *)(wsh + 4 * tid) = w_reg;
     __syncthreads();
 
     // key tiles of this wave: [half * HKT, half * HKT + HKT) intersected with the chunk
@@ -550,11 +549,11 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     if (active && nkt > 0) {
         // ---- Q^T operand: query q, head elements 32ks + 8grp .. +8 (normed, roped, scaled), three terms ----
         bf16x8_t qb[KS][3];
-        head_norm_rope_row<D>(hq, a.eps, a.qscale);
+        head_norm_rope_row<D>(qv, wsh, csh + q * (D + 4), grp, a.eps, a.qscale);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) split8(hq.v[ks], qb[ks]);
+        for (int ks = 0; ks < KS; ++ks) split8(qv[ks], qb[ks]);
         // the block's key q of this kv head (normed, roped), for the block chunk
-        if (is_block) head_norm_rope_row<D>(hk, a.eps, 1.0f);
+        if (is_block) head_norm_rope_row<D>(kbv, wsh + D, csh + q * (D + 4), grp, a.eps, 1.0f);
         // ---- S^T = K Q^T, key tile kt: lane holds keys 16(kt0+kt) + 4grp + i (i < 4) of query q ----
         f32x4_t st[HKT];
 #pragma clang loop unroll(full)
@@ -573,7 +572,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
                     float kv[8];
                     if (is_block) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) kv[e] = hk.v[ks][e];  // key == q: the block has one key tile
+                        for (int e = 0; e < 8; ++e) kv[e] = kbv[ks][e];  // key == q: the block has one key tile
                     } else {
                         load8((const float *)Kb + (head_base + s0 + key) * D + d0, kv);
                     }
@@ -697,15 +696,16 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
 // LDS of the partial kernel: for a bf16 ring the chunk's keys [CH][D+8] bf16;
 // the V^T planes (one bf16 plane of CH keys for a bf16 ring, three planes for
 // f32 values, the block padded to 32 keys; every row +4 elements); the chunk's
-// slot positions; the second-half exchange [4][64][D/16*4 + 2] f32.
+// slot positions; the second-half exchange [4][64][D/16*4 + 2] f32; the q and
+// k norm weights [2][D] and the block rows' rope pairs [block][D + 4] f32.
 int attn_vt_elems(int D, int CH, int ring_dtype) {
     const int ring = (CH + 4) * (ring_dtype == DFLASH_BF16 ? 1 : 3);
     return (ring > 3 * 36 ? ring : 3 * 36) * D;
 }
-size_t attn_smem_bytes(int D, int CH, int ring_dtype) {
+size_t attn_smem_bytes(int D, int CH, int ring_dtype, int block) {
     const size_t kbytes = ring_dtype == DFLASH_BF16 ? (size_t)CH * (D + 8) * 2 : 0;
     return kbytes + (size_t)attn_vt_elems(D, CH, ring_dtype) * 2 + (size_t)CH * 4 +
-           (size_t)4 * 64 * (D / 16 * 4 + 2) * 4;
+           (size_t)4 * 64 * (D / 16 * 4 + 2) * 4 + (size_t)(2 * D + block * (D + 4)) * 4;
 }
 
 template <int D, int KT>
@@ -802,7 +802,8 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.ml = c->att_ml;
     a.o = c->att_o;
     dim3 grid(c->NCH + 1, c->Hkv, B);
-    const size_t smem = attn_smem_bytes(c->D, a.CH, c->cfg.ring_dtype);
+    if (c->cfg.block * c->D / 4 > 512) return hipErrorInvalidValue;  // rope rows staged by one float4 per thread
+    const size_t smem = attn_smem_bytes(c->D, a.CH, c->cfg.ring_dtype, c->cfg.block);
     const int hkt = a.CH / 32;
 #define DFLASH_ATTN_LAUNCH(DD, KK) hipLaunchKernelGGL((attn_partial_kernel<DD, KK>), grid, dim3(512), smem, s, a)
     if (c->D == 128 && hkt == 4) DFLASH_ATTN_LAUNCH(128, 4);

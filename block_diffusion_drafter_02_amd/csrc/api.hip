@@ -201,6 +201,7 @@ size_t carve(dflash_ctx &x, char *base) {
     x.partial = cv.take<float>(4 * pmax);
     x.partial_floats = pmax;
     x.counters = cv.take<int>(4ull * gmax);
+    x.pf_sink = cv.take<unsigned>(64);
     x.n_counters = gmax;
     x.am_val = cv.take<float>(4ull * (V / GROUP_N) * Mmax);
     x.am_idx = cv.take<int>(4ull * (V / GROUP_N) * Mmax);

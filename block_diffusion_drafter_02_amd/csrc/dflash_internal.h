@@ -259,6 +259,7 @@ struct dflash_ctx {
     int act_fmt;       // activation format of the step GEMVs
     int last_B;        // batch of the last block step (0 before the first)
     int cus;           // compute units of the device
+    unsigned *pf_sink; // target of the prefetch workgroups' never-taken store
     size_t wbytes_el;  // bytes per streamed weight element (4, 2, 1)
     char *ws;
     size_t ws_bytes;

@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 METRIC = "drafter block-step µs + achieved HBM GB/s (% of peak), real dims bf16, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "gate_up_gemv_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "block_diffusion_drafter_02_amd", "csrc", "kernels_weights.hip")
+KERNEL_SRC = [os.path.join(ROOT, "block_diffusion_drafter_02_amd", "csrc", f)
+              for f in ("kernels_weights.hip", "gemv_device.h", "dflash_internal.h")]
 
 WORKLOADS = {
     # name: (weight dtype, ring dtype, feature dtype, batch, positions injected before every step)
@@ -88,7 +89,10 @@ def visible_slots(n_past: int, window: int, block: int) -> int:
 
 
 def kernel_src_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(bytes_per_launch_alg: float):

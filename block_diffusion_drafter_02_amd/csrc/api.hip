@@ -181,8 +181,9 @@ size_t carve(dflash_ctx &x, char *base) {
     x.act_f = cv.take<void>(act_es * Mmax * E);
     x.act_d = cv.take<void>(act_es * Mmax * F);
     x.act_o = cv.take<void>(act_es * Mmax * qdim);
-    x.ss_a = cv.take<float>(4ull * G_E * Mmax);
-    x.ss_f = cv.take<float>(4ull * G_E * Mmax);
+    // sums of squares per column group; half-group launches write twice as many
+    x.ss_a = cv.take<float>(4ull * 2 * G_E * Mmax);
+    x.ss_f = cv.take<float>(4ull * 2 * G_E * Mmax);
     x.qkv_out = cv.take<float>(4ull * Mmax * nqkv);
     x.rope_cs = cv.take<float>(4ull * c.max_batch * c.block * D);
     x.att_ml = cv.take<float>(4ull * c.max_batch * c.n_head_kv * (NCH + 1) * G * 16 * 2);
@@ -200,11 +201,11 @@ size_t carve(dflash_ctx &x, char *base) {
     }
     x.partial = cv.take<float>(4 * pmax);
     x.partial_floats = pmax;
-    x.counters = cv.take<int>(4ull * gmax);
+    x.counters = cv.take<int>(4ull * 2 * gmax);  // half-group launches count per 32 columns
     x.pf_sink = cv.take<unsigned>(64);
-    x.n_counters = gmax;
-    x.am_val = cv.take<float>(4ull * (V / GROUP_N) * Mmax);
-    x.am_idx = cv.take<int>(4ull * (V / GROUP_N) * Mmax);
+    x.n_counters = 2 * gmax;
+    x.am_val = cv.take<float>(4ull * (V / 32) * Mmax);
+    x.am_idx = cv.take<int>(4ull * (V / 32) * Mmax);
     x.am_counter = cv.take<int>(4);
     x.ids = cv.take<int32_t>(4ull * Mmax);
 
@@ -451,6 +452,21 @@ EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
     return e;
 }
 
+// Columns per workgroup of a block-step projection: 32 (half a column group,
+// 16 waves, no k-split) for f32 weights when one sequence's projection has at
+// most as many half groups as the GPU has compute units and its epilogue is
+// not SwiGLU (which pairs the two halves of a group); 64 otherwise. Half groups
+// drop the split-K handshake but make every workgroup read the whole
+// activation row, which only pays where the weights dominate the reads (f32:
+// measured 2128 -> 2087 us per real-dims step; bf16 1184 -> 1250, so not used).
+// The consumers of the sums of squares that a residual epilogue writes count
+// N / width groups.
+int gemv_col_width(const dflash_ctx &x, int N, int M, int WN, int kind) {
+    if (M > 16 && x.bpartial) return GROUP_N;  // batched path: 64-column tiles
+    if (x.cfg.weight_dtype != DFLASH_F32 || mt_for(M) != 1 || WN != 1 || kind == EPI_SWIGLU) return GROUP_N;
+    return N / 32 <= x.cus ? 32 : GROUP_N;
+}
+
 int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, const EpiArgs &epi, hipStream_t s,
          int WN = 1) {
     if (epi.M > 16 && x.bpartial) {
@@ -474,14 +490,16 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     a.K = K;
     a.act = act;
     a.act_rows = x.Mmax;
-    const int G = N / (GROUP_N * WN), KB = K / KBLK;
+    const int KB = K / KBLK;
+    const int cw = gemv_col_width(x, N, epi.M, WN, epi.kind);
+    const int G = N / (cw * WN);
     int nwv = 4;
     choose_split(G, KB, a.S, a.kb_per_split);
-    if (mt_for(epi.M) == 1 && WN == 1 && 2 * G <= x.cus) {
-        // few column groups: one 16-wave workgroup per compute unit, as many
-        // k-splits as fit (the tail then has one split-K handshake at most)
+    if (cw < GROUP_N || (mt_for(epi.M) == 1 && WN == 1 && 2 * G <= x.cus)) {
+        // few column groups: one 16-wave workgroup per compute unit (half
+        // groups where that is enough to fill the GPU), as many k-splits as fit
         nwv = 16;
-        const int cap = (int)std::min<size_t>(x.partial_floats / ((size_t)G * 16 * GROUP_N), 64);
+        const int cap = (int)std::min<size_t>(x.partial_floats / ((size_t)G * 16 * cw), 64);
         const int S = std::max(1, std::min(std::min(x.cus / G, KB / 8), cap));
         a.kb_per_split = (KB + S - 1) / S;
         a.S = (KB + a.kb_per_split - 1) / a.kb_per_split;
@@ -489,7 +507,8 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     a.partial = x.partial;
     a.counters = x.counters;
     a.epi = epi;
-    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), WN, nwv, dim3(G, a.S), a, s),
+    if (G > x.n_counters) return fail(DFLASH_EINVAL, "GEMV with %d column groups exceeds the counter table", G);
+    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), WN, nwv, cw, dim3(G, a.S), a, s),
             "block-step GEMV launch");
     return DFLASH_OK;
 }
@@ -501,7 +520,8 @@ int stage_qkv(const dflash_ctx &x, int l, int M, hipStream_t s) {
     EpiArgs e = epi_base(x, EPI_SCALED, M);
     e.wscale = b.s_qkv;
     e.ss = x.ss_a;
-    e.ss_groups = x.G_E;
+    // layer 0 reads the embed kernel's 64-column sums, later layers the down projection's
+    e.ss_groups = l == 0 ? x.G_E : x.E / gemv_col_width(x, x.E, M, 1, EPI_RESID);
     e.out = x.qkv_out;
     e.ld_out = x.nqkv;
     return gemv(x, b.qkv, x.nqkv, x.E, x.act_a, e, s, QKV_WN);
@@ -525,7 +545,7 @@ int stage_gu(const dflash_ctx &x, int l, int M, hipStream_t s) {
     EpiArgs e = epi_base(x, EPI_SWIGLU, M);
     e.wscale = b.s_gu;
     e.ss = x.ss_f;
-    e.ss_groups = x.G_E;
+    e.ss_groups = x.E / gemv_col_width(x, x.E, M, 1, EPI_RESID);  // written by Wo
     e.act_out = x.act_d;
     e.act_K = x.F;
     return gemv(x, b.gu, 2 * x.F, x.E, x.act_f, e, s);
@@ -549,7 +569,7 @@ int stage_lm(const dflash_ctx &x, int M, float *logits, int32_t *drafts, const i
     EpiArgs e = epi_base(x, EPI_LOGITS, M);
     e.wscale = x.s_lm;
     e.ss = x.ss_a;
-    e.ss_groups = x.G_E;
+    e.ss_groups = x.E / gemv_col_width(x, x.E, M, 1, EPI_RESID);  // written by the last down
     e.out = logits;
     e.ld_out = x.V;
     e.am_val = x.am_val;

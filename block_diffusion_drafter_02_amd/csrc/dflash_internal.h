@@ -390,7 +390,7 @@ hipError_t launch_tile_scales(const float *src, int src_rows, float *dst, int ro
 hipError_t launch_vec_to_f32(const void *src, int dtype, int n, float *dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *codes, float *scales, hipStream_t s);
-hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, dim3 grid, const GemvArgs &a,
+hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, int CW, dim3 grid, const GemvArgs &a,
                        hipStream_t s);
 hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s, bool lanes = false);
 hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, hipStream_t s);

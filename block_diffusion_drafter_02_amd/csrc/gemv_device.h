@@ -304,12 +304,16 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs &e, int g, EpiPre &p)
     }
 }
 
-template <int EPI, int MT, int WN, bool PF = false>  // PF: operands prefetched by epi_prefetch (MT = 1)
+// CW: columns of group g (64, or 32 for half groups; lanes >= CW idle). The
+// G groups of one launch write ss_out / am_val rows 0..G-1.
+template <int EPI, int MT, int WN, bool PF = false, int CW = GROUP_N>  // PF: operands from epi_prefetch (MT = 1)
 __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, float *tile, float *rs_s, int *flag_s,
                                               int *best_s, const EpiPre &pre = EpiPre{}) {
     static_assert(!PF || MT == 1, "prefetched epilogue operands cover one row tile");
+    static_assert(!PF || CW == GROUP_N, "prefetched epilogue operands cover a full group");
+    static_assert(CW == GROUP_N || (WN == 1 && EPI != EPI_SWIGLU), "half groups: one wave column, no SwiGLU");
     constexpr int MP = MT * 16;
-    constexpr int GN = GROUP_N * WN;
+    constexpr int GN = CW * WN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int M = e.M;
     // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps): 16 threads per row, each summing
@@ -330,17 +334,19 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
         __syncthreads();
     }
 
+    const bool col_ok = CW == GROUP_N || lane < CW;
     if constexpr (EPI == EPI_SCALED) {
-        const float sc = PF ? pre.sc : (e.wscale ? e.wscale[g * GROUP_N + lane] : 1.0f);
-        for (int m = wave; m < M; m += 4) {
-            const int n = g * GROUP_N + lane;
-            float v = tile[m * GN + lane] * rs_s[m];
-            if (e.wscale) v *= sc;
-            st_f32(e.out + (size_t)m * e.ld_out + n, v);
-        }
+        const int n = g * CW + lane;
+        const float sc = PF ? pre.sc : (e.wscale && col_ok ? e.wscale[n] : 1.0f);
+        if (col_ok)
+            for (int m = wave; m < M; m += 4) {
+                float v = tile[m * GN + lane] * rs_s[m];
+                if (e.wscale) v *= sc;
+                st_f32(e.out + (size_t)m * e.ld_out + n, v);
+            }
     } else if constexpr (EPI == EPI_RESID) {
         constexpr int RPW = MP / 4;  // rows per wave; all residual loads issued first
-        const int n = g * GROUP_N + lane;
+        const int n = g * CW + lane;
         float sc, wn;
         float xv[RPW];
         if constexpr (PF) {
@@ -349,22 +355,24 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
 #pragma unroll
             for (int r = 0; r < RPW; ++r) xv[r] = pre.x[r];
         } else {
-            sc = e.wscale ? e.wscale[n] : 1.0f;
+            sc = e.wscale && col_ok ? e.wscale[n] : 1.0f;
 #pragma unroll
             for (int r = 0; r < RPW; ++r) {
                 const int m = wave + 4 * r;
-                xv[r] = m < M ? e.x[(size_t)m * e.ld_x + n] : 0.0f;
+                xv[r] = m < M && col_ok ? e.x[(size_t)m * e.ld_x + n] : 0.0f;
             }
-            wn = e.wnext[n];
+            wn = col_ok ? e.wnext[n] : 0.0f;
         }
         float *xo = e.x_out ? e.x_out : e.x;
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             const int m = wave + 4 * r;
             if (m < M) {
-                const float xn = xv[r] + tile[m * GN + lane] * sc;
-                st_f32(xo + (size_t)m * e.ld_x + n, xn);
-                write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, n, xn * wn);
+                const float xn = col_ok ? xv[r] + tile[m * GN + lane] * sc : 0.0f;
+                if (col_ok) {
+                    st_f32(xo + (size_t)m * e.ld_x + n, xn);
+                    write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, n, xn * wn);
+                }
                 const float sq = wave_sum(xn * xn);
                 if (lane == 0) st_f32(e.ss_out + (size_t)g * e.ss_stride + m, sq);
             }
@@ -385,12 +393,15 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
             }
         }
     } else {  // EPI_LOGITS
-        const float sc = PF ? pre.sc : (e.wscale ? e.wscale[g * GROUP_N + lane] : 1.0f);
+        const int n = g * CW + lane;
+        const float sc = PF ? pre.sc : (e.wscale && col_ok ? e.wscale[n] : 1.0f);
         for (int m = wave; m < M; m += 4) {
-            const int n = g * GROUP_N + lane;
-            float v = tile[m * GN + lane] * rs_s[m];
-            if (e.wscale) v *= sc;
-            st_f32(e.out + (size_t)m * e.ld_out + n, v);
+            float v = -INFINITY;
+            if (col_ok) {
+                v = tile[m * GN + lane] * rs_s[m];
+                if (e.wscale) v *= sc;
+                st_f32(e.out + (size_t)m * e.ld_out + n, v);
+            }
             float bv = v;
             int bi = n;
             for (int o = 32; o > 0; o >>= 1) {

@@ -98,39 +98,45 @@ hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *code
 // NWV = 16 (one 16-row tile, WN = 1) widens the workgroup to 16 wavefronts
 // along the reduction, so that a group needs fewer k-splits (often none): the
 // waves are summed through LDS in a fixed order, then the first four waves
-// carry on as above.
-template <int WT, int AF, int MT, int EPI, int WN, int NWV = 4>
+// carry on as above. With it, CW = 32 narrows a workgroup to half a column
+// group (two of its four tiles), which doubles the workgroups without a k-split.
+template <int WT, int AF, int MT, int EPI, int WN, int NWV = 4, int CW = GROUP_N>
 __global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
     static_assert(NWV == 4 || (NWV == 16 && MT == 1 && WN == 1), "wide workgroups take one tile group");
+    static_assert(CW == GROUP_N || (CW == 32 && NWV == 16 && EPI != EPI_SWIGLU), "half groups: 16 waves, no SwiGLU");
     constexpr int NV = WTraits<WT>::NV;
     constexpr int NW = AFTraits<AF>::NW;
     constexpr int MP = MT * 16;
-    constexpr int GN = GROUP_N * WN;  // columns per group
-    constexpr int WK = NWV / WN;      // waves along the reduction
+    constexpr int TPW = CW / 16;     // 16-column tiles per workgroup and wave column
+    constexpr int GN = CW * WN;      // columns per group
+    constexpr int WK = NWV / WN;     // waves along the reduction
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wn = wave % WN, wk = wave / WN;
     const int g = blockIdx.x, s = blockIdx.y;
     const int G = a.N / GN, KB = a.K / KBLK;
+    // stored 64-column group and first tile of this workgroup's columns
+    const int gs = g * CW / GROUP_N, t0 = (g * CW % GROUP_N) / 16;
     const int kb0 = s * a.kb_per_split;
     const int kb1 = min(KB, kb0 + a.kb_per_split);
     const int M = a.epi.M;
 
-    f32x4 acc[MT][4];
+    f32x4 acc[MT][TPW];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < TPW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int kb = kb0 + wk; kb < kb1; kb += WK) {
-        u32x4 w[4][NV];
+        u32x4 w[TPW][NV];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) load_wtile<WT>(a.W, ((size_t)g * KB + kb) * 4 * WN + 4 * wn + t, lane, w[t]);
+        for (int t = 0; t < TPW; ++t)
+            load_wtile<WT>(a.W, ((size_t)gs * KB + kb) * 4 * WN + 4 * wn + t0 + t, lane, w[t]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             u32x4 av[NW];
             load_act_lanes<AF>(a.act, a.act_rows, a.K, mt, mt * 16 < M, kb, lane, av);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) tile_mfma<WT, AF>(w[t], av, acc[mt][t]);
+            for (int t = 0; t < TPW; ++t) tile_mfma<WT, AF>(w[t], av, acc[mt][t]);
         }
     }
 
@@ -141,16 +147,16 @@ __global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
     if constexpr (NWV == 16) {
         // waves 0-7 store, waves 8-15 add into wave w-8's slot, then thread t
         // sums element t over the eight slots in slot order
-        __shared__ float red[8][16 * GROUP_N];
+        __shared__ float red[8][16 * CW];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             if ((wk >> 3) == half) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int t = 0; t < TPW; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int m = 4 * (lane >> 4) + i, col = 16 * t + (lane & 15);
-                        float *r = &red[wk & 7][m * GROUP_N + col];
+                        float *r = &red[wk & 7][m * CW + col];
                         if (half == 0)
                             *r = acc[0][t][i];
                         else
@@ -159,10 +165,12 @@ __global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
             }
             __syncthreads();
         }
-        float v = red[0][tid];
+        if (tid < 16 * CW) {
+            float v = red[0][tid];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) v += red[i][tid];
-        tile[tid] = v;
+            for (int i = 1; i < 8; ++i) v += red[i][tid];
+            tile[tid] = v;
+        }
         __syncthreads();
         if (tid >= 256) return;  // the split-K handshake and the epilogue run on four waves
     } else {
@@ -174,16 +182,22 @@ __global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
                                    (size_t)G * TE, a.S, &a.counters[g], &flag_s))
             return;
     }
-    gemv_epilogue<EPI, MT, WN>(a.epi, g, G, tile, rs_s, &flag_s, best_s);
+    gemv_epilogue<EPI, MT, WN, false, CW>(a.epi, g, G, tile, rs_s, &flag_s, best_s);
 }
 
 template <int WT, int AF, int EPI, int WN>
-static hipError_t launch_gemv_mt(int MT, int NWV, dim3 grid, const GemvArgs &a, hipStream_t s) {
+static hipError_t launch_gemv_mt(int MT, int NWV, int CW, dim3 grid, const GemvArgs &a, hipStream_t s) {
     if (NWV == 16) {
         if (MT != 1 || WN != 1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI, 1, 16>), grid, dim3(1024), 0, s, a);
+        if (CW == 32) {
+            if constexpr (EPI == EPI_SWIGLU) return hipErrorInvalidValue;
+            else hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI, 1, 16, 32>), grid, dim3(1024), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI, 1, 16>), grid, dim3(1024), 0, s, a);
+        }
         return hipGetLastError();
     }
+    if (CW != GROUP_N) return hipErrorInvalidValue;
     if (NWV != 4) return hipErrorInvalidValue;
     switch (MT) {
         case 1: hipLaunchKernelGGL((gemv_kernel<WT, AF, 1, EPI, WN>), grid, dim3(256), 0, s, a); break;
@@ -197,25 +211,25 @@ static hipError_t launch_gemv_mt(int MT, int NWV, dim3 grid, const GemvArgs &a, 
 
 // Every projection streams 64-column groups (WN = 1).
 template <int WT, int AF>
-static hipError_t launch_gemv_epi(int MT, int WN, int NWV, dim3 grid, const GemvArgs &a, hipStream_t s) {
+static hipError_t launch_gemv_epi(int MT, int WN, int NWV, int CW, dim3 grid, const GemvArgs &a, hipStream_t s) {
     if (WN != 1) return hipErrorInvalidValue;
     switch (a.epi.kind) {
-        case EPI_SCALED: return launch_gemv_mt<WT, AF, EPI_SCALED, 1>(MT, NWV, grid, a, s);
-        case EPI_RESID: return launch_gemv_mt<WT, AF, EPI_RESID, 1>(MT, NWV, grid, a, s);
-        case EPI_SWIGLU: return launch_gemv_mt<WT, AF, EPI_SWIGLU, 1>(MT, NWV, grid, a, s);
-        case EPI_LOGITS: return launch_gemv_mt<WT, AF, EPI_LOGITS, 1>(MT, NWV, grid, a, s);
+        case EPI_SCALED: return launch_gemv_mt<WT, AF, EPI_SCALED, 1>(MT, NWV, CW, grid, a, s);
+        case EPI_RESID: return launch_gemv_mt<WT, AF, EPI_RESID, 1>(MT, NWV, CW, grid, a, s);
+        case EPI_SWIGLU: return launch_gemv_mt<WT, AF, EPI_SWIGLU, 1>(MT, NWV, CW, grid, a, s);
+        case EPI_LOGITS: return launch_gemv_mt<WT, AF, EPI_LOGITS, 1>(MT, NWV, CW, grid, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, dim3 grid, const GemvArgs &a,
+hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, int CW, dim3 grid, const GemvArgs &a,
                        hipStream_t s) {
     if (wdtype == DFLASH_F32 && act_fmt == ACT_F32)
-        return launch_gemv_epi<DFLASH_F32, ACT_F32>(MT, WN, NWV, grid, a, s);
+        return launch_gemv_epi<DFLASH_F32, ACT_F32>(MT, WN, NWV, CW, grid, a, s);
     if (wdtype == DFLASH_BF16 && act_fmt == ACT_SPLIT3)
-        return launch_gemv_epi<DFLASH_BF16, ACT_SPLIT3>(MT, WN, NWV, grid, a, s);
+        return launch_gemv_epi<DFLASH_BF16, ACT_SPLIT3>(MT, WN, NWV, CW, grid, a, s);
     if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_SPLIT3)
-        return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, WN, NWV, grid, a, s);
+        return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, WN, NWV, CW, grid, a, s);
     return hipErrorInvalidValue;
 }
 

@@ -220,6 +220,39 @@ struct EpiArgs {
     int32_t *n_ok;        // [B] or null
 };
 
+// Bytes that a later launch reads, to be read now by otherwise idle compute
+// units so that they sit in the memory-side cache. (Measured: worth it only
+// inside the attention launch; compute units left idle by a weight-streaming
+// launch are not free, extra reads there slow its own stream.)
+struct Prefetch {
+    const char *base;
+    size_t bytes;
+    unsigned *sink;  // written only if the loaded words hash to a fixed value (keeps the loads)
+};
+
+// Workgroup p of P reads its share of the prefetch bytes and drops them.
+// (Taken by value: a reference into a kernel argument would put the argument
+// in scratch memory.)
+__device__ __forceinline__ void prefetch_slice(Prefetch f, int p, int P) {
+    const size_t n16 = f.bytes / 16, per = (n16 + P - 1) / P;
+    const size_t i0 = (size_t)p * per, i1 = n16 < i0 + per ? n16 : i0 + per;
+    const uint4 *src = (const uint4 *)f.base;
+    uint32_t acc = 0;
+    constexpr int U = 8;
+    const size_t nt = blockDim.x;
+    for (size_t i = i0 + threadIdx.x; i < i1; i += U * nt) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const size_t k = i + u * nt;
+            v[u] = k < i1 ? src[k] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    if (acc == 0x9e3779b9u && f.sink != nullptr) *f.sink = acc;
+}
+
 struct GemvArgs {
     const void *W;  // tiled weights
     int N, K;       // output columns (multiple of 64), reduction length (multiple of 64)
@@ -422,4 +455,17 @@ __host__ __device__ inline size_t ring_v_offset(int L, int Hkv, int W, int D, in
 }
 __host__ __device__ inline size_t ring_pos_offset(int L, int Hkv, int W, int D, int es) {
     return ring_v_offset(L, Hkv, W, D, es) + align256(ring_kv_elems(L, Hkv, W, D) * es);
+}
+
+// Memory-side cache prefetch of the attention launch
+inline size_t gu_bytes(const dflash_ctx &c) { return (size_t)2 * c.F * c.E * c.wbytes_el; }
+// prefetch workgroups of an attention launch (one per compute unit its grid leaves idle, per kv head and sequence)
+inline int attn_pf_x(const dflash_ctx &c, int B) {
+    const int attn_wgs = (c.NCH + 1) * c.Hkv * B;
+    return (c.cus > attn_wgs ? c.cus - attn_wgs : 0) / (c.Hkv * B);
+}
+// gate/up bytes the attention launch of one layer reads ahead: 0.5 MB per prefetch workgroup
+inline size_t attn_gu_prefetch(const dflash_ctx &c, int B) {
+    const size_t want = (size_t)attn_pf_x(c, B) * c.Hkv * B << 19;
+    return want < gu_bytes(c) ? want : gu_bytes(c);
 }

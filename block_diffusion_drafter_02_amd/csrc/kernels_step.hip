@@ -329,34 +329,12 @@ struct AttnArgs {
     const float *q_norm, *k_norm;  // [D]
     const float *rope_cs;          // [B][block][D/2][2] (cos, sin) at position n_past + i
     float eps, qscale;             // qscale = 1/sqrt(D), folded into q
-    // workgroups c > NCH read pf_bytes of weights that a later launch streams
-    // (into the memory-side cache) while the attention workgroups run
-    const char *pf;
-    size_t pf_bytes;
+    // workgroups c > NCH read `pf` (into the memory-side cache) while the
+    // attention workgroups run
+    Prefetch pf;
     int pf_x;                      // such workgroups per (kv head, sequence)
-    unsigned *pf_sink;             // written only if the loaded words hash to a fixed value
 };
 
-// Read slice p of P of a byte range and drop it; the loads are kept by a
-// data-dependent store that in practice never happens.
-__device__ __forceinline__ void prefetch_slice(const char *base, size_t bytes, unsigned *sink, int p, int P) {
-    const size_t n16 = bytes / 16, per = (n16 + P - 1) / P;
-    const size_t i0 = (size_t)p * per, i1 = min(n16, i0 + per);
-    const uint4 *src = (const uint4 *)base;
-    uint32_t acc = 0;
-    constexpr int U = 8, NT = 512;
-    for (size_t i = i0 + threadIdx.x; i < i1; i += (size_t)U * NT) {
-        uint4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const size_t k = i + (size_t)u * NT;
-            v[u] = k < i1 ? src[k] : make_uint4(0u, 0u, 0u, 0u);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    }
-    if (acc == 0x9e3779b9u && sink != nullptr) *sink = acc;
-}
 
 // One head vector of query or key row `row` of sequence b, held as
 // v[ks][e] = element 32ks + 8grp + e by the four lanes grp = 0..3 that share a
@@ -448,8 +426,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     extern __shared__ float smem[];
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     if (c > a.NCH) {  // a prefetch workgroup: no LDS, no barriers
-        prefetch_slice(a.pf, a.pf_bytes, a.pf_sink, (b * a.Hkv + j) * a.pf_x + (c - a.NCH - 1),
-                       a.pf_x * a.Hkv * gridDim.z);
+        prefetch_slice(a.pf, (b * a.Hkv + j) * a.pf_x + (c - a.NCH - 1), a.pf_x * a.Hkv * gridDim.z);
         return;
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -839,11 +816,11 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     // memory-side cache meanwhile (the gate/up GEMV is bandwidth-bound; the Wo
     // GEMV in between is latency-bound): 0.5 MB per such workgroup, an amount
     // one compute unit reads within the attention kernel's run time.
-    const int attn_wgs = (c->NCH + 1) * c->Hkv * B;
-    a.pf_x = std::max(0, c->cus - attn_wgs) / (c->Hkv * B);
-    a.pf = (const char *)c->layer[l].gu;
-    a.pf_bytes = std::min((size_t)2 * c->F * c->E * c->wbytes_el, (size_t)a.pf_x * c->Hkv * B << 19);
-    a.pf_sink = c->pf_sink;
+    a.pf_x = attn_pf_x(*c, B);
+    a.pf = Prefetch{};
+    a.pf.base = (const char *)c->layer[l].gu;
+    a.pf.bytes = attn_gu_prefetch(*c, B);
+    a.pf.sink = c->pf_sink;
     dim3 grid(c->NCH + 1 + a.pf_x, c->Hkv, B);
     if (c->cfg.block * c->D / 4 > 512) return hipErrorInvalidValue;  // rope rows staged by one float4 per thread
     const size_t smem = attn_smem_bytes(c->D, a.CH, c->cfg.ring_dtype, c->cfg.block);

@@ -175,7 +175,9 @@ size_t carve(dflash_ctx &x, char *base) {
     x.lm = cv.take<void>(esw * (size_t)V * E);
     x.s_lm = fp8 ? cv.take<float>(4ull * V) : nullptr;
 
-    const int G_E = E / GROUP_N, G = c.n_head / c.n_head_kv, NCH = c.window / attn_chunk(c.ring_dtype, c.window);
+    // attention partials: the most chunks any batch size uses (the smallest chunk)
+    const int G_E = E / GROUP_N, G = c.n_head / c.n_head_kv,
+              NCH = c.window / std::min(attn_chunk(c.ring_dtype, c.window, 1), attn_chunk(c.ring_dtype, c.window, 2));
     x.x = cv.take<float>(4ull * Mmax * E);
     x.act_a = cv.take<void>(act_es * Mmax * E);
     x.act_f = cv.take<void>(act_es * Mmax * E);
@@ -260,7 +262,6 @@ void derive(dflash_ctx &x) {
     x.nqkv = x.qdim + 2 * x.kvdim;
     x.Mmax = 16 * c.max_batch;
     x.G_E = x.E / GROUP_N;
-    x.NCH = x.W / attn_chunk(c.ring_dtype, x.W);
     x.act_fmt = c.weight_dtype == DFLASH_F32 ? ACT_F32 : ACT_SPLIT3;
     x.wbytes_el = dtype_bytes(c.weight_dtype);
 }

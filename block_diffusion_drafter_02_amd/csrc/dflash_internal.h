@@ -288,7 +288,7 @@ struct PStepArgs;  // persistent chain arguments (below)
 struct dflash_ctx {
     dflash_config cfg;
     int device;
-    int E, H, Hkv, D, F, W, L, V, C, qdim, kvdim, nqkv, Mmax, G_E, NCH;
+    int E, H, Hkv, D, F, W, L, V, C, qdim, kvdim, nqkv, Mmax, G_E;
     int act_fmt;       // activation format of the step GEMVs
     int last_B;        // batch of the last block step (0 before the first)
     int cus;           // compute units of the device
@@ -438,12 +438,16 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, const int32_t *n_past, int B,
                             hipStream_t s);
 hipError_t attention_set_smem_limit();
-// ring slots per attention chunk (one workgroup per chunk and kv head): 128
-// (64 when the window is not a multiple of 128) for a bf16 ring, 32 for an
-// f32 ring (its values take three planes of LDS)
-inline int attn_chunk(int ring_dtype, int W) {
+// Attention partial workgroups: 512 threads (two wavefronts per q head) for one
+// sequence, whose chunks alone leave most compute units idle; 256 threads for
+// several sequences, so that two workgroups share a compute unit.
+inline int attn_threads(int B) { return B == 1 ? 512 : 256; }
+// ring slots per attention chunk (one workgroup per chunk and kv head): for a
+// bf16 ring 128 with 512 threads (64 when the window is not a multiple of 128)
+// and 64 with 256; 32 for an f32 ring (its values take three planes of LDS)
+inline int attn_chunk(int ring_dtype, int W, int B) {
     if (ring_dtype != DFLASH_BF16) return 32;
-    return W % 128 == 0 ? 128 : 64;
+    return attn_threads(B) == 512 && W % 128 == 0 ? 128 : 64;
 }
 hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, int n, int32_t *n_ok, hipStream_t s);
 
@@ -461,7 +465,7 @@ __host__ __device__ inline size_t ring_pos_offset(int L, int Hkv, int W, int D, 
 inline size_t gu_bytes(const dflash_ctx &c) { return (size_t)2 * c.F * c.E * c.wbytes_el; }
 // prefetch workgroups of an attention launch (one per compute unit its grid leaves idle, per kv head and sequence)
 inline int attn_pf_x(const dflash_ctx &c, int B) {
-    const int attn_wgs = (c.NCH + 1) * c.Hkv * B;
+    const int attn_wgs = (c.W / attn_chunk(c.cfg.ring_dtype, c.W, B) + 1) * c.Hkv * B;
     return (c.cus > attn_wgs ? c.cus - attn_wgs : 0) / (c.Hkv * B);
 }
 // gate/up bytes the attention launch of one layer reads ahead: 0.5 MB per prefetch workgroup

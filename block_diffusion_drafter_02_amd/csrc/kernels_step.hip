@@ -299,13 +299,15 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 // ---------------------------------------------------------------------------
 // Non-causal sliding-window GQA attention (dflash-ops card, Method)
 // ---------------------------------------------------------------------------
-// Partial kernel: grid (NCH + 1, Hkv, B), 512 threads = 8 wavefronts. Chunk
-// c < NCH covers ring slots [c*CH, c*CH + CH); chunk NCH is the block's own 16
-// keys. Every wave RMS-norms (q_norm) and ropes its q head at positions
-// n_past + i and scales it by 1/sqrt(D); the block chunk does the same for the
-// block's k (k_norm, no scale). Wave w serves q head jG + (w % 4) for the
-// first (w < 4) or second half of the chunk's key tiles; the two halves merge
-// through LDS.
+// Partial kernel: grid (NCH + 1, Hkv, B), NT threads (512 for one sequence,
+// 256 for several). Chunk c < NCH covers ring slots [c*CH, c*CH + CH) with
+// CH = 16 * HKT * NT / 256; chunk NCH is the block's own 16 keys. Every wave
+// RMS-norms (q_norm) and ropes its q head at positions n_past + i and scales it
+// by 1/sqrt(D); the block chunk does the same for the block's k (k_norm, no
+// scale). Wave w serves q head jG + (w % 4) for HKT key tiles: with 512 threads
+// the first (w < 4) or second half of the chunk, the two halves merging through
+// LDS; with 256 threads the whole chunk, so that two workgroups share a
+// compute unit when a batch brings many more chunks than compute units.
 //
 // Scores are computed transposed, S^T = K Q^T (keys as MFMA rows, queries as
 // columns), so that each lane holds the scores of one query for 4 keys of every
@@ -417,12 +419,14 @@ __device__ __forceinline__ void load8(const float *p, float (&v)[8]) {
 
 #define MFMA_BF16(A, B, C) __builtin_amdgcn_mfma_f32_16x16x32_bf16((A), (B), (C), 0, 0, 0)
 
-template <int D, int HKT>
-__global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
+template <int D, int HKT, int NT>
+__global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
+    static_assert(NT == 256 || NT == 512, "one or two wavefronts per q head");
+    constexpr int NHALF = NT / 256;  // wavefronts per q head
     constexpr int KS = D / 32;   // MFMA k-steps over the head dimension
     constexpr int DT = D / 16;   // 16-wide tiles of the head dimension
     constexpr int KROW = D + 8;  // bf16 elements per staged K row (+8 spreads LDS banks)
-                                 // HKT: 16-key tiles per half chunk (CH = 32 * HKT)
+                                 // HKT: 16-key tiles per wavefront (CH = 16 * HKT * NHALF)
     extern __shared__ float smem[];
     const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
     if (c > a.NCH) {  // a prefetch workgroup: no LDS, no barriers
@@ -441,8 +445,8 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     uint16_t *ksh = (uint16_t *)smem;                              // [CH][KROW] bf16 ring keys
     uint16_t *vt = ksh + (bf16_ring ? a.CH * KROW : 0);            // [planes][D][CHP] V^T in bf16 terms
     int *kpos = (int *)(vt + a.vt_elems);                          // [CH] positions of the chunk's slots
-    float *xch = (float *)(kpos + a.CH);                           // [4][64][DT*4 + 2] second-half results
-    float *wsh = xch + 4 * 64 * (DT * 4 + 2);                       // [2][D] q_norm, k_norm
+    float *xch = (float *)(kpos + a.CH);                           // [4][64][DT*4 + 2] second-half results (NHALF 2)
+    float *wsh = xch + (NHALF > 1 ? 4 * 64 * (DT * 4 + 2) : 0);     // [2][D] q_norm, k_norm
     float *csh = wsh + 2 * D;                                       // [block][D + 4] rope (cos, sin) pairs
 
     const int es = bf16_ring ? 2 : 4;
@@ -469,15 +473,19 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
     }
     const int kp_reg = (!is_block && tid < a.CH) ? sp[s0 + tid] : 0;
     const int ncs4 = a.block * D / 4;  // float4 words of the rope table rows (at most 512)
-    float4 cs_reg = make_float4(0.f, 0.f, 0.f, 0.f), w_reg = cs_reg;
-    if (tid < ncs4) cs_reg = *(const float4 *)(a.rope_cs + (size_t)b * a.block * D + 4 * tid);
+    constexpr int NCS = 512 / NT;
+    float4 cs_reg[NCS], w_reg = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < NCS; ++u)
+        cs_reg[u] = tid + NT * u < ncs4 ? *(const float4 *)(a.rope_cs + (size_t)b * a.block * D + 4 * (tid + NT * u))
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid < D / 2) w_reg = *(const float4 *)((tid < D / 4 ? a.q_norm : a.k_norm) + 4 * (tid % (D / 4)));
 
     // ---- chunk keys and values into LDS ----
     if (is_block) {
-        for (int idx = tid; idx < 3 * D * CHP; idx += 512) vt[idx] = 0;  // keys 16..31 pad the k-step
+        for (int idx = tid; idx < 3 * D * CHP; idx += NT) vt[idx] = 0;  // keys 16..31 pad the k-step
         __syncthreads();
-        for (int idx = tid; idx < 16 * D; idx += 512) {
+        for (int idx = tid; idx < 16 * D; idx += NT) {
             const int key = idx / D, d = idx % D;
             uint16_t t0, t1, t2;
             split3(qkvb[(size_t)key * a.nqkv + a.qdim + a.kvdim + (size_t)j * D + d], t0, t1, t2);
@@ -487,7 +495,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
         }
     } else if (bf16_ring) {
         // K rows and V rows: CH*D/8 16-byte words each, in batches with all loads in flight
-        constexpr int NWORD = (32 * HKT * D / 8 + 511) / 512;
+        constexpr int NWORD = (16 * NHALF * HKT * D / 8 + NT - 1) / NT;
         constexpr int BATCH = NWORD < 4 ? NWORD : 4;
         const int nword = a.CH * D / 8;
         const uint16_t *kg = (const uint16_t *)Kb + (head_base + s0) * D;
@@ -497,13 +505,13 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
             uint4 kbuf[BATCH], vbuf[BATCH];
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int w = min(tid + 512 * (u0 + u), nword - 1);  // clamped: every lane loads
+                const int w = min(tid + NT * (u0 + u), nword - 1);  // clamped: every lane loads
                 kbuf[u] = *(const uint4 *)(kg + 8 * (size_t)w);
                 vbuf[u] = *(const uint4 *)(vg + 8 * (size_t)w);
             }
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int w = tid + 512 * (u0 + u);
+                const int w = tid + NT * (u0 + u);
                 if (w < nword) {
                     const int key = (8 * w) / D, d = (8 * w) % D;
                     *(uint4 *)(ksh + key * KROW + d) = kbuf[u];
@@ -518,7 +526,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
         }
     } else {
         // f32 ring: values split into three planes (keys are read from memory and split at use)
-        constexpr int NW4 = (32 * HKT * D / 4 + 511) / 512;
+        constexpr int NW4 = (16 * NHALF * HKT * D / 4 + NT - 1) / NT;
         constexpr int BATCH = NW4 < 8 ? NW4 : 8;
         const int nw4 = a.CH * D / 4;
         const float *vg = (const float *)Vb + (head_base + s0) * D;
@@ -526,10 +534,10 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
         for (int u0 = 0; u0 < NW4; u0 += BATCH) {
             float4 buf[BATCH];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) buf[u] = *(const float4 *)(vg + 4 * (size_t)min(tid + 512 * (u0 + u), nw4 - 1));
+            for (int u = 0; u < BATCH; ++u) buf[u] = *(const float4 *)(vg + 4 * (size_t)min(tid + NT * (u0 + u), nw4 - 1));
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
-                const int w = tid + 512 * (u0 + u);
+                const int w = tid + NT * (u0 + u);
                 if (w < nw4) {
                     const int key = (4 * w) / D, d = (4 * w) % D;
                     const float f[4] = {buf[u].x, buf[u].y, buf[u].z, buf[u].w};
@@ -546,7 +554,11 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
         }
     }
     if (!is_block && tid < a.CH) kpos[tid] = kp_reg;
-    if (tid < ncs4) *(float4 *)(csh + (4 * tid / D) * (D + 4) + 4 * tid % D) = cs_reg;  // rows padded against bank conflicts
+#pragma unroll
+    for (int u = 0; u < NCS; ++u) {  // rope rows padded against bank conflicts
+        const int i4 = 4 * (tid + NT * u);
+        if (tid + NT * u < ncs4) *(float4 *)(csh + (i4 / D) * (D + 4) + i4 % D) = cs_reg[u];
+    }
     if (tid < D / 2) *(float4 *)(wsh + 4 * tid) = w_reg;
     __syncthreads();
 
@@ -668,6 +680,9 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
         }
     }
     // ---- merge the second half into the first through LDS ----
+    if constexpr (NHALF == 1) {
+        if (!active) return;
+    } else {
     constexpr int XS = DT * 4 + 2;
     if (half == 1 && active) {
         float *xp = xch + ((size_t)hh * 64 + lane) * XS;
@@ -693,6 +708,7 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
             for (int i = 0; i < 4; ++i) ot[dt][i] = ot[dt][i] * a1 + xp[dt * 4 + i] * a2;
         mx = mn;
     }
+    }
     // ---- partial (max, sum, unnormalised output) of query (hh, q) ----
     const size_t slot = (((size_t)b * a.Hkv + j) * (a.NCH + 1) + c) * NQ + hh * 16 + q;
     if (grp == 0) {
@@ -707,33 +723,38 @@ __global__ __launch_bounds__(512) void attn_partial_kernel(AttnArgs a) {
 // LDS of the partial kernel: for a bf16 ring the chunk's keys [CH][D+8] bf16;
 // the V^T planes (one bf16 plane of CH keys for a bf16 ring, three planes for
 // f32 values, the block padded to 32 keys; every row +4 elements); the chunk's
-// slot positions; the second-half exchange [4][64][D/16*4 + 2] f32; the q and
-// k norm weights [2][D] and the block rows' rope pairs [block][D + 4] f32.
+// slot positions; the second-half exchange [4][64][D/16*4 + 2] f32 (512
+// threads only); the q and k norm weights [2][D] and the block rows' rope
+// pairs [block][D + 4] f32.
 int attn_vt_elems(int D, int CH, int ring_dtype) {
     const int ring = (CH + 4) * (ring_dtype == DFLASH_BF16 ? 1 : 3);
     return (ring > 3 * 36 ? ring : 3 * 36) * D;
 }
-size_t attn_smem_bytes(int D, int CH, int ring_dtype, int block) {
+size_t attn_smem_bytes(int D, int CH, int ring_dtype, int block, int NT) {
     const size_t kbytes = ring_dtype == DFLASH_BF16 ? (size_t)CH * (D + 8) * 2 : 0;
     return kbytes + (size_t)attn_vt_elems(D, CH, ring_dtype) * 2 + (size_t)CH * 4 +
-           (size_t)4 * 64 * (D / 16 * 4 + 2) * 4 + (size_t)(2 * D + block * (D + 4)) * 4;
+           (NT > 256 ? (size_t)4 * 64 * (D / 16 * 4 + 2) * 4 : 0) + (size_t)(2 * D + block * (D + 4)) * 4;
 }
 
-template <int D, int KT>
+template <int D, int KT, int NT>
 static hipError_t set_attn_limit(int bytes) {
-    return hipFuncSetAttribute((const void *)attn_partial_kernel<D, KT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               bytes);
+    return hipFuncSetAttribute((const void *)attn_partial_kernel<D, KT, NT>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 hipError_t attention_set_smem_limit() {
     const int bytes = 160 * 1024;
     hipError_t e;
-    if ((e = set_attn_limit<128, 4>(bytes)) != hipSuccess) return e;
-    if ((e = set_attn_limit<128, 2>(bytes)) != hipSuccess) return e;
-    if ((e = set_attn_limit<128, 1>(bytes)) != hipSuccess) return e;
-    if ((e = set_attn_limit<64, 4>(bytes)) != hipSuccess) return e;
-    if ((e = set_attn_limit<64, 2>(bytes)) != hipSuccess) return e;
-    return set_attn_limit<64, 1>(bytes);
+    if ((e = set_attn_limit<128, 4, 512>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<128, 2, 512>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<128, 1, 512>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<64, 4, 512>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<64, 2, 512>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<64, 1, 512>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<128, 4, 256>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<128, 2, 256>(bytes)) != hipSuccess) return e;
+    if ((e = set_attn_limit<64, 4, 256>(bytes)) != hipSuccess) return e;
+    return set_attn_limit<64, 2, 256>(bytes);
 }
 
 // Combine kernel: grid (H, B, D / 32), 256 threads. Thread t serves block row
@@ -805,8 +826,9 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.W = c->W;
     a.ring_dtype = c->cfg.ring_dtype;
     a.G = c->H / c->Hkv;
-    a.NCH = c->NCH;
-    a.CH = c->W / c->NCH;
+    const int NT = attn_threads(B);
+    a.CH = attn_chunk(c->cfg.ring_dtype, c->W, B);
+    a.NCH = c->W / a.CH;
     a.vt_elems = attn_vt_elems(c->D, a.CH, c->cfg.ring_dtype);
     a.block = c->cfg.block;
     a.n_past = n_past;
@@ -821,17 +843,22 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.pf.base = (const char *)c->layer[l].gu;
     a.pf.bytes = attn_gu_prefetch(*c, B);
     a.pf.sink = c->pf_sink;
-    dim3 grid(c->NCH + 1 + a.pf_x, c->Hkv, B);
-    if (c->cfg.block * c->D / 4 > 512) return hipErrorInvalidValue;  // rope rows staged by one float4 per thread
-    const size_t smem = attn_smem_bytes(c->D, a.CH, c->cfg.ring_dtype, c->cfg.block);
-    const int hkt = a.CH / 32;
-#define DFLASH_ATTN_LAUNCH(DD, KK) hipLaunchKernelGGL((attn_partial_kernel<DD, KK>), grid, dim3(512), smem, s, a)
-    if (c->D == 128 && hkt == 4) DFLASH_ATTN_LAUNCH(128, 4);
-    else if (c->D == 128 && hkt == 2) DFLASH_ATTN_LAUNCH(128, 2);
-    else if (c->D == 128 && hkt == 1) DFLASH_ATTN_LAUNCH(128, 1);
-    else if (c->D == 64 && hkt == 4) DFLASH_ATTN_LAUNCH(64, 4);
-    else if (c->D == 64 && hkt == 2) DFLASH_ATTN_LAUNCH(64, 2);
-    else if (c->D == 64 && hkt == 1) DFLASH_ATTN_LAUNCH(64, 1);
+    dim3 grid(a.NCH + 1 + a.pf_x, c->Hkv, B);
+    if (c->cfg.block * c->D / 4 > 512) return hipErrorInvalidValue;  // rope rows: at most 512 float4 words
+    const size_t smem = attn_smem_bytes(c->D, a.CH, c->cfg.ring_dtype, c->cfg.block, NT);
+    const int hkt = a.CH * 256 / (16 * NT);
+#define DFLASH_ATTN_LAUNCH(DD, KK, TT) \
+    hipLaunchKernelGGL((attn_partial_kernel<DD, KK, TT>), grid, dim3(TT), smem, s, a)
+    if (NT == 512 && c->D == 128 && hkt == 4) DFLASH_ATTN_LAUNCH(128, 4, 512);
+    else if (NT == 512 && c->D == 128 && hkt == 2) DFLASH_ATTN_LAUNCH(128, 2, 512);
+    else if (NT == 512 && c->D == 128 && hkt == 1) DFLASH_ATTN_LAUNCH(128, 1, 512);
+    else if (NT == 512 && c->D == 64 && hkt == 4) DFLASH_ATTN_LAUNCH(64, 4, 512);
+    else if (NT == 512 && c->D == 64 && hkt == 2) DFLASH_ATTN_LAUNCH(64, 2, 512);
+    else if (NT == 512 && c->D == 64 && hkt == 1) DFLASH_ATTN_LAUNCH(64, 1, 512);
+    else if (NT == 256 && c->D == 128 && hkt == 4) DFLASH_ATTN_LAUNCH(128, 4, 256);
+    else if (NT == 256 && c->D == 128 && hkt == 2) DFLASH_ATTN_LAUNCH(128, 2, 256);
+    else if (NT == 256 && c->D == 64 && hkt == 4) DFLASH_ATTN_LAUNCH(64, 4, 256);
+    else if (NT == 256 && c->D == 64 && hkt == 2) DFLASH_ATTN_LAUNCH(64, 2, 256);
     else return hipErrorInvalidValue;
 #undef DFLASH_ATTN_LAUNCH
     hipError_t err = hipGetLastError();
@@ -839,7 +866,7 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     CombArgs cb;
     cb.ml = c->att_ml;
     cb.o = c->att_o;
-    cb.NCH = c->NCH;
+    cb.NCH = a.NCH;
     cb.G = a.G;
     cb.Hkv = c->Hkv;
     cb.D = c->D;

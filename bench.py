@@ -16,6 +16,7 @@ on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -34,11 +35,12 @@ KERNEL_SRC = [os.path.join(ROOT, "block_diffusion_drafter_02_amd", "csrc", f)
               for f in ("kernels_weights.hip", "gemv_device.h", "dflash_internal.h")]
 
 WORKLOADS = {
-    # name: (weight dtype, ring dtype, feature dtype, batch, positions injected before every step)
-    "bf16": ("bf16", "bf16", "bf16", 1, 0),
-    "f32": ("f32", "f32", "f32", 1, 0),
-    "bf16-batch8": ("bf16", "bf16", "bf16", 8, 0),
-    "fp8-inject512": ("fp8", "bf16", "bf16", 1, 512),
+    # name: (weight dtype, ring dtype, feature dtype, batch, positions injected before every step, block width)
+    "bf16": ("bf16", "bf16", "bf16", 1, 0, 16),
+    "f32": ("f32", "f32", "f32", 1, 0, 16),
+    "bf16-batch8": ("bf16", "bf16", "bf16", 8, 0, 16),
+    "fp8-inject512": ("fp8", "bf16", "bf16", 1, 512, 16),
+    "bf16-g4": ("bf16", "bf16", "bf16", 1, 0, 4),
 }
 FEATURE_POOL = 4  # distinct resident feature blocks cycled by the per-step inject (content does not change cost)
 
@@ -107,13 +109,13 @@ def read_traffic(bytes_per_launch_alg: float):
 
 
 def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes, inject_feats=None, min_seconds=10.0,
-                 max_seconds=30.0):
+                 max_seconds=30.0, block_width=16):
     """The oracle, as it stands, for block steps of one sequence at the same dimensions on a synthetic ring
     with the same fill (each preceded by encoding and injecting ``inject_feats`` when given); returns the rate
     in the metric's unit (algorithmic GB/s)."""
     from oracle import dflash_oracle as O
 
-    cfg = O.Config.from_shape(shape, rdt)
+    cfg = dataclasses.replace(O.Config.from_shape(shape, rdt), block=block_width)
     w = O.Weights(raw, wdt)
     ring = O.Ring(cfg)
     rng = np.random.default_rng(0)
@@ -150,7 +152,8 @@ def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes, inject_feats=None, m
     per = dt / steps
     return {"value": round(total_bytes / per / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds_per_step": round(per, 3), "steps": steps,
-            "sample": f"{steps} block steps of one sequence (5 layers + lm_head) at the same dimensions and dtypes"
+            "sample": f"{steps} block steps of one sequence (5 layers + lm_head, block width {cfg.block}) at the same "
+                      f"dimensions and dtypes"
                       f"{', each after injecting %d positions' % inject_feats.shape[0] if inject_feats is not None else ''}, "
                       f"ring filled to n_past={n_past} with synthetic values (content does not change the cost); "
                       f"the rate is this workload's algorithmic bytes per step over the oracle's time per step"}
@@ -179,7 +182,7 @@ def main() -> int:
     from block_diffusion_drafter_02_amd import _lib, synth
     from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
 
-    wdt, rdt, fdt, B, T_inj = WORKLOADS[args.workload]
+    wdt, rdt, fdt, B, T_inj, g = WORKLOADS[args.workload]
     shape = synth.REAL
     t_setup = time.perf_counter()
     print(f"[bench] generating {args.workload} weights", file=sys.stderr, flush=True)
@@ -219,11 +222,12 @@ def main() -> int:
         pos_all = torch.from_numpy((starts[:, None] + np.arange(T_inj)[None]).astype(np.int32)).to(dr.device)
         np_all = torch.from_numpy((starts[1:, None]).astype(np.int32)).to(dr.device)
     ids_all = torch.from_numpy(synth.integers(0, "bench.id_last", (W + K, B), 0, shape.n_vocab)).to(dr.device)
-    tgt_all = torch.from_numpy(synth.integers(0, "bench.target", (W + K, B, 15), 0, shape.n_vocab)).to(dr.device)
+    dr.set_block_width(g)
+    tgt_all = torch.from_numpy(synth.integers(0, "bench.target", (W + K, B, g - 1), 0, shape.n_vocab)).to(dr.device)
     il = ids_all[0].clone()
     npst = torch.tensor(n_pasts, dtype=torch.int32, device=dr.device)
     logits = torch.empty((16 * B, shape.n_vocab), dtype=torch.float32, device=dr.device)
-    drafts = torch.empty((B, 15), dtype=torch.int32, device=dr.device)
+    drafts = torch.empty((B, g - 1), dtype=torch.int32, device=dr.device)
     target = tgt_all[0].clone()
     n_ok = torch.empty((B,), dtype=torch.int32, device=dr.device)
     stream = torch.cuda.Stream()
@@ -318,8 +322,9 @@ def main() -> int:
         "config": {
             "workload": f"DFlash drafter block step + acceptance, real dims (5 layers, n_embd 6656, heads 32/8, "
                         f"head_dim 128, n_ff 19968, window 2048, block 16, vocab 8192), {wdt} weights, {rdt} ring, "
-                        f"batch {B}, n_past {n_pasts}",
+                        f"batch {B}, n_past {n_pasts}" + (f", block width {g}" if g != 16 else ""),
             "batch": B,
+            "block_width": g,
             "path": "persistent" if dr.step_path(B) == _lib.PATH_PERSISTENT else "kernels",
             "algorithmic_bytes_per_step": total,
             "weight_bytes_per_step": nb["weights"],
@@ -353,7 +358,8 @@ def main() -> int:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(
             shape, raw, wdt, rdt, n_pasts[0], step_bytes(shape, wdt, rdt, n_vis[:1])["total"] + (ib["total"] if ib else 0),
-            inject_feats=synth.features(shape, T_inj, fdt, seed=0, tag="bench.inject0") if T_inj else None)
+            inject_feats=synth.features(shape, T_inj, fdt, seed=0, tag="bench.inject0") if T_inj else None,
+            block_width=g)
     else:
         line["cpu_baseline"] = None
     if args.calibrate_copy_mib:

@@ -65,6 +65,8 @@ SYMBOLS = {
     "dflash_replay_stage": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
     "dflash_quantize_fp8_rows": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dflash_set_path": (C.c_int, [C.c_void_p, C.c_int32]),
+    "dflash_set_block_width": (C.c_int, [C.c_void_p, C.c_int32]),
+    "dflash_block_width": (C.c_int32, [C.c_void_p]),
     "dflash_step_path": (C.c_int32, [C.c_void_p, C.c_int32]),
     "dflash_check_device": (C.c_int, [C.c_void_p, C.c_void_p]),
     "dflash_last_error": (C.c_char_p, []),

@@ -436,7 +436,7 @@ int prepare_chain(dflash_ctx &x, hipStream_t s) {
 // more slowly than the per-launch grids (the third workgroup of every CU lags,
 // and every phase waits for the slowest), so it stays an explicit choice.
 bool use_chain(const dflash_ctx &x, int B) {
-    if (B != 1 || x.pchain_wg < 1) return false;
+    if (B != 1 || x.pchain_wg < 1 || x.gamma != x.cfg.block) return false;
     return x.path == DFLASH_PATH_PERSISTENT;
 }
 
@@ -448,6 +448,7 @@ EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
     e.inv_E = 1.0f / (float)x.E;
     e.eps = x.cfg.rms_eps;
     e.block = x.cfg.block;
+    e.gamma = x.gamma;
     e.act_rows = x.Mmax;
     e.act_fmt = x.act_fmt;
     return e;
@@ -660,6 +661,7 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
     x->ws = (char *)workspace;
     x->ws_bytes = workspace_bytes;
     x->tok_embd = w->tok_embd;
+    x->gamma = x->cfg.block;
     hipError_t e = hipGetDevice(&x->device);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&x->cus, hipDeviceAttributeMultiprocessorCount, x->device);
     if (e != hipSuccess) {
@@ -777,7 +779,7 @@ int dflash_accept(dflash_ctx *x, const int32_t *drafts, const int32_t *target, i
                   void *stream) {
     if (!x || !drafts || !target || !n_ok) return fail(DFLASH_EINVAL, "a pointer is NULL");
     if (B < 1 || B > x->cfg.max_batch) return fail(DFLASH_ERANGE, "B=%d outside 1..max_batch=%d", B, x->cfg.max_batch);
-    HIP_TRY(launch_accept(drafts, target, B, x->cfg.block - 1, n_ok, (hipStream_t)stream), "accept launch");
+    HIP_TRY(launch_accept(drafts, target, B, x->gamma - 1, n_ok, (hipStream_t)stream), "accept launch");
     return DFLASH_OK;
 }
 
@@ -843,6 +845,14 @@ int dflash_replay_stage(dflash_ctx *x, int32_t stage, int32_t layer, void *strea
         default: return fail(DFLASH_EINVAL, "unknown stage %d", stage);
     }
 }
+
+int dflash_set_block_width(dflash_ctx *x, int32_t gamma) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    x->gamma = std::max(2, std::min((int)gamma, x->cfg.block));  // clamped into 2..block
+    return DFLASH_OK;
+}
+
+int32_t dflash_block_width(const dflash_ctx *x) { return x ? x->gamma : 0; }
 
 int dflash_set_path(dflash_ctx *x, int32_t path) {
     if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");

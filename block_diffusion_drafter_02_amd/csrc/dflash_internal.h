@@ -211,6 +211,7 @@ struct EpiArgs {
     int act_K;
     float *ss_out;        // [G][ss_stride] sums of squares of the updated x
     int block;  // rows per sequence
+    int gamma;  // block width in use: drafts and acceptance cover rows 1..gamma-1
     // EPI_LOGITS: argmax across groups
     float *am_val;
     int *am_idx;
@@ -291,6 +292,7 @@ struct dflash_ctx {
     int E, H, Hkv, D, F, W, L, V, C, qdim, kvdim, nqkv, Mmax, G_E;
     int act_fmt;       // activation format of the step GEMVs
     int last_B;        // batch of the last block step (0 before the first)
+    int gamma;         // block width of the steps (2..block; rows gamma.. of each sequence are padding)
     int cus;           // compute units of the device
     unsigned *pf_sink; // target of the prefetch workgroups' never-taken store
     size_t wbytes_el;  // bytes per streamed weight element (4, 2, 1)

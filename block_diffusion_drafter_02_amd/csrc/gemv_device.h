@@ -452,14 +452,14 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
             if (sub == 0 && m < M) {
                 best_s[m] = bi;
                 const int b = m / e.block, i = m % e.block;
-                if (i > 0) st_i32(e.drafts + (size_t)b * (e.block - 1) + i - 1, bi);
+                if (i > 0 && i < e.gamma) st_i32(e.drafts + (size_t)b * (e.gamma - 1) + i - 1, bi);
             }
         }
         __syncthreads();
         if (e.target != nullptr && tid < M / e.block) {
             const int b = tid;
             int n = 0;
-            while (n < e.block - 1 && best_s[b * e.block + 1 + n] == e.target[(size_t)b * (e.block - 1) + n]) ++n;
+            while (n < e.gamma - 1 && best_s[b * e.block + 1 + n] == e.target[(size_t)b * (e.gamma - 1) + n]) ++n;
             st_i32(e.n_ok + b, n);
         }
         if (tid == 0) __hip_atomic_store(e.am_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

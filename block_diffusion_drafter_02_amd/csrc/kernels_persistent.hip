@@ -193,6 +193,7 @@ __device__ __forceinline__ EpiArgs epi_base(const PStepArgs &a, int kind) {
     e.inv_E = a.inv_E;
     e.eps = a.eps;
     e.block = a.block;
+    e.gamma = a.block;  // the persistent chain runs full-width blocks only
     e.act_rows = a.act_rows;
     e.act_fmt = a.act_fmt;
     return e;

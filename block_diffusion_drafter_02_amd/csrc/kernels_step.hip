@@ -318,12 +318,14 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 // Operands are exact: fp32 values enter as three bf16 terms (a + b <= 2 cross
 // products, error ~2^-27 relative), bf16 ring keys and values as one term.
 // A ring key at slot s is visible to block row i when slot_pos[s] >= 0 and
-// 0 <= n_past + i - slot_pos[s] < W; block keys are always visible.
+// 0 <= n_past + i - slot_pos[s] < W; block keys 0..gamma-1 are always visible
+// (with a block width gamma < 16 the rows gamma..15 are padding).
 struct AttnArgs {
     const float *qkv;  // [M][nqkv]: the raw q/k/v projection of the block rows
     int nqkv, qdim, kvdim;
     void *const *rings;
     int layer, L, Hkv, W, ring_dtype, G, NCH, CH, block;
+    int gamma;     // block keys gamma..block-1 are padding, visible to no row
     int vt_elems;  // bf16 elements of the V^T region in LDS
     const int32_t *n_past;
     float *ml, *o;
@@ -617,6 +619,7 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 bool vis = kt < nkt;
+                if (vis && is_block) vis = 16 * (kt0 + kt) + 4 * grp + i < a.gamma;
                 if (vis && !is_block) {
                     const int kp = kpos[16 * (kt0 + kt) + 4 * grp + i];
                     const int dlt = qpos - kp;
@@ -831,6 +834,7 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.NCH = c->W / a.CH;
     a.vt_elems = attn_vt_elems(c->D, a.CH, c->cfg.ring_dtype);
     a.block = c->cfg.block;
+    a.gamma = c->gamma;
     a.n_past = n_past;
     a.ml = c->att_ml;
     a.o = c->att_o;

@@ -179,7 +179,7 @@ class Drafter:
     def _outputs(self, B):
         s = self.shape
         logits = torch.empty((s.block * B, s.n_vocab), dtype=torch.float32, device=self.device)
-        drafts = torch.empty((B, s.block - 1), dtype=torch.int32, device=self.device)
+        drafts = torch.empty((B, self.block_width() - 1), dtype=torch.int32, device=self.device)
         return logits, drafts
 
     def block_step(self, ring_table: torch.Tensor, id_last: torch.Tensor, n_past: torch.Tensor, out=None,
@@ -221,6 +221,14 @@ class Drafter:
             None if target is None else _dev(target, torch.int32, "target"),
             None if n_ok is None else _dev(n_ok, torch.int32, "n_ok"), s.cuda_stream, C.byref(h)))
         return StepGraph(h.value, [ring_table, id_last, n_past, logits, drafts, target, n_ok, self])
+
+    def set_block_width(self, g: int) -> int:
+        """Block width of later steps and graph captures (clamped into 2..block); returns the width in use."""
+        check(lib().dflash_set_block_width(self._ctx, g))
+        return self.block_width()
+
+    def block_width(self) -> int:
+        return int(lib().dflash_block_width(self._ctx))
 
     def set_path(self, path: int) -> None:
         """Route later block steps: _lib.PATH_AUTO, PATH_KERNELS or PATH_PERSISTENT."""

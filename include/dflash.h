@@ -153,12 +153,15 @@ int dflash_inject(dflash_ctx *ctx, void *ring, const float *h, const int32_t *po
 
 /* The drafter block step for B sequences (rows sequence-major, 16 per
  * sequence). rings: device array [B] of ring pointers; id_last [B] and
- * n_past [B] int32 (device, so a graph replays with fresh values). Block row
- * i of sequence b holds [id_last, mask...][i] at position n_past[b] + i and
- * attends non-causally to all 16 block rows and to the ring slots with
- * 0 <= n_past[b] + i - slot_pos < window. Outputs logits [16*B, n_vocab] f32
- * and drafts [B, 15] int32 = argmax of rows 1..15 (ties to the lowest
- * index). Ids outside [0, n_vocab) embed as zero vectors. 1 <= B <= max_batch. */
+ * n_past [B] int32 (device, so a graph replays with fresh values). With the
+ * block width g of dflash_set_block_width (16 unless set), block row i < g of
+ * sequence b holds [id_last, mask...][i] at position n_past[b] + i and
+ * attends non-causally to block rows 0..g-1 and to the ring slots with
+ * 0 <= n_past[b] + i - slot_pos < window; rows g..15 are padding that no row
+ * attends to. Outputs logits [16*B, n_vocab] f32 (rows g..15 of a sequence
+ * hold padding values) and drafts [B, g-1] int32 = argmax of rows 1..g-1
+ * (ties to the lowest index). Ids outside [0, n_vocab) embed as zero vectors.
+ * 1 <= B <= max_batch. */
 int dflash_block_step(dflash_ctx *ctx, void *const *rings, const int32_t *id_last, const int32_t *n_past, int32_t B,
                       float *logits, int32_t *drafts, void *stream);
 
@@ -169,7 +172,8 @@ int dflash_block_forward(dflash_ctx *ctx, void *const *rings, const int32_t *blo
 
 /* First-mismatch acceptance (dflash-ops card, Usage; dflash_engine.py page,
  * DFlashSpeculativeVerifier.verify_block): n_ok[b] = number of leading i with
- * drafts[b][i] == target[b][i], in 0..15. drafts, target [B, 15] int32. */
+ * drafts[b][i] == target[b][i], in 0..g-1 for the block width g in use.
+ * drafts, target [B, g-1] int32. */
 int dflash_accept(dflash_ctx *ctx, const int32_t *drafts, const int32_t *target, int32_t B, int32_t *n_ok,
                   void *stream);
 
@@ -209,6 +213,16 @@ typedef enum { DFLASH_PATH_AUTO = 0, DFLASH_PATH_KERNELS = 1, DFLASH_PATH_PERSIS
  * EUNSUPPORTED for DFLASH_PATH_PERSISTENT when the persistent kernel does not
  * fit this configuration or device. */
 int dflash_set_path(dflash_ctx *ctx, int32_t path);
+
+/* Block width g (metrale dflash_head.rs page, BlockDiffusionDraftHead,
+ * block_g / set_block_g and its per-width propose graphs): later block steps,
+ * acceptance scans and graph captures use g tokens [id_last, mask x (g-1)]
+ * and g-1 drafts. g is clamped into 2..block (16). A graph keeps the width it
+ * was captured with. The persistent path runs full-width blocks only; at
+ * g < 16 a step takes the per-launch kernels. dflash_block_width returns the
+ * width in use (0 for a NULL ctx). */
+int dflash_set_block_width(dflash_ctx *ctx, int32_t g);
+int32_t dflash_block_width(const dflash_ctx *ctx);
 
 /* The path (DFLASH_PATH_KERNELS or DFLASH_PATH_PERSISTENT) a block step of B
  * sequences takes now; -1 for a NULL ctx. */

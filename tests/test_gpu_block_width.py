@@ -1,0 +1,135 @@
+"""GPU parity of the variable block width g (metrale dflash_head.rs page, BlockDiffusionDraftHead,
+block_g / set_block_g, one propose graph per width).
+
+At width g the step drafts from the block [id_last, mask x (g-1)]: rows 0..g-1 of each sequence are
+checked against the oracle run with block = g (its block size is a plain parameter of every function),
+drafts and acceptance cover g-1 positions, and the padding rows g..15 must leave rows < g untouched.
+Bars as in test_gpu_parity.py."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from block_diffusion_drafter_02_amd import synth
+from oracle import dflash_oracle as O
+from tests import workload as WL
+from tests.test_gpu_parity import _build, _check_logits, _spec_id, _step
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+SPECS = [WL.Spec(synth.TINY, "f32", "f32", "f32"), WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16")]
+
+
+@pytest.mark.parametrize("g", [2, 5, 8, 16])
+@pytest.mark.parametrize("spec", SPECS, ids=_spec_id)
+def test_block_width_matches_oracle_of_that_width(gpu, spec, g):
+    torch = _torch()
+    n_ctx = spec.shape.window + 16
+    dr, ring, fdev, (ocfg, ow, oring), raw, feats = _build(spec, n_ctx)
+    assert dr.set_block_width(g) == g
+    print(f"[case] {_spec_id(spec)} g={g}", flush=True)
+    st = synth.step_inputs(spec.shape, 1, seed=11)
+    logits, drafts = _step(dr, [ring], st["id_last"], [n_ctx])
+    assert drafts.shape == (1, g - 1)
+    cfg_g = dataclasses.replace(ocfg, block=g)
+    ref = O.block_forward(cfg_g, ow, oring, O.block_ids(cfg_g, int(st["id_last"][0])), n_ctx)
+    assert ref.shape == (g, spec.shape.n_vocab)
+    tol = _check_logits(spec, ref, logits[:g], label=f"g={g}")
+    bad, ties = WL.compare_drafts(ref, drafts[0], tol)
+    assert not bad, f"draft mismatches at rows {bad} (near ties {ties})"
+    # acceptance over g-1 positions with a planted mismatch at every index 0..g-1 (g-1: none)
+    odr = O.greedy_drafts(ref)
+    for m in range(g):
+        tgt = synth.planted_targets(odr[None], np.array([m]), np.zeros((1, g - 1), np.int64), spec.shape.n_vocab)
+        n_ok = dr.accept(torch.from_numpy(drafts).to(dr.device), torch.from_numpy(tgt.astype(np.int32)).to(dr.device))
+        if not ties:
+            assert int(n_ok.cpu()[0]) == O.accept(odr, tgt[0]) == m, (g, m)
+    dr.set_block_width(16)
+
+
+def test_batch_at_width_4_matches_per_sequence_oracle(gpu):
+    """B = 3 ragged rings (partial, full, wrapped) at g = 4: the batched path (GEMM + row-tiled epilogue,
+    256-thread attention) with padding rows in every sequence."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
+
+    spec = WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16")
+    shape = spec.shape
+    raw = synth.weights(shape, "bf16", seed=0)
+    dr = Drafter(shape, raw, "bf16", "bf16", "bf16", max_batch=3, max_inject=128)
+    g = 4
+    dr.set_block_width(g)
+    n_pasts = [40, 256, 300]
+    rings, orings = [], []
+    for b, n in enumerate(n_pasts):
+        feats = synth.features(shape, n, "bf16", seed=0, tag=f"feats{b}")
+        pos = np.arange(n, dtype=np.int64)
+        r = dr.new_ring()
+        WL.gpu_inject(dr, r, to_device(feats, dr.device), pos, 128)
+        rings.append(r)
+        orings.append(WL.oracle_side(spec, raw, feats, pos, 128))
+    st = synth.step_inputs(shape, 3, seed=13)
+    print("[case] batch B=3 g=4 n_past=", n_pasts, flush=True)
+    logits, drafts = _step(dr, rings, st["id_last"], n_pasts)
+    assert drafts.shape == (3, g - 1)
+    for b, n in enumerate(n_pasts):
+        ocfg, ow, oring = orings[b]
+        cfg_g = dataclasses.replace(ocfg, block=g)
+        ref = O.block_forward(cfg_g, ow, oring, O.block_ids(cfg_g, int(st["id_last"][b])), n)
+        tol = _check_logits(spec, ref, logits[16 * b:16 * b + g], label=f"seq{b}")
+        bad, ties = WL.compare_drafts(ref, drafts[b], tol)
+        assert not bad, (b, bad, ties)
+    del torch
+
+
+def test_per_width_graphs_replay_their_own_width(gpu):
+    """Graphs captured at g = 4 and at g = 16 each replay bitwise like an eager step at their width, with
+    the ctx's width switched between the replays; set_block_width clamps into 2..16."""
+    torch = _torch()
+    spec = WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16")
+    dr, ring, fdev, _, raw, feats = _build(spec, 300)
+    table = dr.ring_table([ring])
+    il = torch.tensor([5], dtype=torch.int32, device=dr.device)
+    npst = torch.tensor([300], dtype=torch.int32, device=dr.device)
+    assert dr.set_block_width(1) == 2 and dr.set_block_width(99) == 16
+    stream = torch.cuda.Stream()
+    graphs, eager = {}, {}
+    for g in (4, 16):
+        dr.set_block_width(g)
+        e_logits, e_drafts = dr.block_step(table, il, npst)
+        torch.cuda.synchronize()
+        logits, drafts = torch.empty_like(e_logits), torch.empty_like(e_drafts)
+        graphs[g] = (dr.capture_step(table, il, npst, logits, drafts, stream=stream), logits, drafts)
+        eager[g] = (e_logits, e_drafts)
+    print("[case] graphs at widths 4 and 16", flush=True)
+    dr.set_block_width(8)  # neither width: a replay keeps its own
+    for rep in range(3):
+        for g in (4, 16):
+            gr, logits, drafts = graphs[g]
+            with torch.cuda.stream(stream):
+                gr.launch(stream)
+            stream.synchronize()
+            assert drafts.shape == (1, g - 1)
+            assert torch.equal(drafts, eager[g][1]), (g, rep)
+            assert torch.equal(logits[:g], eager[g][0][:g]), (g, rep)
+    for g in graphs:
+        graphs[g][0].close()
+    dr.set_block_width(16)
+
+
+def test_persistent_path_falls_back_below_full_width(gpu):
+    spec = WL.Spec(synth.TINY, "bf16", "bf16", "bf16")
+    dr, ring, fdev, _, raw, feats = _build(spec, 80)
+    dr.set_path(2)  # DFLASH_PATH_PERSISTENT
+    assert dr.step_path(1) == 2
+    dr.set_block_width(6)
+    assert dr.step_path(1) == 1  # the per-launch kernels
+    dr.set_block_width(16)
+    assert dr.step_path(1) == 2

@@ -783,6 +783,14 @@ int dflash_accept(dflash_ctx *x, const int32_t *drafts, const int32_t *target, i
     return DFLASH_OK;
 }
 
+int dflash_accept_bonus(dflash_ctx *x, const int32_t *drafts, const int32_t *target, int32_t B, int32_t *n_ok,
+                        int32_t *bonus, void *stream) {
+    if (!x || !drafts || !target || !n_ok || !bonus) return fail(DFLASH_EINVAL, "a pointer is NULL");
+    if (B < 1 || B > x->cfg.max_batch) return fail(DFLASH_ERANGE, "B=%d outside 1..max_batch=%d", B, x->cfg.max_batch);
+    HIP_TRY(launch_accept(drafts, target, B, x->gamma - 1, n_ok, (hipStream_t)stream, bonus), "accept launch");
+    return DFLASH_OK;
+}
+
 int dflash_step_graph_create(dflash_ctx *x, void *const *rings, const int32_t *id_last, const int32_t *n_past,
                              int32_t B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
                              void *stream, dflash_graph **out) {

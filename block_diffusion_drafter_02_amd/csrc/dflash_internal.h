@@ -451,7 +451,8 @@ inline int attn_chunk(int ring_dtype, int W, int B) {
     if (ring_dtype != DFLASH_BF16) return 32;
     return attn_threads(B) == 512 && W % 128 == 0 ? 128 : 64;
 }
-hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, int n, int32_t *n_ok, hipStream_t s);
+hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, int n, int32_t *n_ok, hipStream_t s,
+                         int32_t *bonus = nullptr);
 
 // ring layout helpers (host and device)
 __host__ __device__ inline size_t ring_kv_elems(int L, int Hkv, int W, int D) { return (size_t)L * Hkv * W * D; }

@@ -887,14 +887,23 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
 // Acceptance scan: one wavefront per sequence; lane i compares draft i with the
 // target token; the first set bit of the mismatch ballot is n_ok.
 // ---------------------------------------------------------------------------
-__global__ void accept_kernel(const int32_t *drafts, const int32_t *target, int n, int32_t *n_ok) {
+// target rows are ld_t long; with bonus, bonus[b] = target[b][n_ok[b]] (the
+// target's token at the first mismatch, or at position n after n matches).
+__global__ void accept_kernel(const int32_t *drafts, const int32_t *target, int n, int ld_t, int32_t *n_ok,
+                              int32_t *bonus) {
     const int b = blockIdx.x, lane = threadIdx.x;
-    const bool mis = lane < n && drafts[(size_t)b * n + lane] != target[(size_t)b * n + lane];
+    const bool mis = lane < n && drafts[(size_t)b * n + lane] != target[(size_t)b * ld_t + lane];
     const unsigned long long mask = __ballot(mis);
-    if (lane == 0) n_ok[b] = mask ? (__ffsll((long long)mask) - 1) : n;
+    const int k = mask ? (__ffsll((long long)mask) - 1) : n;
+    if (lane == 0) {
+        n_ok[b] = k;
+        if (bonus != nullptr) bonus[b] = target[(size_t)b * ld_t + k];
+    }
 }
 
-hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, int n, int32_t *n_ok, hipStream_t s) {
-    hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(64), 0, s, drafts, target, n, n_ok);
+hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, int n, int32_t *n_ok, hipStream_t s,
+                         int32_t *bonus) {
+    if (n < 0 || n > 63) return hipErrorInvalidValue;  // one wavefront compares the drafts
+    hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(64), 0, s, drafts, target, n, bonus ? n + 1 : n, n_ok, bonus);
     return hipGetLastError();
 }

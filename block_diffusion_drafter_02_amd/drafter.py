@@ -208,6 +208,16 @@ class Drafter:
                                   B, _dev(n_ok, torch.int32, "n_ok"), _stream(stream)))
         return n_ok
 
+    def accept_bonus(self, drafts: torch.Tensor, target: torch.Tensor, stream=None):
+        """(n_ok [B], bonus [B]): acceptance with the target's token at the first mismatch; target [B, g]."""
+        B = drafts.shape[0]
+        n_ok = torch.empty((B,), dtype=torch.int32, device=self.device)
+        bonus = torch.empty((B,), dtype=torch.int32, device=self.device)
+        check(lib().dflash_accept_bonus(self._ctx, _dev(drafts, torch.int32, "drafts"),
+                                        _dev(target, torch.int32, "target"), B, _dev(n_ok, torch.int32, "n_ok"),
+                                        _dev(bonus, torch.int32, "bonus"), _stream(stream)))
+        return n_ok, bonus
+
     def capture_step(self, ring_table, id_last, n_past, logits, drafts, target=None, n_ok=None,
                      stream=None) -> StepGraph:
         """Capture the block step (plus accept when target/n_ok are given) on a non-default stream."""

@@ -177,6 +177,16 @@ int dflash_block_forward(dflash_ctx *ctx, void *const *rings, const int32_t *blo
 int dflash_accept(dflash_ctx *ctx, const int32_t *drafts, const int32_t *target, int32_t B, int32_t *n_ok,
                   void *stream);
 
+/* Acceptance with the bonus token (dflash_engine.py page,
+ * DFlashSpeculativeVerifier.verify_block): target [B, g] int32 holds the
+ * target's tokens at the g-1 draft positions and at the position after them.
+ * n_ok[b] as dflash_accept; bonus[b] = target[b][n_ok[b]], the target's token
+ * at the first mismatch (or after the last draft when all match), so the
+ * accepted run is drafts[b][0..n_ok[b]) followed by bonus[b], tau = n_ok + 1
+ * tokens. drafts [B, g-1], n_ok and bonus [B] int32, all device. */
+int dflash_accept_bonus(dflash_ctx *ctx, const int32_t *drafts, const int32_t *target, int32_t B, int32_t *n_ok,
+                        int32_t *bonus, void *stream);
+
 /* Capture the block step (and, when target and n_ok are non-NULL, the
  * acceptance scan) for fixed pointers into a HIP graph by stream capture on
  * `stream`. Nothing is allocated inside the capture; every intermediate

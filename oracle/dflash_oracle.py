@@ -426,6 +426,55 @@ def greedy_drafts(logits: np.ndarray) -> np.ndarray:
     return np.argmax(np.asarray(logits)[1:], axis=-1).astype(np.int32)
 
 
+# --------------------------------------------------------------------------- sampling
+PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers of Philox-4x32
+PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # key increments (Weyl sequence) between rounds
+MASK32 = 0xFFFFFFFF
+
+
+def philox4x32_10(counter, key):
+    """Philox-4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as
+    1, 2, 3", SC 2011), elementwise over arrays: counter = (c0, c1, c2, c3), key = (k0, k1), each an
+    array (or scalar) of unsigned 32-bit values. Returns the four output words."""
+    c = [np.asarray(x, dtype=np.uint64) & MASK32 for x in counter]
+    k0 = np.asarray(key[0], dtype=np.uint64) & MASK32
+    k1 = np.asarray(key[1], dtype=np.uint64) & MASK32
+    for r in range(10):
+        if r > 0:
+            k0 = (k0 + PHILOX_W[0]) & MASK32
+            k1 = (k1 + PHILOX_W[1]) & MASK32
+        p0 = c[0] * np.uint64(PHILOX_M[0])  # exact: both factors < 2^32
+        p1 = c[2] * np.uint64(PHILOX_M[1])
+        hi0, lo0 = p0 >> np.uint64(32), p0 & MASK32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & MASK32
+        c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]
+    return [x.astype(np.uint32) for x in c]
+
+
+def gumbel_noise(seed: int, b: int, positions, n_vocab: int) -> np.ndarray:
+    """Gumbel(0, 1) noise [len(positions), n_vocab] for sequence b: u = (x0 >> 8) + 1/2 scaled by 2^-24,
+    x0 the first Philox output word at counter (position, vocab id, b, 0) under key (seed low, seed high),
+    and g = -log(-log(u)) in fp64. The 24-bit u is exact in fp32 and fp64 alike."""
+    pos = np.asarray(positions, dtype=np.uint64)[:, None]
+    n = np.arange(n_vocab, dtype=np.uint64)[None, :]
+    x0 = philox4x32_10((pos + 0 * n, n + 0 * pos, np.uint64(b), np.uint64(0)),
+                       (seed & MASK32, (seed >> 32) & MASK32))[0]
+    u = ((x0 >> np.uint32(8)).astype(F64) + 0.5) * 2.0 ** -24
+    return -np.log(-np.log(u))
+
+
+def sampled_drafts(logits: np.ndarray, temperature: float, seed: int, b: int, n_past: int) -> np.ndarray:
+    """Temperature sampling of the drafts (dflash_engine.py page, DFlashDraftModel.forward: a draw from
+    softmax(logits / T) at block positions 1..block-1), by the Gumbel-max rule: the draft at row i is
+    argmax over the vocabulary of logits[i] / T + g[i], g the Gumbel noise of position n_past + i
+    (ties to the lowest index). T = 0 is the greedy draft."""
+    logits = np.asarray(logits, dtype=F64)
+    if temperature == 0.0:
+        return greedy_drafts(logits)
+    g = gumbel_noise(seed, b, n_past + np.arange(1, logits.shape[0]), logits.shape[1])
+    return np.argmax(logits[1:] / temperature + g, axis=-1).astype(np.int32)
+
+
 def block_step(cfg: Config, w: Weights, ring: Ring, id_last: int, n_past: int):
     """(logits [block, V], drafts [block-1]) of one sequence."""
     logits = block_forward(cfg, w, ring, block_ids(cfg, id_last), n_past)
@@ -445,3 +494,17 @@ def accept(drafts, target) -> int:
             break
         n += 1
     return n
+
+
+def verify(drafts, target):
+    """Acceptance with the bonus token: (k_match, bonus, accepted tokens).
+
+    dflash_engine.py page, DFlashSpeculativeVerifier.verify_block: ``target``
+    holds the target's tokens (its argmax) at the len(drafts) draft positions
+    and at one more position; k_match drafts are accepted and the target's
+    token at index k_match is appended, so tau = k_match + 1 tokens.
+    """
+    assert len(target) == len(drafts) + 1
+    k = accept(drafts, target[:len(drafts)])
+    bonus = int(target[k])
+    return k, bonus, [int(d) for d in drafts[:k]] + [bonus]

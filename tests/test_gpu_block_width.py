@@ -133,3 +133,29 @@ def test_persistent_path_falls_back_below_full_width(gpu):
     assert dr.step_path(1) == 1  # the per-launch kernels
     dr.set_block_width(16)
     assert dr.step_path(1) == 2
+
+
+@pytest.mark.parametrize("g", [16, 5])
+def test_accept_with_bonus_matches_oracle_verify(gpu, g):
+    """dflash_accept_bonus against the oracle's verify_block (k_match, bonus token at index k_match) for
+    every planted mismatch index 0..g-1 (g-1: all drafts match, the bonus is the extra target position)."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter
+
+    spec = WL.Spec(synth.TINY, "f32", "f32", "f32")
+    dr = Drafter(spec.shape, synth.weights(spec.shape, "f32"), "f32", "f32", "f32", max_batch=8)
+    dr.set_block_width(g)
+    rng = np.random.default_rng(21 + g)
+    print(f"[case] accept_bonus g={g}", flush=True)
+    for trial in range(10):
+        d = rng.integers(0, 512, (8, g - 1)).astype(np.int32)
+        m = rng.integers(0, g, 8)
+        t = synth.planted_targets(d, m, rng.integers(0, 512, (8, g - 1)), 512)
+        t = np.concatenate([t, rng.integers(0, 512, (8, 1)).astype(np.int32)], axis=1)  # the bonus position
+        n_ok, bonus = dr.accept_bonus(torch.from_numpy(d).cuda(), torch.from_numpy(t).cuda())
+        n_ok, bonus = n_ok.cpu().numpy(), bonus.cpu().numpy()
+        for b in range(8):
+            k, bb, acc = O.verify(d[b], t[b])
+            assert (n_ok[b], bonus[b]) == (k, bb), (trial, b)
+        np.testing.assert_array_equal(n_ok, m)
+    dr.set_block_width(16)

@@ -464,6 +464,25 @@ def test_accept_worked_example_from_the_pages():
     assert t[n_ok] == ex["expected_bonus"]
 
 
+def test_verify_with_bonus_worked_example_from_the_pages():
+    """The page's invariant 4: three matching drafts, a mismatch at index 3 -> tau = 4, accepted[3] is the
+    mismatching target token; the fixture's target row gets one more (bonus) position appended."""
+    ex = json.load(open(os.path.join(GOLDEN, "accept_worked_example.json")))
+    d = np.array(ex["drafts"])
+    t = np.array(ex["target"] + [77])
+    k, bonus, acc = O.verify(d, t)
+    assert k == ex["expected_n_ok"] and len(acc) == ex["expected_tau"] and acc[-1] == bonus == ex["expected_bonus"]
+    assert acc[:k] == list(d[:k])
+
+
+def test_verify_full_match_takes_the_bonus_after_the_last_draft():
+    d = np.array([4, 4, 9, 1])
+    k, bonus, acc = O.verify(d, np.array([4, 4, 9, 1, 23]))
+    assert (k, bonus, acc) == (4, 23, [4, 4, 9, 1, 23])
+    k, bonus, acc = O.verify(d, np.array([5, 4, 9, 1, 23]))
+    assert (k, bonus, acc) == (0, 5, [5])
+
+
 def test_planted_targets_round_trip_through_accept():
     st = synth.step_inputs(synth.TINY, 64, seed=5)
     drafts = synth.integers(5, "drafts", (64, 15), 0, 512)
@@ -486,3 +505,38 @@ def test_per_head_qk_norm_makes_step_invariant_to_projection_scale():
     np.testing.assert_allclose(O.block_forward(cfg, w, ring2, ids, 80), base, rtol=0, atol=2e-5)
     raw["layers"][0]["q_norm"] = raw["layers"][0]["q_norm"] * np.float32(1.5)
     assert np.abs(O.block_forward(cfg, w, ring2, ids, 80) - base).max() > 1e-3
+
+
+# --------------------------------------------------------------------------- sampling
+def test_philox_known_answer_vectors():
+    kat = json.load(open(os.path.join(GOLDEN, "philox4x32_10_kat.json")))
+    for v in kat["vectors"]:
+        ctr = [int(x, 16) for x in v["counter"]]
+        key = [int(x, 16) for x in v["key"]]
+        out = [int(x) for x in O.philox4x32_10(ctr, key)]
+        assert out == [int(x, 16) for x in v["output"]]
+
+
+def test_gumbel_max_draws_follow_softmax_over_temperature():
+    """The sampling law: over many positions, the Gumbel-max draft frequencies match softmax(logits / T)
+    (each within 5 standard deviations of the binomial count)."""
+    logits = np.array([0.0, 1.0, -0.5, 2.0, 0.3, 1.7])
+    n = 20000
+    for T in (0.5, 1.0, 2.0):
+        p = np.exp(logits / T - (logits / T).max())
+        p /= p.sum()
+        g = O.gumbel_noise(seed=0x1234ABCD5678, b=0, positions=np.arange(n), n_vocab=len(logits))
+        draws = np.argmax(logits[None] / T + g, axis=1)
+        counts = np.bincount(draws, minlength=len(logits))
+        sd = np.sqrt(n * p * (1 - p))
+        assert np.all(np.abs(counts - n * p) <= 5 * sd + 1), (T, counts, n * p)
+
+
+def test_sampling_at_vanishing_temperature_is_greedy_and_zero_is_greedy():
+    rng = np.random.default_rng(2)
+    logits = rng.standard_normal((16, 64))
+    greedy = O.greedy_drafts(logits)
+    assert np.array_equal(O.sampled_drafts(logits, 0.0, 7, 0, 100), greedy)
+    assert np.array_equal(O.sampled_drafts(logits, 1e-9, 7, 0, 100), greedy)
+    # and a real temperature moves some drafts (the noise is not constant)
+    assert not np.array_equal(O.sampled_drafts(logits, 5.0, 7, 0, 100), greedy)

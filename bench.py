@@ -35,12 +35,14 @@ KERNEL_SRC = [os.path.join(ROOT, "block_diffusion_drafter_02_amd", "csrc", f)
               for f in ("kernels_weights.hip", "gemv_device.h", "dflash_internal.h")]
 
 WORKLOADS = {
-    # name: (weight dtype, ring dtype, feature dtype, batch, positions injected before every step, block width)
-    "bf16": ("bf16", "bf16", "bf16", 1, 0, 16),
-    "f32": ("f32", "f32", "f32", 1, 0, 16),
-    "bf16-batch8": ("bf16", "bf16", "bf16", 8, 0, 16),
-    "fp8-inject512": ("fp8", "bf16", "bf16", 1, 512, 16),
-    "bf16-g4": ("bf16", "bf16", "bf16", 1, 0, 4),
+    # name: (weight dtype, ring dtype, feature dtype, batch, positions injected before every step, block width,
+    #        draft sampling temperature)
+    "bf16": ("bf16", "bf16", "bf16", 1, 0, 16, 0.0),
+    "f32": ("f32", "f32", "f32", 1, 0, 16, 0.0),
+    "bf16-batch8": ("bf16", "bf16", "bf16", 8, 0, 16, 0.0),
+    "fp8-inject512": ("fp8", "bf16", "bf16", 1, 512, 16, 0.0),
+    "bf16-g4": ("bf16", "bf16", "bf16", 1, 0, 4, 0.0),
+    "bf16-sample": ("bf16", "bf16", "bf16", 1, 0, 16, 1.0),
 }
 FEATURE_POOL = 4  # distinct resident feature blocks cycled by the per-step inject (content does not change cost)
 
@@ -182,7 +184,7 @@ def main() -> int:
     from block_diffusion_drafter_02_amd import _lib, synth
     from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
 
-    wdt, rdt, fdt, B, T_inj, g = WORKLOADS[args.workload]
+    wdt, rdt, fdt, B, T_inj, g, temp = WORKLOADS[args.workload]
     shape = synth.REAL
     t_setup = time.perf_counter()
     print(f"[bench] generating {args.workload} weights", file=sys.stderr, flush=True)
@@ -223,6 +225,7 @@ def main() -> int:
         np_all = torch.from_numpy((starts[1:, None]).astype(np.int32)).to(dr.device)
     ids_all = torch.from_numpy(synth.integers(0, "bench.id_last", (W + K, B), 0, shape.n_vocab)).to(dr.device)
     dr.set_block_width(g)
+    dr.set_sampling(temp, 0x5EED)
     tgt_all = torch.from_numpy(synth.integers(0, "bench.target", (W + K, B, g - 1), 0, shape.n_vocab)).to(dr.device)
     il = ids_all[0].clone()
     npst = torch.tensor(n_pasts, dtype=torch.int32, device=dr.device)
@@ -322,9 +325,11 @@ def main() -> int:
         "config": {
             "workload": f"DFlash drafter block step + acceptance, real dims (5 layers, n_embd 6656, heads 32/8, "
                         f"head_dim 128, n_ff 19968, window 2048, block 16, vocab 8192), {wdt} weights, {rdt} ring, "
-                        f"batch {B}, n_past {n_pasts}" + (f", block width {g}" if g != 16 else ""),
+                        f"batch {B}, n_past {n_pasts}" + (f", block width {g}" if g != 16 else "")
+                        + (f", drafts sampled at temperature {temp}" if temp > 0 else ""),
             "batch": B,
             "block_width": g,
+            "temperature": temp,
             "path": "persistent" if dr.step_path(B) == _lib.PATH_PERSISTENT else "kernels",
             "algorithmic_bytes_per_step": total,
             "weight_bytes_per_step": nb["weights"],

@@ -436,7 +436,7 @@ int prepare_chain(dflash_ctx &x, hipStream_t s) {
 // more slowly than the per-launch grids (the third workgroup of every CU lags,
 // and every phase waits for the slowest), so it stays an explicit choice.
 bool use_chain(const dflash_ctx &x, int B) {
-    if (B != 1 || x.pchain_wg < 1 || x.gamma != x.cfg.block) return false;
+    if (B != 1 || x.pchain_wg < 1 || x.gamma != x.cfg.block || x.temp > 0.0f) return false;
     return x.path == DFLASH_PATH_PERSISTENT;
 }
 
@@ -449,6 +449,9 @@ EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
     e.eps = x.cfg.rms_eps;
     e.block = x.cfg.block;
     e.gamma = x.gamma;
+    e.temp = x.temp;
+    e.seed_lo = (uint32_t)x.seed;
+    e.seed_hi = (uint32_t)(x.seed >> 32);
     e.act_rows = x.Mmax;
     e.act_fmt = x.act_fmt;
     return e;
@@ -567,7 +570,7 @@ int stage_down(const dflash_ctx &x, int l, int M, hipStream_t s) {
 }
 
 int stage_lm(const dflash_ctx &x, int M, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
-             hipStream_t s) {
+             const int32_t *n_past, hipStream_t s) {
     EpiArgs e = epi_base(x, EPI_LOGITS, M);
     e.wscale = x.s_lm;
     e.ss = x.ss_a;
@@ -580,6 +583,7 @@ int stage_lm(const dflash_ctx &x, int M, float *logits, int32_t *drafts, const i
     e.drafts = drafts;
     e.target = target;
     e.n_ok = n_ok;
+    e.n_past = n_past;  // positions of the sampling noise
     return gemv(x, x.lm, x.V, x.E, x.act_a, e, s);
 }
 
@@ -609,7 +613,7 @@ int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const in
         TRY(stage_gu(x, l, M, s));
         TRY(stage_down(x, l, M, s));
     }
-    TRY(stage_lm(x, M, logits, drafts, target, n_ok, s));
+    TRY(stage_lm(x, M, logits, drafts, target, n_ok, n_past, s));
     x.last_B = B;
     return DFLASH_OK;
 }
@@ -662,6 +666,8 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
     x->ws_bytes = workspace_bytes;
     x->tok_embd = w->tok_embd;
     x->gamma = x->cfg.block;
+    x->temp = 0.0f;
+    x->seed = 0;
     hipError_t e = hipGetDevice(&x->device);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&x->cus, hipDeviceAttributeMultiprocessorCount, x->device);
     if (e != hipSuccess) {
@@ -861,6 +867,15 @@ int dflash_set_block_width(dflash_ctx *x, int32_t gamma) {
 }
 
 int32_t dflash_block_width(const dflash_ctx *x) { return x ? x->gamma : 0; }
+
+int dflash_set_sampling(dflash_ctx *x, float temperature, uint64_t seed) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    if (!(temperature >= 0.0f) || !isfinite(temperature))
+        return fail(DFLASH_EINVAL, "temperature must be finite and >= 0");
+    x->temp = temperature;
+    x->seed = seed;
+    return DFLASH_OK;
+}
 
 int dflash_set_path(dflash_ctx *x, int32_t path) {
     if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");

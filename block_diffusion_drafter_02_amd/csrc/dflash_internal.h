@@ -216,9 +216,14 @@ struct EpiArgs {
     float *am_val;
     int *am_idx;
     int *am_counter;
-    int32_t *drafts;      // [B][block-1]
-    const int32_t *target;  // [B][block-1] or null
+    int32_t *drafts;      // [B][gamma-1]
+    const int32_t *target;  // [B][gamma-1] or null
     int32_t *n_ok;        // [B] or null
+    // temperature sampling of the drafts (temp > 0): argmax of logit / temp +
+    // Gumbel noise of (position n_past[b] + i, vocab id, b) under the seed
+    float temp;
+    uint32_t seed_lo, seed_hi;
+    const int32_t *n_past;
 };
 
 // Bytes that a later launch reads, to be read now by otherwise idle compute
@@ -293,6 +298,8 @@ struct dflash_ctx {
     int act_fmt;       // activation format of the step GEMVs
     int last_B;        // batch of the last block step (0 before the first)
     int gamma;         // block width of the steps (2..block; rows gamma.. of each sequence are padding)
+    float temp;        // draft sampling temperature (0: greedy)
+    uint64_t seed;     // key of the sampling noise
     int cus;           // compute units of the device
     unsigned *pf_sink; // target of the prefetch workgroups' never-taken store
     size_t wbytes_el;  // bytes per streamed weight element (4, 2, 1)

@@ -255,6 +255,37 @@ __device__ __forceinline__ bool splitk_last(float *tile, float *mine, const floa
 }
 
 // ---------------------------------------------------------------------------
+// Sampling noise: Philox-4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw,
+// SC 2011) -- its first output word at counter (c0, c1, c2, c3) under key
+// (k0, k1) -- and the Gumbel(0, 1) value of that word: u = ((x >> 8) + 1/2)
+// 2^-24, exact in fp32, and -log(-log(u)).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t philox4x32_10_x0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                     uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+        const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    return c0;
+}
+
+__device__ __forceinline__ float gumbel_noise(uint32_t seed_lo, uint32_t seed_hi, int b, int pos, int n) {
+    const uint32_t x = philox4x32_10_x0((uint32_t)pos, (uint32_t)n, (uint32_t)b, 0u, seed_lo, seed_hi);
+    const float u = ((float)(x >> 8) + 0.5f) * 0x1p-24f;
+    return -logf(-logf(u));
+}
+
+// ---------------------------------------------------------------------------
 // Fused epilogues on the finished [16*MT][64*WN] tile of column group g
 // ---------------------------------------------------------------------------
 // All outputs are written with device-coherent stores, so a consumer in the
@@ -401,6 +432,10 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                 v = tile[m * GN + lane] * rs_s[m];
                 if (e.wscale) v *= sc;
                 st_f32(e.out + (size_t)m * e.ld_out + n, v);
+                if (e.temp > 0.0f) {  // the draft is a sample: the argmax runs on logit / T + Gumbel noise
+                    const int b = m / e.block;
+                    v = v / e.temp + gumbel_noise(e.seed_lo, e.seed_hi, b, e.n_past[b] + m % e.block, n);
+                }
             }
             float bv = v;
             int bi = n;

@@ -240,6 +240,10 @@ class Drafter:
     def block_width(self) -> int:
         return int(lib().dflash_block_width(self._ctx))
 
+    def set_sampling(self, temperature: float, seed: int = 0) -> None:
+        """Draft sampling of later steps: greedy at 0, else Gumbel-max draws from softmax(logits / T)."""
+        check(lib().dflash_set_sampling(self._ctx, float(temperature), int(seed)))
+
     def set_path(self, path: int) -> None:
         """Route later block steps: _lib.PATH_AUTO, PATH_KERNELS or PATH_PERSISTENT."""
         check(lib().dflash_set_path(self._ctx, path))

@@ -234,6 +234,17 @@ int dflash_set_path(dflash_ctx *ctx, int32_t path);
 int dflash_set_block_width(dflash_ctx *ctx, int32_t g);
 int32_t dflash_block_width(const dflash_ctx *ctx);
 
+/* Draft sampling (dflash_engine.py page, DFlashDraftModel.forward: greedy at
+ * temperature 0, otherwise a draw from softmax(logits / T)): later block steps
+ * and graph captures take draft i of sequence b as the argmax over the
+ * vocabulary of logits[i] / T + G, with G = -log(-log(u)) Gumbel noise and
+ * u = ((x >> 8) + 1/2) * 2^-24, x the first output word of Philox-4x32-10
+ * (Salmon et al., SC 2011) at counter (n_past[b] + i, vocab id, b, 0) under key
+ * (seed & 0xffffffff, seed >> 32); ties to the lowest index. The logits output
+ * stays the unperturbed logits. temperature must be finite and >= 0 (0:
+ * greedy), else DFLASH_EINVAL. Sampling steps take the per-launch kernels. */
+int dflash_set_sampling(dflash_ctx *ctx, float temperature, uint64_t seed);
+
 /* The path (DFLASH_PATH_KERNELS or DFLASH_PATH_PERSISTENT) a block step of B
  * sequences takes now; -1 for a NULL ctx. */
 int32_t dflash_step_path(const dflash_ctx *ctx, int32_t B);

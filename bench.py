@@ -43,7 +43,9 @@ WORKLOADS = {
     "fp8-inject512": ("fp8", "bf16", "bf16", 1, 512, 16, 0.0),
     "bf16-g4": ("bf16", "bf16", "bf16", 1, 0, 4, 0.0),
     "bf16-sample": ("bf16", "bf16", "bf16", 1, 0, 16, 1.0),
+    "bf16-paged": ("bf16", "bf16", "bf16", 1, 0, 16, 0.0),
 }
+PAGED = {"bf16-paged"}  # rings live in 128-slot pages of one pool, named by shuffled block tables
 FEATURE_POOL = 4  # distinct resident feature blocks cycled by the per-step inject (content does not change cost)
 
 
@@ -197,8 +199,13 @@ def main() -> int:
     dr.set_path({"auto": _lib.PATH_AUTO, "kernels": _lib.PATH_KERNELS, "persistent": _lib.PATH_PERSISTENT}[args.path])
     print("[bench] injecting context", file=sys.stderr, flush=True)
     rings = []
+    paged = args.workload in PAGED
+    if paged:
+        n_tab = shape.window // dr.PAGE_SLOTS
+        pool = dr.new_pool(n_tab * B)
+        page_ids = np.random.default_rng(0).permutation(n_tab * B).astype(np.int32)
     for b, n in enumerate(n_pasts):
-        ring = dr.new_ring()
+        ring = (torch.from_numpy(page_ids[b * n_tab:(b + 1) * n_tab]).to(dr.device) if paged else dr.new_ring())
         first = max(0, n - (n // shape.window + 1) * shape.window) if wdt == "f32" else max(0, n - shape.window)
         pos = np.arange(first, n, dtype=np.int32)
         feats = to_device(synth.features(shape, len(pos), fdt, seed=0, tag=f"bench.feats{b}"), dr.device)
@@ -326,10 +333,12 @@ def main() -> int:
             "workload": f"DFlash drafter block step + acceptance, real dims (5 layers, n_embd 6656, heads 32/8, "
                         f"head_dim 128, n_ff 19968, window 2048, block 16, vocab 8192), {wdt} weights, {rdt} ring, "
                         f"batch {B}, n_past {n_pasts}" + (f", block width {g}" if g != 16 else "")
-                        + (f", drafts sampled at temperature {temp}" if temp > 0 else ""),
+                        + (f", drafts sampled at temperature {temp}" if temp > 0 else "")
+                        + (", paged KV (128-slot pages, shuffled block tables)" if paged else ""),
             "batch": B,
             "block_width": g,
             "temperature": temp,
+            "paged_kv": paged,
             "path": "persistent" if dr.step_path(B) == _lib.PATH_PERSISTENT else "kernels",
             "algorithmic_bytes_per_step": total,
             "weight_bytes_per_step": nb["weights"],

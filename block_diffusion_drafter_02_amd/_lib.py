@@ -70,6 +70,9 @@ SYMBOLS = {
     "dflash_set_block_width": (C.c_int, [C.c_void_p, C.c_int32]),
     "dflash_block_width": (C.c_int32, [C.c_void_p]),
     "dflash_set_sampling": (C.c_int, [C.c_void_p, C.c_float, C.c_uint64]),
+    "dflash_page_bytes": (C.c_size_t, [C.c_void_p]),
+    "dflash_set_paged_pool": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
+    "dflash_pages_reset": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
     "dflash_step_path": (C.c_int32, [C.c_void_p, C.c_int32]),
     "dflash_check_device": (C.c_int, [C.c_void_p, C.c_void_p]),
     "dflash_last_error": (C.c_char_p, []),

@@ -266,11 +266,13 @@ void derive(dflash_ctx &x) {
     x.wbytes_el = dtype_bytes(c.weight_dtype);
 }
 
-size_t ring_bytes_of(const dflash_config &c) {
+// bytes of a ring of `window` slots (a page is one with PAGE_SLOTS)
+size_t ring_bytes_w(const dflash_config &c, int window) {
     const int es = dtype_bytes(c.ring_dtype);
-    const size_t kv = a256((size_t)c.n_layer * c.n_head_kv * c.window * c.head_dim * es);
-    return 2 * kv + a256(4ull * c.window);
+    const size_t kv = a256((size_t)c.n_layer * c.n_head_kv * window * c.head_dim * es);
+    return 2 * kv + a256(4ull * window);
 }
+size_t ring_bytes_of(const dflash_config &c) { return ring_bytes_w(c, c.window); }
 
 int tile_matrix(const void *src, int rows, int K, int es, void *dst, int row_map, int row0, int half, hipStream_t s,
                 int tpg = TILES_PER_GROUP) {
@@ -666,6 +668,7 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
     x->ws_bytes = workspace_bytes;
     x->tok_embd = w->tok_embd;
     x->gamma = x->cfg.block;
+    x->paged = PagedPool{nullptr, 0, 0};
     x->temp = 0.0f;
     x->seed = 0;
     hipError_t e = hipGetDevice(&x->device);
@@ -691,15 +694,49 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
 
 void dflash_destroy(dflash_ctx *ctx) { delete ctx; }
 
+// Empty a ring of `window` slots: K and V are zeroed too, since attention
+// weights a masked slot's value by an exact 0, which only stays 0 when the
+// value is finite.
+int reset_ring_w(const dflash_ctx &x, char *ring, int window, hipStream_t s) {
+    const int es = dtype_bytes(x.cfg.ring_dtype);
+    const size_t kv = a256((size_t)x.L * x.Hkv * window * x.D * es);
+    HIP_TRY(launch_fill_i32((int32_t *)ring, 0, 2 * kv / 4, s), "ring reset launch");
+    HIP_TRY(launch_fill_i32((int32_t *)(ring + 2 * kv), -1, window, s), "ring reset launch");
+    return DFLASH_OK;
+}
+
 int dflash_ring_reset(dflash_ctx *x, void *ring, void *stream) {
     if (!x || !ring) return fail(DFLASH_EINVAL, "ctx or ring is NULL");
+    if (x->paged.pool) return fail(DFLASH_ESTATE, "paged mode: reset pages with dflash_pages_reset");
     if ((uintptr_t)ring % 256) return fail(DFLASH_EINVAL, "ring must be 256-byte aligned");
-    const int es = dtype_bytes(x->cfg.ring_dtype);
-    const size_t kv = a256((size_t)x->L * x->Hkv * x->W * x->D * es);
-    // K and V are zeroed too: attention weights a masked slot's value by an exact 0, which only
-    // stays 0 when the value is finite
-    HIP_TRY(launch_fill_i32((int32_t *)ring, 0, 2 * kv / 4, (hipStream_t)stream), "ring reset launch");
-    HIP_TRY(launch_fill_i32((int32_t *)((char *)ring + 2 * kv), -1, x->W, (hipStream_t)stream), "ring reset launch");
+    return reset_ring_w(*x, (char *)ring, x->W, (hipStream_t)stream);
+}
+
+size_t dflash_page_bytes(const dflash_config *cfg) {
+    if (check_config(cfg) != DFLASH_OK || cfg->window % PAGE_SLOTS) return 0;
+    return ring_bytes_w(*cfg, PAGE_SLOTS);
+}
+
+int dflash_set_paged_pool(dflash_ctx *x, void *pool, int32_t n_pages) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    if (pool == nullptr) {
+        x->paged = PagedPool{nullptr, 0, 0};
+        return DFLASH_OK;
+    }
+    if (x->W % PAGE_SLOTS) return fail(DFLASH_EUNSUPPORTED, "paged KV needs a window that is a multiple of %d", PAGE_SLOTS);
+    if ((uintptr_t)pool % 256) return fail(DFLASH_EINVAL, "pool must be 256-byte aligned");
+    if (n_pages < 1) return fail(DFLASH_ERANGE, "n_pages=%d must be >= 1", n_pages);
+    x->paged = PagedPool{(char *)pool, n_pages, ring_bytes_w(x->cfg, PAGE_SLOTS)};
+    return DFLASH_OK;
+}
+
+int dflash_pages_reset(dflash_ctx *x, int32_t first, int32_t count, void *stream) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    if (!x->paged.pool) return fail(DFLASH_ESTATE, "no page pool is set");
+    if (first < 0 || count < 0 || first + count > x->paged.n_pages)
+        return fail(DFLASH_ERANGE, "pages [%d, %d) outside 0..%d", first, first + count, x->paged.n_pages);
+    for (int p = first; p < first + count; ++p)
+        TRY(reset_ring_w(*x, x->paged.pool + (size_t)p * x->paged.page_bytes, PAGE_SLOTS, (hipStream_t)stream));
     return DFLASH_OK;
 }
 
@@ -743,7 +780,8 @@ int dflash_encode(dflash_ctx *x, const void *feats, int32_t T, float *h, void *s
 
 int dflash_inject(dflash_ctx *x, void *ring, const float *h, const int32_t *pos, int32_t T, void *stream) {
     if (!x || !ring || !h || !pos) return fail(DFLASH_EINVAL, "ctx, ring, h or pos is NULL");
-    if ((uintptr_t)ring % 256) return fail(DFLASH_EINVAL, "ring must be 256-byte aligned");
+    if ((uintptr_t)ring % (x->paged.pool ? 4 : 256))
+        return fail(DFLASH_EINVAL, x->paged.pool ? "block table must be 4-byte aligned" : "ring must be 256-byte aligned");
     if (T < 1 || T > x->W || T > x->cfg.max_inject)
         return fail(DFLASH_ERANGE, "T=%d outside 1..min(window=%d, max_inject=%d)", T, x->W, x->cfg.max_inject);
     hipStream_t s = (hipStream_t)stream;

@@ -291,6 +291,17 @@ struct LayerBufs {
 
 struct PStepArgs;  // persistent chain arguments (below)
 
+// Paged drafter KV: a page holds PAGE_SLOTS ring slots of every layer in the
+// ring layout (K, V, slot_pos); a sequence's ring is then a block table of
+// W / PAGE_SLOTS int32 page ids into one pool, shared by all layers. Attention
+// chunks (at most 128 slots, dividing 128) never straddle a page.
+constexpr int PAGE_SLOTS = 128;
+struct PagedPool {
+    char *pool;  // null: rings are contiguous
+    int n_pages;
+    size_t page_bytes;
+};
+
 struct dflash_ctx {
     dflash_config cfg;
     int device;
@@ -298,6 +309,7 @@ struct dflash_ctx {
     int act_fmt;       // activation format of the step GEMVs
     int last_B;        // batch of the last block step (0 before the first)
     int gamma;         // block width of the steps (2..block; rows gamma.. of each sequence are padding)
+    PagedPool paged;   // paged drafter KV (pool null: contiguous rings)
     float temp;        // draft sampling temperature (0: greedy)
     uint64_t seed;     // key of the sampling noise
     int cus;           // compute units of the device
@@ -469,6 +481,19 @@ __host__ __device__ inline size_t ring_v_offset(int L, int Hkv, int W, int D, in
 }
 __host__ __device__ inline size_t ring_pos_offset(int L, int Hkv, int W, int D, int es) {
     return ring_v_offset(L, Hkv, W, D, es) + align256(ring_kv_elems(L, Hkv, W, D) * es);
+}
+
+struct RingLoc {
+    char *base;  // ring or page holding the slot
+    int slot;    // slot within it
+    int W;       // its window
+    bool ok;     // false for a page id outside 0..n_pages-1 (the slot then reads as empty, writes are dropped)
+};
+__device__ __forceinline__ RingLoc ring_locate(const void *ring_or_table, const PagedPool &pp, int W, int slot) {
+    if (pp.pool == nullptr) return RingLoc{(char *)ring_or_table, slot, W, true};
+    const int pg = ((const int32_t *)ring_or_table)[slot / PAGE_SLOTS];
+    const bool ok = pg >= 0 && pg < pp.n_pages;
+    return RingLoc{pp.pool + (size_t)(ok ? pg : 0) * pp.page_bytes, slot % PAGE_SLOTS, PAGE_SLOTS, ok};
 }
 
 // Memory-side cache prefetch of the attention launch

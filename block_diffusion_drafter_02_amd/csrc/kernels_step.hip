@@ -155,12 +155,14 @@ __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ k
                                                      const int32_t *__restrict__ pos,
                                                      const double *__restrict__ inv_freq,
                                                      const float *__restrict__ k_norm_all, float eps, void *ring,
-                                                     int ring_dtype) {
+                                                     int ring_dtype, PagedPool pp) {
     const int t = blockIdx.x, l = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = pos[t];
     if (p < 0) return;
-    const int slot = p % W;
+    const RingLoc loc = ring_locate(ring, pp, W, p % W);
+    if (!loc.ok) return;  // a page id outside the pool: the write is dropped
+    const int slot = loc.slot;
     __shared__ float cs[D];
     for (int f = tid; f < D / 2; f += 256) {
         double sn, cn;
@@ -173,9 +175,9 @@ __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ k
     const size_t kvdim = (size_t)Hkv * D;
     const float *row = kv + (size_t)t * L * 2 * kvdim + (size_t)l * 2 * kvdim;
     const size_t split = (size_t)T * L * 2 * kvdim;  // floats between partials
-    char *rb = (char *)ring;
+    char *rb = loc.base;
     void *Kb = rb;
-    void *Vb = rb + ring_v_offset(L, Hkv, W, D, es);
+    void *Vb = rb + ring_v_offset(L, Hkv, loc.W, D, es);
     const float *kn = k_norm_all + (size_t)l * D;
     for (int j = wave; j < Hkv; j += 4) {
         float x[D / 64], v[D / 64];
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ k
             }
         }
         head_norm_rope<D>(x, kn, cs, eps, lane);
-        const size_t base = (((size_t)l * Hkv + j) * W + slot) * D;
+        const size_t base = (((size_t)l * Hkv + j) * loc.W + slot) * D;
 #pragma unroll
         for (int e = 0; e < D / 64; ++e) {
             ring_store(Kb, ring_dtype, base + lane + 64 * e, x[e]);
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ k
         }
     }
     if (l == 0 && tid == 0) {
-        int32_t *sp = (int32_t *)(rb + ring_pos_offset(L, Hkv, W, D, es));
+        int32_t *sp = (int32_t *)(rb + ring_pos_offset(L, Hkv, loc.W, D, es));
         sp[slot] = p;
     }
 }
@@ -207,10 +209,10 @@ hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, in
     const float eps = c->cfg.rms_eps;
     if (c->D == 128)
         hipLaunchKernelGGL(inject_kernel<128>, grid, dim3(256), 0, s, c->inj_kv, S, T, c->L, c->Hkv, c->W, pos, c->inv_freq,
-                           c->k_norm, eps, ring, c->cfg.ring_dtype);
+                           c->k_norm, eps, ring, c->cfg.ring_dtype, c->paged);
     else if (c->D == 64)
         hipLaunchKernelGGL(inject_kernel<64>, grid, dim3(256), 0, s, c->inj_kv, S, T, c->L, c->Hkv, c->W, pos, c->inv_freq,
-                           c->k_norm, eps, ring, c->cfg.ring_dtype);
+                           c->k_norm, eps, ring, c->cfg.ring_dtype, c->paged);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
@@ -323,7 +325,8 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
 struct AttnArgs {
     const float *qkv;  // [M][nqkv]: the raw q/k/v projection of the block rows
     int nqkv, qdim, kvdim;
-    void *const *rings;
+    void *const *rings;  // rings, or block tables when paged.pool is set
+    PagedPool paged;
     int layer, L, Hkv, W, ring_dtype, G, NCH, CH, block;
     int gamma;     // block keys gamma..block-1 are padding, visible to no row
     int vt_elems;  // bf16 elements of the V^T region in LDS
@@ -452,12 +455,14 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
     float *csh = wsh + 2 * D;                                       // [block][D + 4] rope (cos, sin) pairs
 
     const int es = bf16_ring ? 2 : 4;
-    const char *rb = (const char *)a.rings[b];
+    // the ring (or the page) holding the chunk's slots; the block chunk reads none
+    const RingLoc loc = ring_locate(a.rings[b], a.paged, a.W, is_block ? 0 : c * a.CH);
+    const char *rb = loc.base;
     const void *Kb = rb;
-    const void *Vb = rb + ring_v_offset(a.L, a.Hkv, a.W, D, es);
-    const int32_t *sp = (const int32_t *)(rb + ring_pos_offset(a.L, a.Hkv, a.W, D, es));
-    const size_t head_base = ((size_t)a.layer * a.Hkv + j) * a.W;  // slot-row index of slot 0
-    const int s0 = c * a.CH;
+    const void *Vb = rb + ring_v_offset(a.L, a.Hkv, loc.W, D, es);
+    const int32_t *sp = (const int32_t *)(rb + ring_pos_offset(a.L, a.Hkv, loc.W, D, es));
+    const size_t head_base = ((size_t)a.layer * a.Hkv + j) * loc.W;  // slot-row index of slot 0
+    const int s0 = loc.slot;  // the chunk's first slot within it
     const float *qkvb = a.qkv + (size_t)b * a.block * a.nqkv;     // this sequence's 16 rows
     const int hh = wave & 3, half = wave >> 2;
     const bool active = hh < a.G;
@@ -473,7 +478,7 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
         head_load<D>(qv, qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D, grp);
         if (is_block) head_load<D>(kbv, qkvb + (size_t)q * a.nqkv + a.qdim + (size_t)j * D, grp);
     }
-    const int kp_reg = (!is_block && tid < a.CH) ? sp[s0 + tid] : 0;
+    const int kp_reg = (!is_block && tid < a.CH) ? (loc.ok ? sp[s0 + tid] : -1) : 0;  // bad page: empty
     const int ncs4 = a.block * D / 4;  // float4 words of the rope table rows (at most 512)
     constexpr int NCS = 512 / NT;
     float4 cs_reg[NCS], w_reg = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -823,6 +828,7 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     a.qdim = c->qdim;
     a.kvdim = c->kvdim;
     a.rings = rings;
+    a.paged = c->paged;
     a.layer = l;
     a.L = c->L;
     a.Hkv = c->Hkv;

@@ -140,6 +140,58 @@ class Drafter:
     def ring_reset(self, ring: torch.Tensor, stream=None) -> None:
         check(lib().dflash_ring_reset(self._ctx, _dev(ring, torch.uint8, "ring"), _stream(stream)))
 
+    # ------------------------------------------------------------------ paged drafter KV
+    PAGE_SLOTS = 128
+
+    def page_bytes(self) -> int:
+        return int(lib().dflash_page_bytes(C.byref(self.cfg)))
+
+    def set_paged_pool(self, pool: torch.Tensor | None, n_pages: int = 0) -> None:
+        """Switch to paged KV over `pool` (uint8, n_pages * page_bytes()), or back to contiguous rings (None).
+        In paged mode the `ring` of inject and the entries of ring_table are int32 block tables."""
+        ptr = None if pool is None else _dev(pool, torch.uint8, "pool")
+        check(lib().dflash_set_paged_pool(self._ctx, ptr, n_pages))
+        self._paged = pool is not None
+
+    def pages_reset(self, first: int, count: int, stream=None) -> None:
+        check(lib().dflash_pages_reset(self._ctx, first, count, _stream(stream)))
+
+    def new_pool(self, n_pages: int, stream=None) -> torch.Tensor:
+        """A pool of n_pages pages, switched to and reset."""
+        pool = torch.empty(n_pages * self.page_bytes(), dtype=torch.uint8, device=self.device)
+        self.set_paged_pool(pool, n_pages)
+        self.pages_reset(0, n_pages, stream)
+        return pool
+
+    def page_views(self, pool: torch.Tensor, page: int):
+        """(K, V, slot_pos) of one page: K, V [L, Hkv, 128, D], slot_pos [128]."""
+        s = self.shape
+        es = 4 if self.ring_dtype == "f32" else 2
+        P = self.PAGE_SLOTS
+        kv = s.n_layer * s.n_head_kv * P * s.head_dim * es
+        kv_al = (kv + 255) // 256 * 256
+        pg = pool[page * self.page_bytes():(page + 1) * self.page_bytes()]
+        dt = torch.float32 if es == 4 else torch.bfloat16
+        shp = (s.n_layer, s.n_head_kv, P, s.head_dim)
+        return pg[:kv].view(dt).view(shp), pg[kv_al:kv_al + kv].view(dt).view(shp), \
+            pg[2 * kv_al:2 * kv_al + 4 * P].view(torch.int32)
+
+    def gather_ring(self, pool: torch.Tensor, table: torch.Tensor):
+        """The logical ring (K, V [L, Hkv, W, D], slot_pos [W]) a block table describes (entries outside the
+        pool read as empty slots with zero K/V)."""
+        s = self.shape
+        ids = table.cpu().tolist()
+        n_pages = pool.numel() // self.page_bytes()
+        Ks, Vs, sps = [], [], []
+        for pg in ids:
+            if 0 <= pg < n_pages:
+                K, V, sp = self.page_views(pool, pg)
+            else:
+                K0, V0, sp0 = self.page_views(pool, 0)
+                K, V, sp = torch.zeros_like(K0), torch.zeros_like(V0), torch.full_like(sp0, -1)
+            Ks.append(K), Vs.append(V), sps.append(sp)
+        return torch.cat(Ks, dim=2), torch.cat(Vs, dim=2), torch.cat(sps)
+
     def _ring_geom(self):
         s = self.shape
         es = 4 if self.ring_dtype == "f32" else 2
@@ -170,7 +222,8 @@ class Drafter:
 
     def inject(self, ring: torch.Tensor, h: torch.Tensor, positions: torch.Tensor, stream=None) -> None:
         T = h.shape[0]
-        check(lib().dflash_inject(self._ctx, _dev(ring, torch.uint8, "ring"), _dev(h, torch.float32, "h"),
+        rdt = torch.int32 if getattr(self, "_paged", False) else torch.uint8
+        check(lib().dflash_inject(self._ctx, _dev(ring, rdt, "ring"), _dev(h, torch.float32, "h"),
                                   _dev(positions, torch.int32, "positions"), T, _stream(stream)))
 
     def ring_table(self, rings) -> torch.Tensor:

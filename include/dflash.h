@@ -134,7 +134,8 @@ void dflash_destroy(dflash_ctx *ctx);
 /* Mark every slot of `ring` empty (slot_pos[] = -1) and zero its K/V
  * storage. Empty slots get attention weight exactly 0; zeroed storage keeps
  * their contribution 0 (an arbitrary bit pattern could be NaN). A ring must be
- * reset once before its first inject. */
+ * reset once before its first inject. ESTATE in paged mode (reset pages with
+ * dflash_pages_reset). */
 int dflash_ring_reset(dflash_ctx *ctx, void *ring, void *stream);
 
 /* Cross-layer feature fusion (dflash_engine.py page, TargetContextFeatureFuser):
@@ -244,6 +245,25 @@ int32_t dflash_block_width(const dflash_ctx *ctx);
  * stays the unperturbed logits. temperature must be finite and >= 0 (0:
  * greedy), else DFLASH_EINVAL. Sampling steps take the per-launch kernels. */
 int dflash_set_sampling(dflash_ctx *ctx, float temperature, uint64_t seed);
+
+/* Paged drafter KV (metrale dflash_head.rs page, DflashBatch: a drafter block
+ * table per sequence, one table for all layers). A page holds 128 ring slots
+ * of every layer in the ring layout above (K [L][Hkv][128][D], V, slot_pos
+ * [128], each region 256-byte aligned): dflash_page_bytes of the config bytes
+ * (0 if window is not a multiple of 128). After dflash_set_paged_pool(ctx,
+ * pool, n_pages) with a non-NULL, 256-byte aligned device pool of n_pages
+ * pages, the `ring` of dflash_inject and the entries of `rings` of the step
+ * calls are device block tables instead: int32 [window / 128] page ids, slot s
+ * of the sequence living in page table[s / 128] at slot s % 128. A table
+ * entry outside 0..n_pages-1 makes its 128 slots empty (injection there is
+ * dropped); pages must not be shared by two live tables. Reset pages before
+ * their first use with dflash_pages_reset (zeroes K/V, slot_pos = -1; an
+ * invalid entry reads page 0's memory under an all-masked chunk, so page 0
+ * must hold finite values). pool NULL returns to contiguous rings; the mode
+ * applies to later calls and captures. EUNSUPPORTED if window % 128 != 0. */
+size_t dflash_page_bytes(const dflash_config *cfg);
+int dflash_set_paged_pool(dflash_ctx *ctx, void *pool, int32_t n_pages);
+int dflash_pages_reset(dflash_ctx *ctx, int32_t first, int32_t count, void *stream);
 
 /* The path (DFLASH_PATH_KERNELS or DFLASH_PATH_PERSISTENT) a block step of B
  * sequences takes now; -1 for a NULL ctx. */

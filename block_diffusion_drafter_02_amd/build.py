@@ -53,5 +53,41 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_usage(sources=SOURCES) -> dict:
+    """Per-kernel register, scratch and occupancy figures the compiler reports for gfx950.
+
+    Compiles the device side of each source once more (nothing is written) and
+    parses the kernel-resource-usage remarks: {kernel: {"vgprs", "agprs",
+    "sgprs", "scratch", "occupancy"}}.
+    """
+    hipcc = _hipcc()
+    keys = {"VGPRs": "vgprs", "AGPRs": "agprs", "TotalSGPRs": "sgprs",
+            "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy"}
+
+    def one(src: str) -> dict:
+        cmd = [hipcc, *FLAGS, "--cuda-device-only", "-c", os.path.join(CSRC, src), "-o", os.devnull,
+               "-Rpass-analysis=kernel-resource-usage"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile of {src} failed:\n{r.stderr}")
+        out, cur = {}, None
+        for line in r.stderr.splitlines():
+            if "remark:" not in line:
+                continue
+            text = line.split("remark:", 1)[1].split(" [-Rpass", 1)[0].strip()
+            name, _, val = text.rpartition(": ")
+            if name == "Function Name":
+                cur = out.setdefault(val, {})
+            elif cur is not None and name in keys:
+                cur[keys[name]] = int(val)
+        return out
+
+    res = {}
+    with ThreadPoolExecutor(len(sources)) as ex:
+        for part in ex.map(one, sources):
+            res.update(part)
+    return res
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

@@ -489,7 +489,7 @@ struct RingLoc {
     int W;       // its window
     bool ok;     // false for a page id outside 0..n_pages-1 (the slot then reads as empty, writes are dropped)
 };
-__device__ __forceinline__ RingLoc ring_locate(const void *ring_or_table, const PagedPool &pp, int W, int slot) {
+__device__ __forceinline__ RingLoc ring_locate(const void *ring_or_table, PagedPool pp, int W, int slot) {
     if (pp.pool == nullptr) return RingLoc{(char *)ring_or_table, slot, W, true};
     const int pg = ((const int32_t *)ring_or_table)[slot / PAGE_SLOTS];
     const bool ok = pg >= 0 && pg < pp.n_pages;

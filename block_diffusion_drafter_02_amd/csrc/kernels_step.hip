@@ -509,19 +509,20 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
         const uint16_t *vg = (const uint16_t *)Vb + (head_base + s0) * D;
 #pragma unroll
         for (int u0 = 0; u0 < NWORD; u0 += BATCH) {
-            uint4 kbuf[BATCH], vbuf[BATCH];
+            // native vectors, not uint4: a struct copy into LDS can leave the buffer in scratch memory
+            u32x4_t kbuf[BATCH], vbuf[BATCH];
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
                 const int w = min(tid + NT * (u0 + u), nword - 1);  // clamped: every lane loads
-                kbuf[u] = *(const uint4 *)(kg + 8 * (size_t)w);
-                vbuf[u] = *(const uint4 *)(vg + 8 * (size_t)w);
+                kbuf[u] = *(const u32x4_t *)(kg + 8 * (size_t)w);
+                vbuf[u] = *(const u32x4_t *)(vg + 8 * (size_t)w);
             }
 #pragma unroll
             for (int u = 0; u < BATCH; ++u) {
                 const int w = tid + NT * (u0 + u);
                 if (w < nword) {
                     const int key = (8 * w) / D, d = (8 * w) % D;
-                    *(uint4 *)(ksh + key * KROW + d) = kbuf[u];
+                    *(u32x4_t *)(ksh + key * KROW + d) = kbuf[u];
                     const uint32_t pk[4] = {vbuf[u].x, vbuf[u].y, vbuf[u].z, vbuf[u].w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {

@@ -112,6 +112,65 @@ def read_traffic(bytes_per_launch_alg: float):
     return c.get("hbm_bytes_per_launch")
 
 
+GU_KERNEL = "gemv_kernel<1, 0, 1, 2, 1, 4>"  # bf16 weights, split activations, one row tile, SwiGLU, 4 waves
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_means(run_dir: str, counter: str) -> tuple[float, float]:
+    """(mean per dispatch of the gate/up GEMV, mean of the five largest device copies) of one rocprofv3 --pmc
+    counter in KiB, from the counter_collection CSV under run_dir."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    gu, copies = [], []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if GU_KERNEL in r["Kernel_Name"]:
+                gu.append(v)
+            elif COPY_KERNEL in r["Kernel_Name"]:
+                copies.append(v)
+    if not gu or len(copies) < 5:
+        raise SystemExit(f"{counter}: {len(gu)} gate/up dispatches, {len(copies)} copies in {run_dir}")
+    top = sorted(copies)[-5:]
+    return sum(gu) / len(gu), sum(top) / len(top)
+
+
+def write_counters(fetch_dir: str, write_dir: str, copy_mib: int, commands: list[str]) -> dict:
+    """Reduce two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, each with a device copy of copy_mib MiB
+    for calibration) to the HBM bytes per gate/up launch, stored with the hash of the kernel sources."""
+    fetch, fcopy = _counter_means(fetch_dir, "FETCH_SIZE")
+    write, wcopy = _counter_means(write_dir, "WRITE_SIZE")
+    n = copy_mib << 20
+    ff, wf = n / (fcopy * 1024.0), n / (wcopy * 1024.0)  # true bytes per counted byte, from a copy of known size
+    from block_diffusion_drafter_02_amd import synth
+
+    sh = synth.REAL
+    alg = 2 * sh.n_ff * sh.n_embd * 2 + 16 * (sh.n_embd + sh.n_ff) * 4
+    out = {
+        "kernel": f"void {GU_KERNEL}(GemvArgs)",
+        "workload": "real-dimension bf16 block step, gate/up projection + SwiGLU (one launch per layer)",
+        "fetch_size_kib_per_dispatch": round(fetch, 1),
+        "write_size_kib_per_dispatch": round(write, 1),
+        "calibration": {"kernel": COPY_KERNEL, "bytes": n, "fetch_size_kib": round(fcopy, 3),
+                        "write_size_kib": round(wcopy, 3), "fetch_factor": round(ff, 4),
+                        "write_factor": round(wf, 4)},
+        "hbm_bytes_per_launch": int(round(fetch * 1024.0 * ff + write * 1024.0 * wf)),
+        "algorithmic_bytes_per_launch": alg,
+        "kernel_src_sha256_16": kernel_src_hash(),
+        "commands": commands,
+        "kernel_src": [os.path.relpath(f, ROOT) for f in KERNEL_SRC],
+    }
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
 def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes, inject_feats=None, min_seconds=10.0,
                  max_seconds=30.0, block_width=16):
     """The oracle, as it stands, for block steps of one sequence at the same dimensions on a synthetic ring
@@ -175,7 +234,19 @@ def main() -> int:
                     help="block-step path (auto: the per-launch kernels; persistent: the opt-in persistent chain)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (five times) to calibrate byte counters")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="reduce two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy-mib bench "
+                         "into the committed gate/up traffic figures, then exit (no GPU needed)")
     args = ap.parse_args()
+    if args.write_counters:
+        mib = args.calibrate_copy_mib or 1024
+        cmd = ("rocprofv3 --pmc {c} -d {d} -o run --output-format csv -- python -u bench.py --steps 3 --warmup 1 "
+               f"--no-cpu-baseline --stage-reps 3 --calibrate-copy-mib {mib}")
+        out = write_counters(args.write_counters[0], args.write_counters[1], mib,
+                             [cmd.format(c="FETCH_SIZE", d=args.write_counters[0]),
+                              cmd.format(c="WRITE_SIZE", d=args.write_counters[1])])
+        print(json.dumps(out), flush=True)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)

@@ -224,8 +224,8 @@ hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, in
 // ---------------------------------------------------------------------------
 // Grid (E/64, B), 256 threads. Writes x [M][E], act_a = x * attn_norm_0 in the
 // activation format, ss_a[g][m] = sum of x^2 over the group's 64 columns.
-// Workgroup (0, b) also writes rope_cs[b][i][f] = (cos, sin)((n_past + i) *
-// inv_freq[f]), computed in fp64.
+// The workgroups of sequence b also write rope_cs[b][i][f] = (cos, sin)((n_past
+// + i) * inv_freq[f]), computed in fp64, one entry per thread.
 struct EmbedArgs {
     const void *tok_embd;
     int aux_dtype, E, V, mask_id, block, D;
@@ -258,9 +258,9 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
         const float sq = wave_sum(v * v);
         if (lane == 0) a.ss_a[(size_t)g * a.ss_stride + m] = sq;
     }
-    if (g == 0) {
+    {  // the rope table's block * D/2 entries, spread over the sequence's workgroups
         const int half = a.D / 2;
-        for (int idx = tid; idx < a.block * half; idx += 256) {
+        for (int idx = g * 256 + tid; idx < a.block * half; idx += gridDim.x * 256) {
             const int i = idx / half, f = idx % half;
             const double theta = (double)(a.n_past[b] + i) * a.inv_freq[f];
             double sn, cn;
@@ -587,10 +587,30 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
         if (is_block) head_norm_rope_row<D>(kbv, wsh + D, csh + q * (D + 4), grp, a.eps, 1.0f);
         // ---- S^T = K Q^T, key tile kt: lane holds keys 16(kt0+kt) + 4grp + i (i < 4) of query q ----
         f32x4_t st[HKT];
+#pragma unroll
+        for (int kt = 0; kt < HKT; ++kt) st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // A full chunk of bf16 ring keys (every ring chunk of a bf16 ring) runs
+        // as straight-line code: per k-step the wave's key tiles are read from
+        // LDS together and their MFMA chains interleave. Each accumulator sums
+        // in the same order as the general loop below.
+        const bool fast = !split_kv && nkt == HKT;
+        if (fast) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8_t ka[HKT];
+#pragma unroll
+                for (int kt = 0; kt < HKT; ++kt)
+                    ka[kt] = __builtin_bit_cast(
+                        bf16x8_t, *(const u32x4_t *)(ksh + (16 * (kt0 + kt) + q) * KROW + 32 * ks + 8 * grp));
+#pragma unroll
+                for (int t = 0; t < 3; ++t)
+#pragma unroll
+                    for (int kt = 0; kt < HKT; ++kt) st[kt] = MFMA_BF16(ka[kt], qb[ks][t], st[kt]);
+            }
+        }
 #pragma clang loop unroll(full)
         for (int kt = 0; kt < HKT; ++kt) {
-            st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (kt >= nkt) continue;
+            if (fast || kt >= nkt) continue;
             const int key = 16 * (kt0 + kt) + q;  // A-operand row of this lane
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -622,15 +642,15 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
         // ---- mask and softmax statistics of this wave's keys for query q ----
 #pragma clang loop unroll(full)
         for (int kt = 0; kt < HKT; ++kt) {
+            const int key0 = 16 * (kt0 + kt) + 4 * grp;  // this lane's four keys: key0 .. key0 + 3
+            int4 kp = make_int4(-1, -1, -1, -1);
+            if (!is_block && kt < nkt) kp = *(const int4 *)(kpos + key0);
+            const int kpv[4] = {kp.x, kp.y, kp.z, kp.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                bool vis = kt < nkt;
-                if (vis && is_block) vis = 16 * (kt0 + kt) + 4 * grp + i < a.gamma;
-                if (vis && !is_block) {
-                    const int kp = kpos[16 * (kt0 + kt) + 4 * grp + i];
-                    const int dlt = qpos - kp;
-                    vis = kp >= 0 && dlt >= 0 && dlt < a.W;
-                }
+                // ring key: a written slot whose position lies in [qpos - W + 1, qpos]; block key: < gamma
+                const bool vis = kt < nkt && (is_block ? key0 + i < a.gamma
+                                                       : kpv[i] >= 0 && (unsigned)(qpos - kpv[i]) < (unsigned)a.W);
                 if (!vis) st[kt][i] = -INFINITY;
                 mx = fmaxf(mx, st[kt][i]);
             }
@@ -648,9 +668,37 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
         lsum += __shfl_xor(lsum, 16, 64);
         lsum += __shfl_xor(lsum, 32, 64);
         // ---- O^T = V^T P^T over key pairs of tiles (2ks2, 2ks2 + 1) of this half ----
+        if constexpr (HKT % 2 == 0) {
+            if (fast) {  // one bf16 plane; per key pair all V^T reads first, then the interleaved chains
+#pragma unroll
+                for (int ks2 = 0; ks2 < HKT / 2; ++ks2) {
+                    float pv[8];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pv[i] = st[2 * ks2][i];
+                        pv[4 + i] = st[2 * ks2 + 1][i];
+                    }
+                    bf16x8_t pb[3];
+                    split8(pv, pb);
+                    const int kbase = 16 * kt0 + 32 * ks2;
+                    const int k0 = kbase + 4 * grp, k1 = kbase + 16 + 4 * grp;
+                    bf16x8_t va[DT];
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const uint16_t *row = vt + (size_t)(16 * dt + q) * CHP;
+                        const uint2 lo = *(const uint2 *)(row + k0), hi = *(const uint2 *)(row + k1);
+                        va[dt] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+                    }
+#pragma unroll
+                    for (int t = 0; t < 3; ++t)
+#pragma unroll
+                        for (int dt = 0; dt < DT; ++dt) ot[dt] = MFMA_BF16(va[dt], pb[t], ot[dt]);
+                }
+            }
+        }
 #pragma clang loop unroll(full)
         for (int ks2 = 0; ks2 < (HKT + 1) / 2; ++ks2) {
-            if (2 * ks2 >= nkt) continue;
+            if ((HKT % 2 == 0 && fast) || 2 * ks2 >= nkt) continue;
             float pv[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -786,7 +834,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombArgs a) {
     const int NQ = a.G * 16, qi = hh * 16 + i;
     const size_t base = ((size_t)b * a.Hkv + j) * (a.NCH + 1);
     const int nc = a.NCH + 1;
-    // one pass with a running maximum over batches of 24 chunks whose loads are all in flight together
+    // batches of 24 chunks whose loads are all in flight together; per batch
+    // the running state is rescaled once to the batch's maximum and every
+    // chunk weight exp(m_c - max) is independent of the others
     constexpr int UNR = 24;
     float mstar = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int c0 = 0; c0 < nc; c0 += UNR) {
@@ -797,18 +847,26 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombArgs a) {
             mlb[u] = *(const float2 *)(a.ml + ((base + cc) * NQ + qi) * 2);
             ovb[u] = *(const float2 *)(a.o + ((base + cc) * NQ + qi) * a.D + d);
         }
+        float bm = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < UNR; ++u)
+            if (c0 + u < nc) bm = fmaxf(bm, mlb[u].x);
+        if (bm == -INFINITY) continue;  // no visible key in this batch
+        const float mn = fmaxf(mstar, bm);
+        const float alpha = expf(mstar - mn);  // 0 while mstar is -inf
+        lsum *= alpha;
+        o0 *= alpha;
+        o1 *= alpha;
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-            if (c0 + u < nc && mlb[u].x != -INFINITY) {
-                const float mn = fmaxf(mstar, mlb[u].x);
-                const float alpha = expf(mstar - mn);  // 0 when mstar is -inf
+            if (c0 + u < nc && mlb[u].x != -INFINITY) {  // a chunk without visible keys adds nothing
                 const float w = expf(mlb[u].x - mn);
-                lsum = lsum * alpha + w * mlb[u].y;
-                o0 = o0 * alpha + w * ovb[u].x;
-                o1 = o1 * alpha + w * ovb[u].y;
-                mstar = mn;
+                lsum += w * mlb[u].y;
+                o0 += w * ovb[u].x;
+                o1 += w * ovb[u].y;
             }
         }
+        mstar = mn;
     }
     const float inv = 1.0f / lsum;
     const int row = b * a.block + i;

@@ -120,6 +120,15 @@ __global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
     const int kb1 = min(KB, kb0 + a.kb_per_split);
     const int M = a.epi.M;
 
+    // A 16-wave workgroup runs one per compute unit, so registers are not what
+    // limits its occupancy: the four waves that may run the epilogue load its
+    // operands (norm sums, residual row, column scales) before the weight
+    // stream, taking their latency off the kernel's tail.
+    constexpr bool PF = NWV == 16 && CW == GROUP_N;
+    EpiPre pre{};
+    if constexpr (PF)
+        if (tid < 256) epi_prefetch<EPI, 1>(a.epi, g, pre);
+
     f32x4 acc[MT][TPW];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
                                    (size_t)G * TE, a.S, &a.counters[g], &flag_s))
             return;
     }
-    gemv_epilogue<EPI, MT, WN, false, CW>(a.epi, g, G, tile, rs_s, &flag_s, best_s);
+    gemv_epilogue<EPI, MT, WN, PF, CW>(a.epi, g, G, tile, rs_s, &flag_s, best_s, pre);
 }
 
 template <int WT, int AF, int EPI, int WN>

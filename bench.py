@@ -112,7 +112,7 @@ def read_traffic(bytes_per_launch_alg: float):
     return c.get("hbm_bytes_per_launch")
 
 
-GU_KERNEL = "gemv_kernel<1, 0, 1, 2, 1, 4>"  # bf16 weights, split activations, one row tile, SwiGLU, 4 waves
+GU_KERNEL = "gemv_kernel<1, 0, 1, 2, 1, 4, 64>"  # bf16 weights, split activations, one row tile, SwiGLU, 4 waves, 64 columns
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -240,7 +240,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.write_counters:
         mib = args.calibrate_copy_mib or 1024
-        cmd = ("rocprofv3 --pmc {c} -d {d} -o run --output-format csv -- python -u bench.py --steps 3 --warmup 1 "
+        cmd = ("rocprofv3 --pmc {c} -d {d} -o run --output-format csv -- python3 -u bench.py --steps 3 --warmup 1 "
                f"--no-cpu-baseline --stage-reps 3 --calibrate-copy-mib {mib}")
         out = write_counters(args.write_counters[0], args.write_counters[1], mib,
                              [cmd.format(c="FETCH_SIZE", d=args.write_counters[0]),

@@ -248,7 +248,7 @@ def main() -> int:
         print(json.dumps(out), flush=True)
         return 0
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the drafter library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         return 2
 

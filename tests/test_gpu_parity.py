@@ -320,3 +320,38 @@ def test_accept_scan_bruteforce(gpu):
         n_ok = dr.accept(torch.from_numpy(d).cuda(), torch.from_numpy(t).cuda()).cpu().numpy()
         np.testing.assert_array_equal(n_ok, [O.accept(d[b], t[b]) for b in range(8)])
         np.testing.assert_array_equal(n_ok, m)
+
+
+@pytest.mark.parametrize("spec", [WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16"), WL.Spec(synth.TINY, "f32", "f32", "f32")],
+                         ids=_spec_id)
+def test_empty_ring_at_position_zero_beside_a_wrapped_ring(gpu, spec):
+    """Degenerate start of a sequence: a reset ring and n_past = 0, so the block attends to its own keys only,
+    batched beside a wrapped ring (n_past = window + 44) whose chunks are all in use."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
+
+    shape = spec.shape
+    raw = synth.weights(shape, spec.weight_dtype, seed=0)
+    chunk = min(shape.window, 64)
+    dr = Drafter(shape, raw, spec.weight_dtype, spec.ring_dtype, spec.feature_dtype, max_batch=2, max_inject=chunk)
+    empty = dr.new_ring()
+    n_full = shape.window + 44
+    feats = synth.features(shape, n_full, spec.feature_dtype, seed=0, tag="feats-full")
+    pos = np.arange(n_full, dtype=np.int64)
+    full = dr.new_ring()
+    WL.gpu_inject(dr, full, to_device(feats, dr.device), pos, chunk)
+    ocfg, ow, ofull = WL.oracle_side(spec, raw, feats, pos, chunk)
+    oempty = O.Ring(ocfg)
+    st = synth.step_inputs(shape, 2, seed=11)
+    n_pasts = [0, n_full]
+    print(f"[case] empty + wrapped ring {_spec_id(spec)} n_past={n_pasts}", flush=True)
+    logits, drafts = _step(dr, [empty, full], st["id_last"], n_pasts)
+    for b, (oring, n) in enumerate(((oempty, 0), (ofull, n_full))):
+        ref = O.block_forward(ocfg, ow, oring, O.block_ids(ocfg, int(st["id_last"][b])), n)
+        tol = _check_logits(spec, ref, logits[16 * b:16 * (b + 1)], label=f"seq{b}")
+        bad, ties = WL.compare_drafts(ref, drafts[b], tol)
+        assert not bad, (b, bad, ties)
+    # the empty ring's slot table is untouched by the step
+    _, _, sp = dr.ring_views(empty)
+    assert bool((sp == -1).all())
+    del torch

@@ -355,3 +355,47 @@ def test_empty_ring_at_position_zero_beside_a_wrapped_ring(gpu, spec):
     _, _, sp = dr.ring_views(empty)
     assert bool((sp == -1).all())
     del torch
+
+
+@pytest.mark.parametrize("spec", [WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16"), WL.Spec(synth.TINY, "f32", "f32", "f32")],
+                         ids=_spec_id)
+def test_scattered_inject_with_holes_stale_slots_and_skipped_positions(gpu, spec):
+    """Two inject calls of shuffled, non-contiguous positions: the first fills half the slots (the rest stay
+    empty), the second overwrites some of them with positions a window later and leaves others holding
+    positions that fall out of the window of some block rows. Positions -1 in a call are skipped (no slot is
+    written). Slot table, ring values, logits and drafts against the oracle fed the same calls without them."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
+
+    shape = spec.shape
+    W = shape.window
+    rng = np.random.default_rng(21)
+    raw = synth.weights(shape, spec.weight_dtype, seed=0)
+    dr = Drafter(shape, raw, spec.weight_dtype, spec.ring_dtype, spec.feature_dtype, max_batch=1, max_inject=W)
+    ocfg = O.Config.from_shape(shape, spec.ring_dtype)
+    ow = O.Weights(raw, spec.weight_dtype)
+    oring = O.Ring(ocfg)
+    ring = dr.new_ring()
+    first = rng.permutation(W)[: W // 2]                      # half the slots, shuffled; the rest stay empty
+    res = rng.permutation(W)[: W // 3]                         # residues rewritten one window later (distinct)
+    second = W + res + W * (res < W // 8)                      # a few of them two windows later
+    calls = [first, second]
+    for ci, pos in enumerate(calls):
+        gpu_pos = pos.copy().astype(np.int64)
+        gpu_pos = np.insert(gpu_pos, [1, len(gpu_pos) // 2], -1)  # skipped positions
+        feats = synth.features(shape, len(gpu_pos), spec.feature_dtype, seed=0, tag=f"scatter{ci}")
+        h = dr.encode(to_device(feats, dr.device))
+        dr.inject(ring, h, torch.from_numpy(gpu_pos.astype(np.int32)).to(dr.device))
+        keep = gpu_pos >= 0
+        O.inject(ocfg, ow, oring, O.encode(ocfg, ow, feats[keep]), gpu_pos[keep])
+    torch.cuda.synchronize()
+    _check_ring(dr, ring, oring, spec)
+    n_past = int(max(second.max(), first.max())) + 1
+    st = synth.step_inputs(shape, 1, seed=23)
+    print(f"[case] scattered inject {_spec_id(spec)} n_past={n_past}", flush=True)
+    logits, drafts = _step(dr, [ring], st["id_last"], [n_past])
+    ref = O.block_forward(ocfg, ow, oring, O.block_ids(ocfg, int(st["id_last"][0])), n_past)
+    tol = _check_logits(spec, ref, logits)
+    bad, ties = WL.compare_drafts(ref, drafts[0], tol)
+    assert not bad, (bad, ties)
+    del torch

@@ -742,6 +742,7 @@ int dflash_pages_reset(dflash_ctx *x, int32_t first, int32_t count, void *stream
 
 int dflash_encode(dflash_ctx *x, const void *feats, int32_t T, float *h, void *stream) {
     if (!x || !feats || !h) return fail(DFLASH_EINVAL, "ctx, feats or h is NULL");
+    if ((uintptr_t)feats % 16 || (uintptr_t)h % 16) return fail(DFLASH_EINVAL, "feats and h must be 16-byte aligned");
     if (T < 1 || T > x->cfg.max_inject) return fail(DFLASH_ERANGE, "T=%d outside 1..max_inject=%d", T, x->cfg.max_inject);
     hipStream_t s = (hipStream_t)stream;
     const dflash_config &c = x->cfg;

@@ -88,16 +88,50 @@ hipError_t launch_split(const float *src, int rows, int K, int ld_src, void *dst
 // Encode: h = y * rsqrt(mean(y^2) + eps) * w   (one workgroup per row)
 // ---------------------------------------------------------------------------
 // y holds S k-split partials [S][T][E], summed here in split order first.
+// Each thread takes float4 columns c and c + 256 of the row at once and issues
+// the loads of up to eight splits of both together before adding them in
+// split order (E is a multiple of 64, so a row is whole float4 words).
 __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *y, int S, int T, int E, const float *w,
                                                            float eps, float *h) {
-    const int t = blockIdx.x;
-    float *hr = h + (size_t)t * E;
+    constexpr int U = 2, SB = 8;
+    const int t = blockIdx.x, E4 = E / 4;
+    const float4 *y4 = (const float4 *)y;
+    float4 *h4 = (float4 *)(h + (size_t)t * E);
     float ss = 0.0f;
-    for (int c = threadIdx.x; c < E; c += 256) {
-        float v = y[(size_t)t * E + c];
-        for (int sp = 1; sp < S; ++sp) v += y[((size_t)sp * T + t) * E + c];
-        hr[c] = v;
-        ss += v * v;
+    for (int c0 = threadIdx.x; c0 < E4; c0 += 256 * U) {
+        float4 v[U];
+        for (int s0 = 0; s0 < S; s0 += SB) {
+            float4 p[SB][U];
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + 256 * u;
+                    p[j][u] = (s0 + j < S && c < E4) ? y4[((size_t)(s0 + j) * T + t) * E4 + c]
+                                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (s0 + j == 0) {
+                        v[u] = p[j][u];
+                    } else if (s0 + j < S) {
+                        v[u].x += p[j][u].x;
+                        v[u].y += p[j][u].y;
+                        v[u].z += p[j][u].z;
+                        v[u].w += p[j][u].w;
+                    }
+                }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = c0 + 256 * u;
+            if (c < E4) {
+                h4[c] = v[u];
+                ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
+            }
+        }
     }
     ss = wave_sum(ss);
     __shared__ float red[4];
@@ -105,7 +139,11 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const float *y, int S
     __syncthreads();
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float r = 1.0f / sqrtf(tot / (float)E + eps);
-    for (int c = threadIdx.x; c < E; c += 256) hr[c] = hr[c] * r * w[c];
+    const float4 *w4 = (const float4 *)w;
+    for (int c = threadIdx.x; c < E4; c += 256) {  // the words this thread wrote above
+        const float4 x = h4[c], g = w4[c];
+        h4[c] = make_float4(x.x * r * g.x, x.y * r * g.y, x.z * r * g.z, x.w * r * g.w);
+    }
 }
 
 hipError_t launch_rmsnorm_rows(const float *y, int S, int T, int E, const float *w, float eps, float *h,

@@ -140,7 +140,8 @@ int dflash_ring_reset(dflash_ctx *ctx, void *ring, void *stream);
 
 /* Cross-layer feature fusion (dflash_engine.py page, TargetContextFeatureFuser):
  * h = RMSNorm(feats . fc^T) * hidden_norm. feats [T, n_capture*target_hidden]
- * in feature_dtype, h [T, n_embd] f32. 1 <= T <= max_inject. */
+ * in feature_dtype, h [T, n_embd] f32, both device buffers 16-byte aligned
+ * (EINVAL otherwise). 1 <= T <= max_inject (ERANGE otherwise). */
 int dflash_encode(dflash_ctx *ctx, const void *feats, int32_t T, float *h, void *stream);
 
 /* KV injection (dflash-ops card, Method; Requirements and limits): for every

@@ -399,3 +399,28 @@ def test_scattered_inject_with_holes_stale_slots_and_skipped_positions(gpu, spec
     bad, ties = WL.compare_drafts(ref, drafts[0], tol)
     assert not bad, (bad, ties)
     del torch
+
+
+def test_encode_rejects_misaligned_buffers_before_launch(gpu):
+    """feats and h are read and written as 16-byte words: a buffer 4 bytes off alignment is refused with EINVAL
+    and nothing is written."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd import _lib
+    from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
+
+    shape = synth.TINY
+    raw = synth.weights(shape, "f32", seed=0)
+    dr = Drafter(shape, raw, "f32", "f32", "f32", max_batch=1, max_inject=16)
+    feats = to_device(synth.features(shape, 8, "f32", seed=0), dr.device)
+    flat = torch.full((8 * shape.n_embd + 4,), 7.0, dtype=torch.float32, device=dr.device)
+    h_bad = flat[1:1 + 8 * shape.n_embd].view(8, shape.n_embd)
+    with pytest.raises(_lib.DFlashError) as err:
+        dr.encode(feats, h_bad)
+    assert err.value.code == _lib.EINVAL and "aligned" in str(err.value)
+    torch.cuda.synchronize()
+    assert bool((flat == 7.0).all())
+    h_ok = flat[4:4 + 8 * shape.n_embd].view(8, shape.n_embd)  # 16 bytes in: aligned
+    dr.encode(feats, h_ok)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(h_ok).all())
+    del torch

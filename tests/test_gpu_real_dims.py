@@ -181,3 +181,37 @@ def test_real_fp8_weights_with_bulk_inject(gpu):
     tgt = _targets([ref], st)
     logits, drafts, n_ok = _graph_step(dr, [ring], st["id_last"], [2560], tgt)
     _check_sequence(spec, ref, logits, drafts[0], n_ok[0], st["mismatch"][0], "fp8 n_past 2560")
+
+
+def test_real_bf16_paged_wrapped_ring_step(gpu):
+    """bf16 weights, paged drafter KV at real dimensions: the ring is 16 pages of 128 slots taken in shuffled
+    order from a pool of 20, filled with positions 0..2299 (so it wraps), stepped at n_past 2300 in the bench's
+    launch configuration. The logical ring gathered through the table must equal the oracle's."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter, to_device
+
+    spec = WL.Spec(REAL, "bf16", "bf16", "bf16")
+    raw = synth.weights(REAL, "bf16", seed=0)
+    dr = Drafter(REAL, raw, "bf16", "bf16", "bf16", max_batch=1, max_inject=REAL.window)
+    n_tab = REAL.window // dr.PAGE_SLOTS
+    pool = dr.new_pool(n_tab + 4)
+    table = torch.tensor(np.random.default_rng(5).permutation(n_tab + 4)[:n_tab], dtype=torch.int32,
+                         device=dr.device)
+    pos = np.arange(2300)
+    feats = synth.features(REAL, len(pos), "bf16", seed=0, tag="real.paged.feats")
+    WL.gpu_inject(dr, table, to_device(feats, dr.device), pos, REAL.window)
+    torch.cuda.synchronize()
+    cfg, w, oring = WL.oracle_side(spec, raw, feats, pos, REAL.window)
+    K, V, sp = dr.gather_ring(pool, table)
+    np.testing.assert_array_equal(sp.cpu().numpy(), oring.slot_pos.astype(np.int32))
+    slots = [0, 127, 128, 251, 252, 2047]
+    for l in (0, REAL.n_layer - 1):
+        WL.check_ring_values(spec, K[l][:, slots].float().cpu().numpy().astype(np.float64), oring.K[l][:, slots],
+                             f"paged ring K layer {l}")
+        WL.check_ring_values(spec, V[l][:, slots].float().cpu().numpy().astype(np.float64), oring.V[l][:, slots],
+                             f"paged ring V layer {l}")
+    st = synth.step_inputs(REAL, 1, seed=15)
+    ref = O.block_forward(cfg, w, oring, O.block_ids(cfg, int(st["id_last"][0])), 2300)
+    tgt = _targets([ref], st)
+    logits, drafts, n_ok = _graph_step(dr, [table], st["id_last"], [2300], tgt)
+    _check_sequence(spec, ref, logits, drafts[0], n_ok[0], st["mismatch"][0], "paged bf16 n_past 2300")

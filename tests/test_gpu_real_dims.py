@@ -215,3 +215,40 @@ def test_real_bf16_paged_wrapped_ring_step(gpu):
     tgt = _targets([ref], st)
     logits, drafts, n_ok = _graph_step(dr, [table], st["id_last"], [2300], tgt)
     _check_sequence(spec, ref, logits, drafts[0], n_ok[0], st["mismatch"][0], "paged bf16 n_past 2300")
+
+
+def test_real_bf16_block_width_4_step(gpu):
+    """bf16, ring full at n_past 2048, block width 4 (the bench's bf16-g4 workload): a graph captured at width 4
+    drafts 3 positions and scans them; rows 0..3 against the oracle run with a 4-token block."""
+    import dataclasses
+
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter
+
+    g = 4
+    spec = WL.Spec(REAL, "bf16", "bf16", "bf16")
+    raw = synth.weights(REAL, "bf16", seed=0)
+    dr = Drafter(REAL, raw, "bf16", "bf16", "bf16", max_batch=1, max_inject=REAL.window)
+    ring, (cfg, w, oring), _ = _inject_both(spec, dr, raw, np.arange(2048), "real.g4.feats")
+    assert dr.set_block_width(g) == g
+    st = synth.step_inputs(REAL, 1, seed=16)
+    cfg_g = dataclasses.replace(cfg, block=g)
+    ref = O.block_forward(cfg_g, w, oring, O.block_ids(cfg_g, int(st["id_last"][0])), 2048)
+    odr = O.greedy_drafts(ref)
+    m = int(st["mismatch"][0]) % g
+    tgt = synth.planted_targets(odr[None], np.array([m]), np.zeros((1, g - 1), np.int64), REAL.n_vocab)
+    table = dr.ring_table([ring])
+    il = torch.tensor(st["id_last"], dtype=torch.int32, device=dr.device)
+    npst = torch.tensor([2048], dtype=torch.int32, device=dr.device)
+    logits = torch.empty((16, REAL.n_vocab), dtype=torch.float32, device=dr.device)
+    drafts = torch.empty((1, g - 1), dtype=torch.int32, device=dr.device)
+    target = torch.from_numpy(tgt.astype(np.int32)).to(dr.device)
+    n_ok = torch.empty((1,), dtype=torch.int32, device=dr.device)
+    stream = torch.cuda.Stream()
+    graph = dr.capture_step(table, il, npst, logits, drafts, target, n_ok, stream=stream)
+    with torch.cuda.stream(stream):
+        graph.launch(stream)
+    stream.synchronize()
+    graph.close()
+    got = logits.cpu().numpy().astype(np.float64)[:g]
+    _check_sequence(spec, ref, got, drafts.cpu().numpy()[0], n_ok.cpu().numpy()[0], m, "bf16 g=4 n_past 2048")

@@ -252,3 +252,31 @@ def test_real_bf16_block_width_4_step(gpu):
     graph.close()
     got = logits.cpu().numpy().astype(np.float64)[:g]
     _check_sequence(spec, ref, got, drafts.cpu().numpy()[0], n_ok.cpu().numpy()[0], m, "bf16 g=4 n_past 2048")
+
+
+def test_real_bf16_sampled_drafts_step(gpu):
+    """bf16, ring full at n_past 2048, drafts sampled at temperature 1 (the bench's bf16-sample workload) in
+    the captured step: every draft equals the oracle's Gumbel-max draw over the same Philox-4x32-10 noise or is
+    a near tie of the perturbed scores; the logits output stays unperturbed."""
+    torch = _torch()
+    from block_diffusion_drafter_02_amd.drafter import Drafter
+    from tests.test_gpu_sampling import SEED, _check_sampled
+
+    T = 1.0
+    spec = WL.Spec(REAL, "bf16", "bf16", "bf16")
+    raw = synth.weights(REAL, "bf16", seed=0)
+    dr = Drafter(REAL, raw, "bf16", "bf16", "bf16", max_batch=1, max_inject=REAL.window)
+    ring, (cfg, w, oring), _ = _inject_both(spec, dr, raw, np.arange(2048), "real.sample.feats")
+    dr.set_sampling(T, SEED)
+    st = synth.step_inputs(REAL, 1, seed=18)
+    ref = O.block_forward(cfg, w, oring, O.block_ids(cfg, int(st["id_last"][0])), 2048)
+    want = O.sampled_drafts(ref, T, SEED, 0, 2048)
+    tgt = synth.planted_targets(want[None], st["mismatch"][:1], st["filler"][:1], REAL.n_vocab)
+    logits, drafts, n_ok = _graph_step(dr, [ring], st["id_last"], [2048], tgt)
+    tol = WL.logit_tol(spec, ref)
+    assert np.abs(logits - ref).max() <= tol
+    ties = _check_sampled(ref, drafts[0], T, SEED, 0, 2048, tol)
+    if not ties:
+        assert int(n_ok[0]) == int(st["mismatch"][0])
+    print(f"[bf16 sampled T={T}] near ties {ties}", flush=True)
+    del torch

@@ -82,11 +82,29 @@ void choose_split(int G, int KB, int &S, int &kbps) {
 int mt_for(int M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8; }
 
 // k-splits of a batched block-row projection (gemm_kernel over all 16*B rows,
-// 256 columns per workgroup): about 512 workgroups, at least 8 k-blocks per
-// split. Depends only on N and K.
+// 256 columns per workgroup, one workgroup resident per compute unit). The
+// MFMA work comes in rounds of 256 workgroups (an MI355X's compute units), so
+// the split count is the one that minimises rounds x k-blocks per workgroup x
+// the time of a k-block (about 3 us for a 128 x 256 tile with three-term
+// products) plus the split partials' traffic (S x 128 rows x N f32, written
+// and read back, at about 5 TB/s); at least 8 k-blocks per split. Depends
+// only on N and K, so the workspace can be sized from the config.
 void batch_split(int N, int K, int &S, int &kbps) {
+    constexpr int SLOTS = 256;
+    constexpr double KBLOCK_US = 3.0, ROWS = 128.0, BYTES_PER_US = 5.0e6;
     const int KB = K / KBLK, tiles = (N / GROUP_N + 3) / 4;  // 256-column workgroup tiles
-    S = std::max(1, std::min((512 + tiles - 1) / tiles, std::max(1, KB / 8)));
+    const int smax = std::max(1, KB / 8);
+    double best = 0.0;
+    S = 1;
+    for (int s = 1; s <= smax; ++s) {
+        const int kb = (KB + s - 1) / s, se = (KB + kb - 1) / kb;
+        const double rounds = (double)((tiles * se + SLOTS - 1) / SLOTS);
+        const double us = rounds * kb * KBLOCK_US + se * ROWS * N * 8.0 / BYTES_PER_US;
+        if (s == 1 || us < best) {
+            best = us;
+            S = se;
+        }
+    }
     kbps = (KB + S - 1) / S;
     S = (KB + kbps - 1) / kbps;
 }

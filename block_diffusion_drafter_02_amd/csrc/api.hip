@@ -109,14 +109,28 @@ void batch_split(int N, int K, int &S, int &kbps) {
     S = (KB + kbps - 1) / kbps;
 }
 
-// k-splits of an encode / inject GEMM: enough workgroups (128 x 256 tiles) to
-// fill the GPU about twice, at least 16 k-blocks per split, and the S partial
-// [M][N] products must fit the [rows_cap][N] output buffer.
+// k-splits of an encode / inject GEMM (128 x 256 tiles, one workgroup
+// resident per compute unit): the count that minimises rounds of 256
+// workgroups x k-blocks per workgroup x about 3 us plus the partials' traffic
+// (S x M x N f32, written and read back, at about 5 TB/s), with at least 16
+// k-blocks per split and the S partial [M][N] products fitting the
+// [rows_cap][N] output buffer.
 void gemm_split(GemmArgs &g, int rows_cap) {
+    constexpr int SLOTS = 256;
+    constexpr double KBLOCK_US = 3.0, BYTES_PER_US = 5.0e6;
     const int KB = g.K / KBLK, tiles = ((g.N / GROUP_N + 3) / 4) * ((g.M + 127) / 128);  // 128 x 256 tiles
-    int S = std::max(1, (512 + tiles - 1) / tiles);
-    S = std::min(S, std::max(1, KB / 16));
-    S = std::min(S, std::max(1, rows_cap / g.M));
+    const int smax = std::max(1, std::min(KB / 16, rows_cap / g.M));
+    double best = 0.0;
+    int S = 1;
+    for (int s = 1; s <= smax; ++s) {
+        const int kb = (KB + s - 1) / s, se = (KB + kb - 1) / kb;
+        const double rounds = (double)((tiles * se + SLOTS - 1) / SLOTS);
+        const double us = rounds * kb * KBLOCK_US + (double)se * g.M * g.N * 8.0 / BYTES_PER_US;
+        if (s == 1 || us < best) {
+            best = us;
+            S = se;
+        }
+    }
     g.kbps = (KB + S - 1) / S;
     g.S = (KB + g.kbps - 1) / g.kbps;
 }

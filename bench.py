@@ -305,11 +305,14 @@ def main() -> int:
     dr.set_block_width(g)
     dr.set_sampling(temp, 0x5EED)
     tgt_all = torch.from_numpy(synth.integers(0, "bench.target", (W + K, B, g - 1), 0, shape.n_vocab)).to(dr.device)
-    il = ids_all[0].clone()
+    # per-step inputs side by side ([id_last (B) | target (B x (g-1))]), so one copy refreshes both
+    inputs_all = torch.cat([ids_all, tgt_all.reshape(W + K, B * (g - 1))], dim=1).contiguous()
+    inputs = inputs_all[0].clone()
+    il = inputs[:B]
+    target = inputs[B:].view(B, g - 1)
     npst = torch.tensor(n_pasts, dtype=torch.int32, device=dr.device)
     logits = torch.empty((16 * B, shape.n_vocab), dtype=torch.float32, device=dr.device)
     drafts = torch.empty((B, g - 1), dtype=torch.int32, device=dr.device)
-    target = tgt_all[0].clone()
     n_ok = torch.empty((B,), dtype=torch.int32, device=dr.device)
     stream = torch.cuda.Stream()
     graph = dr.capture_step(table, il, npst, logits, drafts, target, n_ok, stream=stream)
@@ -324,8 +327,7 @@ def main() -> int:
         def step(k):
             if T_inj:
                 inject_step(k)
-            il.copy_(ids_all[k])
-            target.copy_(tgt_all[k])
+            inputs.copy_(inputs_all[k])
             graph.launch(stream)
 
         for k in range(W):

@@ -174,6 +174,12 @@ def features(shape: Shape, T: int, feature_dtype: str, seed: int = 0, tag: str =
     return store(normal(seed, tag, (T, shape.feat_dim)), feature_dtype)
 
 
+def hidden(shape: Shape, T: int, seed: int = 0, tag: str = "hidden") -> np.ndarray:
+    """Encoded context rows ``[T, n_embd]`` float32 drawn N(0, 1): a direct input of the inject call (the
+    scale of an RMS-normed row), for workloads whose subject is not the encoder."""
+    return normal(seed, tag, (T, shape.n_embd))
+
+
 def step_inputs(shape: Shape, B: int, seed: int = 0, tag: str = "step") -> dict:
     """Per-step draws: id_last ~ U[0, V) and a planted mismatch index m ~ U{0..block-1}."""
     return {

@@ -414,6 +414,39 @@ def block_forward(cfg: Config, w: Weights, ring: Ring, block_ids, n_past: int, r
     return (logits, x) if return_hidden else logits
 
 
+def block_forward_batch(cfg: Config, w: Weights, rings, ids, n_pasts) -> np.ndarray:
+    """Logits [B, block, n_vocab] of B independent sequences.
+
+    metrale dflash_head.rs page, DflashBatch: the rows of all sequences go
+    through every weight projection together (sequence-major), while
+    attention runs per sequence against that sequence's own ring at its own
+    n_past. The operations are those of :func:`block_forward`; only the row
+    count of each matmul differs, and each weight matrix is decoded from its
+    storage form once for all rows.
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    B = ids.shape[0]
+    assert ids.shape == (B, cfg.block) and len(rings) == B and len(n_pasts) == B
+    freqs = inv_freq(cfg.rope_base, cfg.head_dim)
+    qpos = np.asarray(n_pasts, dtype=np.int64)[:, None] + np.arange(cfg.block)[None, :]  # [B, block]
+    D, H, Hkv, R = cfg.head_dim, cfg.n_head, cfg.n_head_kv, B * cfg.block
+    x = w.embed_rows(ids.reshape(-1))
+    for l in range(cfg.n_layer):
+        h = rmsnorm(x, w.layer(l, "attn_norm"), cfg.rms_eps)
+        q = linear(h, w.layer(l, "wq")).reshape(B, cfg.block, H, D)
+        k = linear(h, w.layer(l, "wk")).reshape(B, cfg.block, Hkv, D)
+        v = linear(h, w.layer(l, "wv")).reshape(B, cfg.block, Hkv, D)
+        q = rope(rmsnorm(q, w.layer(l, "q_norm"), cfg.rms_eps), qpos[:, :, None], freqs)
+        k = rope(rmsnorm(k, w.layer(l, "k_norm"), cfg.rms_eps), qpos[:, :, None], freqs)
+        o = np.concatenate([attention(cfg, rings[b], l, q[b], k[b], v[b], int(n_pasts[b])) for b in range(B)])
+        x = x + linear(o.reshape(R, H * D), w.layer(l, "wo"))
+        h2 = rmsnorm(x, w.layer(l, "ffn_norm"), cfg.rms_eps)
+        a = silu(linear(h2, w.layer(l, "w_gate"))) * linear(h2, w.layer(l, "w_up"))
+        x = x + linear(a, w.layer(l, "w_down"))
+    logits = linear(rmsnorm(x, w.glob("output_norm"), cfg.rms_eps), w.glob("lm_head"))
+    return logits.reshape(B, cfg.block, -1)
+
+
 def block_ids(cfg: Config, id_last: int) -> np.ndarray:
     """The noise block [id_last, mask x (block-1)] (dflash-ops card, Usage and Method)."""
     ids = np.full(cfg.block, cfg.mask_id, dtype=np.int64)

@@ -429,6 +429,23 @@ def test_block_forward_is_deterministic_and_fp8_uses_dequantised_weights():
     np.testing.assert_array_equal(w.layer(0, "w_up"), want)
 
 
+def test_batched_forward_equals_independent_sequences():
+    """Sequences of one batch are independent: each sequence's logits equal its own single-sequence forward,
+    whatever the other sequences hold (different rings, n_past and block ids), in any batch order."""
+    cfg, raw, w = _model(PIN, "bf16", "bf16")
+    n_pasts = [20, 3, 0, 37]
+    rings = [_filled_ring(cfg, w, n, seed=s)[0] if n else O.Ring(cfg) for s, n in enumerate(n_pasts)]
+    ids = np.array([[5 + b] + [0] * 15 for b in range(4)])
+    ids[3, 7] = 11  # a block with a non-mask id inside
+    got = O.block_forward_batch(cfg, w, rings, ids, n_pasts)
+    for b in range(4):
+        want = O.block_forward(cfg, w, rings[b], ids[b], n_pasts[b])
+        np.testing.assert_allclose(got[b], want, rtol=1e-12, atol=1e-12)
+    perm = [2, 0, 3, 1]
+    got_p = O.block_forward_batch(cfg, w, [rings[i] for i in perm], ids[perm], [n_pasts[i] for i in perm])
+    np.testing.assert_allclose(got_p, got[perm], rtol=1e-12, atol=1e-12)
+
+
 def test_greedy_drafts_skip_row_zero_and_break_ties_low():
     logits = np.zeros((16, 10))
     logits[0, 9] = 100  # row 0 is never drafted

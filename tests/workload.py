@@ -12,12 +12,12 @@ import numpy as np
 from block_diffusion_drafter_02_amd import synth
 from oracle import dflash_oracle as O
 
-# Tolerances. With fp32 storage the HIP path differs from the fp64 oracle only by fp32 rounding inside
-# its sums; a sum of n terms whose partial sums stay at the output's scale drifts like a random walk,
-# about u * sqrt(n) times that scale (u = 2^-24). The bars take that growth with a margin of 4 (ring
-# values, one contraction chain) or 16 (logits, the whole step's chain) and never go below the
-# small-shape bars 1e-5 / 1e-4. bf16 / fp8 storage rounds activations and keys on the way, so the
-# logit bar there is relative to the oracle logits' standard deviation.
+# Tolerances. Logits with fp32 storage (weights and ring) must be within 1e-4 absolute of the fp64
+# oracle: the bar the drafter's correctness statement fixes for fp32 storage. bf16 / fp8 storage rounds
+# weights and ring entries on the way, so there the logit bar is relative to the oracle logits' standard
+# deviation. Ring values: one contraction chain of fp32 sums (fc, then wk / wv) of n terms drifts like a
+# random walk, about u * sqrt(n) times the value's scale (u = 2^-24); the ring bar takes that growth with
+# a margin of 4 and never goes below 1e-5.
 LOGIT_ABS_F32 = 1e-4
 LOGIT_REL_STD = 2e-2
 RING_ABS_F32 = 1e-5
@@ -72,21 +72,14 @@ def inject_chain(shape) -> int:
     return shape.n_capture * shape.target_hidden + shape.n_embd
 
 
-def step_chain(shape) -> int:
-    """Terms summed on the way to one logit: injection, then per layer q/k/v, attention over the window,
-    wo, gate/up and down, then the lm_head."""
-    per_layer = shape.n_embd + shape.window + shape.n_head * shape.head_dim + shape.n_embd + shape.n_ff
-    return inject_chain(shape) + shape.n_layer * per_layer + shape.n_embd
-
-
 def ring_tol_f32(shape) -> float:
     return max(RING_ABS_F32, 4 * U32 * np.sqrt(inject_chain(shape)))
 
 
 def logit_tol(spec: Spec, ref: np.ndarray) -> float:
+    """Logit bar: 1e-4 absolute for fp32 weights and ring, else 2e-2 of the oracle logits' standard deviation."""
     if spec.weight_dtype == "f32" and spec.ring_dtype == "f32":
-        scale = max(1.0, float(np.std(ref)))
-        return max(LOGIT_ABS_F32, 16 * U32 * np.sqrt(step_chain(spec.shape)) * scale)
+        return LOGIT_ABS_F32
     return LOGIT_REL_STD * float(np.std(ref))
 
 

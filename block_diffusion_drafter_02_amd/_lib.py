@@ -75,6 +75,7 @@ SYMBOLS = {
     "dflash_pages_reset": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_void_p]),
     "dflash_step_path": (C.c_int32, [C.c_void_p, C.c_int32]),
     "dflash_check_device": (C.c_int, [C.c_void_p, C.c_void_p]),
+    "dflash_set_wait_limit": (C.c_int, [C.c_void_p, C.c_int64, C.c_void_p]),
     "dflash_last_error": (C.c_char_p, []),
 }
 

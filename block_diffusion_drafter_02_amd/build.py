@@ -9,7 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = ["api.hip", "kernels_weights.hip", "kernels_step.hip", "kernels_persistent.hip"]
+SOURCES = ["api.hip", "kernels_weights.hip", "kernels_step.hip", "kernels_chain.hip"]
 LIB = os.path.join(PKG, "libdflash.so")
 ARCH = os.environ.get("DFLASH_OFFLOAD_ARCH", "gfx950")
 

@@ -2,6 +2,7 @@
 // re-tiling at create time, and the orchestration of encode, inject, the block
 // step (optionally captured into a HIP graph) and the acceptance scan.
 #include <math.h>
+#include <stddef.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -135,28 +136,16 @@ void gemm_split(GemmArgs &g, int rows_cap) {
     g.S = (KB + g.kbps - 1) / g.kbps;
 }
 
-// Partial slots per column group of a chain phase with G groups of KB k-blocks
-// each. The phase's n = min(workgroups, G*KB) <= PSTEP_MAX_WG workgroups own
-// contiguous runs of at least m = floor(G*KB / n) >= 1 k-blocks, so a group
-// meets at most ceil((KB - 1) / m) + 1 <= min(KB, 2 ceil(n / G)) + 2 of them
-// (m >= G*KB / (2n) when G*KB >= n). prepare_chain checks the exact counts.
-int pchain_pmax(int G, int KB) {
-    const int c = 2 * ((PSTEP_MAX_WG + G - 1) / G);
-    return std::min(KB, c) + 2;
+// k-splits of a chain phase with G column groups of KB k-blocks when nwg workgroups each take one item
+// (a group and a k-split) of every phase: as many as keep G * S <= nwg.
+int chain_split(int G, int KB, int nwg) {
+    const int s = std::max(1, std::min(KB, nwg / G));
+    const int kbps = (KB + s - 1) / s;
+    return (KB + kbps - 1) / kbps;
 }
 
-// Largest number of workgroups that share one column group of a chain phase with nwg workgroups (exact).
-int pchain_pieces(int G, int KB, int nwg) {
-    const long long U = (long long)G * KB;
-    const long long n = std::min<long long>(nwg, U);
-    int worst = 0;
-    for (int g = 0; g < G; ++g) {
-        const long long u0 = (long long)g * KB, u1 = u0 + KB - 1;
-        const long long w0 = ((u0 + 1) * n - 1) / U, w1 = ((u1 + 1) * n - 1) / U;
-        worst = std::max(worst, (int)(w1 - w0 + 1));
-    }
-    return worst;
-}
+// Most workgroups a chain launch uses (sizes the chain's partial buffers).
+constexpr int CHAIN_MAX_WG = 2048;
 
 struct Carver {
     char *base;
@@ -251,19 +240,23 @@ size_t carve(dflash_ctx &x, char *base) {
     x.inj_act = act_fmt == ACT_SPLIT3 ? cv.take<void>(6ull * T * E) : nullptr;
     x.inj_kv = cv.take<float>(4ull * T * L * 2 * kvdim);
 
-    // persistent chain: partial slots for the most workgroups a launch may have
+    // dataflow chain: split-K partials and counters per phase slot for the most workgroups a launch may
+    // have; then the epoch, the sticky error word, the argmax counter and the done flags
     x.x2 = cv.take<float>(4ull * Mmax * E);
-    x.pargs = cv.take<PStepArgs>(sizeof(PStepArgs));
-    size_t ppmax = 0;
-    int pgmax = 0;
-    for (auto &sh : shapes) {
-        const int Gn = sh[0] / (GROUP_N * sh[2]), KBn = sh[1] / KBLK;
-        ppmax = std::max(ppmax, (size_t)Gn * pchain_pmax(Gn, KBn) * 16 * GROUP_N * sh[2]);
-        pgmax = std::max(pgmax, Gn);
+    x.cargs = cv.take<ChainArgs>(sizeof(ChainArgs));
+    {
+        const int slot_shape[CS_N][2] = {{nqkv, E}, {E, qdim}, {2 * F, E}, {E, F}, {V, E}};
+        size_t pf = 0;
+        int cnt = 0;
+        for (auto &sh : slot_shape) {
+            const int Gn = sh[0] / GROUP_N, KBn = sh[1] / KBLK;
+            pf += a256(4ull * chain_split(Gn, KBn, CHAIN_MAX_WG) * Gn * 16 * GROUP_N) / 4;
+            cnt += Gn;
+        }
+        x.cpartial = cv.take<float>(4 * pf);
+        x.n_csync = 4 + cnt + G_E + L * (G_E + 2 * F / GROUP_N + G_E);
+        x.csync = cv.take<int>(4ull * x.n_csync);
     }
-    x.ppartial = cv.take<float>(4 * ppmax);
-    x.n_psync = 4 + pgmax;
-    x.psync = cv.take<int>(4ull * x.n_psync);
     // split partials of the batched projections (16*B rows, B > 1)
     x.bpartial = nullptr;
     if (c.max_batch > 1) {
@@ -389,19 +382,20 @@ int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
     TRY(tile_scales(w->s_lm_head, V, x.s_lm, 0, 0, 0, s));
     HIP_TRY(launch_fill_i32(x.counters, 0, x.n_counters, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.am_counter, 0, 1, s), "counter reset");
-    HIP_TRY(launch_fill_i32(x.psync, 0, x.n_psync, s), "counter reset");
+    HIP_TRY(launch_fill_i32(x.csync, 0, x.n_csync, s), "counter reset");
+    HIP_TRY(launch_fill_i32(x.csync, 1, 1, s), "epoch reset");  // epoch 1: flags hold 0 until first set
     return prepare_chain(x, s);
 }
 
-// Arguments of the persistent chain, kept in the workspace for the life of the context.
+// Arguments of the dataflow chain, kept in the workspace for the life of the context.
 int prepare_chain(dflash_ctx &x, hipStream_t s) {
-    x.pchain_wg = 0;
+    x.chain_wg = 0;
     x.path = DFLASH_PATH_AUTO;
-    const int nwg = pchain_grid(&x);
+    const int nwg = std::min(chain_grid(&x), CHAIN_MAX_WG);
     if (nwg < 1) return DFLASH_OK;  // the per-launch kernels serve every step
     int rate_khz = 0;
     HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, x.device), "wall clock rate query");
-    PStepArgs a = {};
+    ChainArgs a = {};
     a.L = x.L;
     a.E = x.E;
     a.F = x.F;
@@ -409,7 +403,6 @@ int prepare_chain(dflash_ctx &x, hipStream_t s) {
     a.D = x.D;
     a.nqkv = x.nqkv;
     a.qdim = x.qdim;
-    a.kvdim = x.kvdim;
     a.G_E = x.G_E;
     a.block = x.cfg.block;
     a.mask_id = x.cfg.mask_id;
@@ -418,17 +411,14 @@ int prepare_chain(dflash_ctx &x, hipStream_t s) {
     a.act_rows = x.Mmax;
     a.eps = x.cfg.rms_eps;
     a.inv_E = 1.0f / (float)x.E;
-    a.qscale = 1.0f / sqrtf((float)x.D);
     a.tok_embd = x.tok_embd;
     a.inv_freq = x.inv_freq;
     a.attn_norm = x.attn_norm;
     a.ffn_norm = x.ffn_norm;
-    a.q_norm = x.q_norm;
-    a.k_norm = x.k_norm;
     a.output_norm = x.output_norm;
     for (int l = 0; l < x.L; ++l) {
         const LayerBufs &b = x.layer[l];
-        a.layer[l] = PLayer{b.qkv, b.o, b.gu, b.down, b.s_qkv, b.s_o, b.s_gu, b.s_down};
+        a.layer[l] = ChainLayer{b.qkv, b.o, b.gu, b.down, b.s_qkv, b.s_o, b.s_gu, b.s_down};
     }
     a.lm = x.lm;
     a.s_lm = x.s_lm;
@@ -443,35 +433,44 @@ int prepare_chain(dflash_ctx &x, hipStream_t s) {
     a.qkv_out = x.qkv_out;
     a.rope_cs = x.rope_cs;
     a.ss_stride = x.Mmax;
-    a.partial = x.ppartial;
-    const int phase_g[5] = {x.nqkv / (GROUP_N * QKV_WN), x.E / GROUP_N, 2 * x.F / GROUP_N, x.E / GROUP_N,
-                            x.V / GROUP_N};
-    const int phase_kb[5] = {x.E / KBLK, x.qdim / KBLK, x.E / KBLK, x.F / KBLK, x.E / KBLK};
-    for (int i = 0; i < 5; ++i) {
-        a.pmax[i] = pchain_pmax(phase_g[i], phase_kb[i]);
-        if (pchain_pieces(phase_g[i], phase_kb[i], nwg) > a.pmax[i])
-            return fail(DFLASH_EHIP, "internal: chain partial slots too few (phase %d)", i);
+    const int slot_shape[CS_N][2] = {{x.nqkv, x.E}, {x.E, x.qdim}, {2 * x.F, x.E}, {x.E, x.F}, {x.V, x.E}};
+    float *pp = x.cpartial;
+    int *sync = x.csync;
+    a.epoch = (unsigned *)sync;
+    a.err = sync + 1;
+    a.am_counter = sync + 2;
+    int *cnt = sync + 4;
+    for (int i = 0; i < CS_N; ++i) {
+        const int Gn = slot_shape[i][0] / GROUP_N, KBn = slot_shape[i][1] / KBLK;
+        a.S[i] = x.chain_S[i] = chain_split(Gn, KBn, nwg);
+        a.partial[i] = pp;
+        pp += a256(4ull * chain_split(Gn, KBn, CHAIN_MAX_WG) * Gn * 16 * GROUP_N) / 4;
+        a.counters[i] = cnt;
+        cnt += Gn;
+        if (a.S[i] > chain_split(Gn, KBn, CHAIN_MAX_WG) || (size_t)Gn * a.S[i] > (size_t)nwg)
+            return fail(DFLASH_EHIP, "internal: chain split of phase slot %d does not fit", i);
     }
+    a.done_embed = cnt;
+    a.done_o = a.done_embed + x.G_E;
+    a.done_gu = a.done_o + (size_t)x.L * x.G_E;
+    a.done_down = a.done_gu + (size_t)x.L * (2 * x.F / GROUP_N);
+    if (a.done_down + (size_t)x.L * x.G_E != x.csync + x.n_csync)
+        return fail(DFLASH_EHIP, "internal: chain flag layout");
     a.am_val = x.am_val;
     a.am_idx = x.am_idx;
-    a.bar = (unsigned *)x.psync;
-    a.err = x.psync + 1;
-    a.am_counter = x.psync + 2;
-    a.counters = x.psync + 4;
     a.spin_ticks = (long long)rate_khz * 1000;  // one second
-    HIP_TRY(hipMemcpyAsync(x.pargs, &a, sizeof a, hipMemcpyHostToDevice, s), "chain argument upload");
+    HIP_TRY(hipMemcpyAsync(x.cargs, &a, sizeof a, hipMemcpyHostToDevice, s), "chain argument upload");
     HIP_TRY(hipStreamSynchronize(s), "chain argument upload");
-    x.pchain_wg = nwg;
+    x.chain_wg = nwg;
     return DFLASH_OK;
 }
 
-// DFLASH_PATH_AUTO takes the per-launch kernels: on MI355X at the real drafter
-// dimensions the persistent chain's 768 resident workgroups stream the weights
-// more slowly than the per-launch grids (the third workgroup of every CU lags,
-// and every phase waits for the slowest), so it stays an explicit choice.
+// DFLASH_PATH_AUTO takes the per-launch kernels: measured on MI355X at the real drafter dimensions, the
+// dataflow chain overlaps each projection's tail with the next one's weight stream, but the handshakes,
+// epilogues and flags on its critical path then queue behind that stream, and the chain launch ends up
+// slower than the kernels it replaces; it stays an explicit choice.
 bool use_chain(const dflash_ctx &x, int B) {
-    if (B != 1 || x.pchain_wg < 1 || x.gamma != x.cfg.block || x.temp > 0.0f) return false;
-    return x.path == DFLASH_PATH_PERSISTENT;
+    return B == 1 && x.chain_wg >= 1 && x.path == DFLASH_PATH_PERSISTENT;
 }
 
 EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
@@ -627,13 +626,13 @@ int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const in
              const int32_t *n_past, int B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
              hipStream_t s) {
     if (use_chain(x, B)) {
-        // persistent chain: embed + q/k/v(0); per layer attention, combine, then Wo .. q/k/v(l+1) or lm_head
-        const PStepIO io{id_last, block_ids, n_past, logits, drafts, target, n_ok};
-        HIP_TRY(launch_fill_i32(x.psync, 0, x.n_psync, s), "chain counter reset");
-        HIP_TRY(launch_pchain_head(&x, x.pargs, io, x.pchain_wg, s), "chain launch");
+        // dataflow chain: head (embed + q/k/v of layer 0); per layer attention, then Wo .. q/k/v(l+1) or lm_head
+        ChainIO io{id_last, block_ids, n_past, logits, drafts, target, n_ok, x.gamma, x.temp, (uint32_t)x.seed,
+                   (uint32_t)(x.seed >> 32)};
+        HIP_TRY(launch_chain_head(&x, io, s), "chain head launch");
         for (int l = 0; l < x.L; ++l) {
             HIP_TRY(launch_attention(&x, l, rings, n_past, B, s), "attention launch");
-            HIP_TRY(launch_pchain_layer(&x, x.pargs, io, l, 1 + 3 * l, x.pchain_wg, s), "chain launch");
+            HIP_TRY(launch_chain_layer(&x, io, l, s), "chain launch");
         }
         x.last_B = B;
         return DFLASH_OK;
@@ -952,8 +951,8 @@ int dflash_set_path(dflash_ctx *x, int32_t path) {
     if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
     if (path != DFLASH_PATH_AUTO && path != DFLASH_PATH_KERNELS && path != DFLASH_PATH_PERSISTENT)
         return fail(DFLASH_EINVAL, "unknown path %d", path);
-    if (path == DFLASH_PATH_PERSISTENT && x->pchain_wg < 1)
-        return fail(DFLASH_EUNSUPPORTED, "the persistent chain is not available for this configuration");
+    if (path == DFLASH_PATH_PERSISTENT && x->chain_wg < 1)
+        return fail(DFLASH_EUNSUPPORTED, "the dataflow chain is not available for this configuration");
     x->path = path;
     return DFLASH_OK;
 }
@@ -965,14 +964,35 @@ int32_t dflash_step_path(const dflash_ctx *x, int32_t B) {
 
 int dflash_check_device(dflash_ctx *x, void *stream) {
     if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
-    HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(hipStreamSynchronize(s), "hipStreamSynchronize");
     int err = 0;
-    HIP_TRY(hipMemcpy(&err, x->psync + 1, sizeof err, hipMemcpyDeviceToHost), "device status read");
+    HIP_TRY(hipMemcpy(&err, x->csync + 1, sizeof err, hipMemcpyDeviceToHost), "device status read");
     if (err) {
-        HIP_TRY(hipMemset(x->psync + 1, 0, sizeof err), "device status reset");
-        return fail(DFLASH_ESTATE, "a grid barrier of the persistent chain gave up waiting; that step's outputs "
-                                   "are invalid");
+        // a step gave up a wait: its flags and split-K counters may be left mid-way, so clear them all
+        // (epoch back to 1) before the next step
+        HIP_TRY(launch_fill_i32(x->csync, 0, x->n_csync, s), "chain state reset");
+        HIP_TRY(launch_fill_i32(x->csync, 1, 1, s), "chain state reset");
+        HIP_TRY(launch_fill_i32(x->counters, 0, x->n_counters, s), "counter reset");
+        HIP_TRY(hipStreamSynchronize(s), "chain state reset");
+        return fail(DFLASH_ESTATE, "a bounded wait of the dataflow chain gave up; the outputs of the steps since "
+                                   "the last check are invalid");
     }
+    return DFLASH_OK;
+}
+
+int dflash_set_wait_limit(dflash_ctx *x, int64_t microseconds, void *stream) {
+    if (!x) return fail(DFLASH_EINVAL, "ctx is NULL");
+    if (microseconds < 0) return fail(DFLASH_EINVAL, "wait limit must be >= 0");
+    if (x->chain_wg < 1) return fail(DFLASH_EUNSUPPORTED, "the dataflow chain is not available for this configuration");
+    int rate_khz = 0;
+    HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, x->device), "wall clock rate query");
+    const long long ticks = (long long)((double)microseconds * rate_khz / 1000.0);
+    hipStream_t s = (hipStream_t)stream;
+    HIP_TRY(hipMemcpyAsync((char *)x->cargs + offsetof(ChainArgs, spin_ticks), &ticks, sizeof ticks,
+                           hipMemcpyHostToDevice, s),
+            "wait limit upload");
+    HIP_TRY(hipStreamSynchronize(s), "wait limit upload");
     return DFLASH_OK;
 }
 

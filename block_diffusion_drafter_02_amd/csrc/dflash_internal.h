@@ -289,7 +289,7 @@ struct LayerBufs {
     float *s_qkv, *s_o, *s_gu, *s_down;  // fp8 scales in tiled column order (or null)
 };
 
-struct PStepArgs;  // persistent chain arguments (below)
+struct ChainArgs;  // dataflow chain arguments (below)
 
 // Paged drafter KV: a page holds PAGE_SLOTS ring slots of every layer in the
 // ring layout (K, V, slot_pos); a sequence's ring is then a block table of
@@ -356,77 +356,93 @@ struct dflash_ctx {
     void *enc_act;      // features converted for the fc GEMM (if needed)
     void *inj_act;      // h converted for the kv GEMM (if needed)
     float *inj_kv;      // [max_inject][L*2*kvdim]
-    // persistent chain (one sequence per step)
+    // dataflow chain (one sequence per step)
     float *x2;          // second residual buffer [Mmax][E]
-    PStepArgs *pargs;   // device copy of the chain arguments
-    float *ppartial;    // stream-K partial tiles
-    int *psync;         // [bar, err, lm argmax counter, pad, group counters...]
-    int n_psync;
+    ChainArgs *cargs;   // device copy of the chain arguments
+    float *cpartial;    // split-K partial tiles, one region per phase slot
+    int *csync;         // [epoch, sticky error, argmax counter, pad, split-K counters..., done flags...]
+    int n_csync;        // ints of csync cleared at create and after a reported failure
+    int chain_wg;       // workgroups per chain launch (0: chain unavailable)
+    int chain_S[5];     // k-splits of the chain's q/k/v, Wo, gate/up, down and lm_head phases
     float *bpartial;    // split partials of the batched projections (null when max_batch == 1)
-    int pchain_wg;      // workgroups per chain launch (0: chain unavailable)
     int path;           // DFLASH_PATH_*
 };
 
 // ---------------------------------------------------------------------------
-// Persistent weight-streaming chain (kernels_persistent.hip)
+// Dataflow chain of the block step (kernels_chain.hip)
 // ---------------------------------------------------------------------------
-// The block step of one sequence with persistent weight-streaming kernels:
-// embed + q/k/v of layer 0 is one launch; then per layer l the attention and
-// combine kernels, and one launch of Wo, gate/up, down and the q/k/v of layer
-// l + 1 (or the lm_head), whose phases are separated by grid-wide barriers.
-constexpr int PSTEP_MAX_LAYERS = 16;
-constexpr int PSTEP_MAX_WG = 2048;  // workgroups per launch at most (sizes the partial buffer)
+// The block step of one sequence as 2L + 1 launches: a head launch (embedding
+// and the q/k/v projection of layer 0), then per layer the attention launch and
+// one chain launch of Wo, gate/up, down and the next layer's q/k/v (or the
+// lm_head). A chain launch runs exactly as many 256-thread workgroups as the
+// GPU holds at once; workgroup w takes item w of every phase (a column group
+// and k-split of that projection). Instead of waiting for a whole phase, an
+// item first issues the weight loads of its first k-block, then waits only for
+// the producer column groups of its own k-slice; the epilogue waits for all
+// producer groups when it needs their norm statistics. Every column group
+// publishes a done flag that holds the step's epoch; the lm_head's last
+// workgroup advances the epoch at the end of the step, so flags never need
+// clearing. All waits are bounded in wall-clock time and raise a sticky error
+// word that only dflash_check_device clears.
+constexpr int CHAIN_MAX_LAYERS = 16;
+constexpr int CHAIN_THREADS = 256;
 
-struct PLayer {
+struct ChainLayer {
     const void *qkv, *o, *gu, *down;          // tiled weights
     const float *s_qkv, *s_o, *s_gu, *s_down;  // fp8 column scales (tiled order) or null
 };
 
+// Phase slots of the chain (each with its own split-K partials and counters).
+enum ChainSlot { CS_QKV = 0, CS_O = 1, CS_GU = 2, CS_DOWN = 3, CS_LM = 4, CS_N = 5 };
+
 // Lives in device memory for the life of the context.
-struct PStepArgs {
-    int L, E, F, V, D, nqkv, qdim, kvdim, G_E, block;
+struct ChainArgs {
+    int L, E, F, V, D, nqkv, qdim, G_E, block;
     int mask_id, aux_dtype, act_fmt, act_rows;
-    float eps, inv_E, qscale;
+    float eps, inv_E;
     const void *tok_embd;
     const double *inv_freq;
-    const float *attn_norm, *ffn_norm, *q_norm, *k_norm, *output_norm;
-    PLayer layer[PSTEP_MAX_LAYERS];
+    const float *attn_norm, *ffn_norm, *output_norm;
+    ChainLayer layer[CHAIN_MAX_LAYERS];
     const void *lm;
     const float *s_lm;
-    // activations (the per-launch path's buffers plus a second residual buffer)
     float *x, *x2;
     void *act_a, *act_f, *act_d, *act_o;
     float *ss_a, *ss_f, *qkv_out, *rope_cs;
     int ss_stride;
-    float *partial;     // stream-K partial tiles
-    int *counters;      // [max groups], zero between phases
-    int pmax[5];        // partial slots per column group: q/k/v, Wo, gate/up, down, lm_head
+    int S[CS_N];              // k-splits per phase slot
+    float *partial[CS_N];     // [S][G][16*64] per phase slot
+    int *counters[CS_N];      // [G] split-K arrival counters per phase slot (zero between uses)
+    // done flags: the embedding's column groups, then per layer those of Wo, gate/up and down (the q/k/v
+    // and lm_head outputs are read only by later launches)
+    int *done_embed;          // [G_E]
+    int *done_o, *done_gu, *done_down;  // [L][groups of that projection]
     float *am_val;
     int *am_idx;
     int *am_counter;
-    unsigned *bar;      // grid barrier counter, zeroed at the start of every step
-    int *err;           // set when a barrier wait gives up
+    unsigned *epoch;          // the step's flag value; advanced by the step's last workgroup
+    int *err;                 // sticky: a bounded wait gave up
     long long spin_ticks;
 };
 
-// Step inputs and outputs of one call (one sequence), passed by value.
-struct PStepIO {
+// Per-call inputs and outputs and per-ctx step settings, passed by value.
+struct ChainIO {
     const int32_t *id_last, *block_ids, *n_past;
     float *logits;
     int32_t *drafts;
     const int32_t *target;
     int32_t *n_ok;
+    int gamma;
+    float temp;
+    uint32_t seed_lo, seed_hi;
 };
 
-// Workgroups per launch of the chain kernels for this configuration (0: not available).
-int pchain_grid(const dflash_ctx *c);
-// Embed + q/k/v of layer 0 (one grid barrier).
-hipError_t launch_pchain_head(const dflash_ctx *c, const PStepArgs *dev_args, const PStepIO &io, int nWG,
-                              hipStream_t s);
-// Wo, gate/up, down of layer l and the q/k/v of layer l + 1 or the lm_head (three grid barriers);
-// bar_base = grid barriers passed earlier in the step.
-hipError_t launch_pchain_layer(const dflash_ctx *c, const PStepArgs *dev_args, const PStepIO &io, int l,
-                               unsigned bar_base, int nWG, hipStream_t s);
+// Workgroups per chain launch for this configuration (0: not available).
+int chain_grid(const dflash_ctx *c);
+// Embedding, the block's rope table and the q/k/v projection of layer 0.
+hipError_t launch_chain_head(const dflash_ctx *c, const ChainIO &io, hipStream_t s);
+// Wo, gate/up and down of layer l, then the q/k/v projection of layer l + 1 or the lm_head.
+hipError_t launch_chain_layer(const dflash_ctx *c, const ChainIO &io, int l, hipStream_t s);
 
 struct dflash_graph {
     dflash_ctx *ctx;

@@ -1,8 +1,8 @@
 // Device code shared by the weight-streaming kernels: operand loading of the
 // tiled weights and lane-ordered activations, the per-tile MFMA step, the
 // fixed-order reduction of a workgroup's waves, the split-K handshake and the
-// fused epilogues. Included by the per-launch kernels and by the persistent
-// whole-step kernel.
+// fused epilogues. Included by the per-launch kernels and by the dataflow
+// chain.
 #pragma once
 
 #include "dflash_internal.h"
@@ -32,12 +32,15 @@ struct WTraits<DFLASH_FP8_E4M3> {
 // ---------------------------------------------------------------------------
 // Operand loading and the per-tile MFMA step
 // ---------------------------------------------------------------------------
+// Weights are read exactly once per step, so their loads are non-temporal: they do not displace the
+// activations, partial sums and ring entries that the caches hold for the rest of the step (measured on
+// the real-dimension bf16 step: gate/up 104.7 -> 97.0 us, step 1176 -> 1108 us).
 template <int WT>
 __device__ __forceinline__ void load_wtile(const void *W, size_t tile_index, int lane, u32x4 (&w)[WTraits<WT>::NV]) {
     constexpr int NV = WTraits<WT>::NV;
     const u32x4 *p = (const u32x4 *)W + tile_index * NV * 64 + lane;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) w[v] = p[v * 64];
+    for (int v = 0; v < NV; ++v) w[v] = __builtin_nontemporal_load(p + v * 64);
 }
 
 // 16 bf16 values of one lane as two MFMA operands

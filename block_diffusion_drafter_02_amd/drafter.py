@@ -305,8 +305,12 @@ class Drafter:
         return int(lib().dflash_step_path(self._ctx, B))
 
     def check_device(self, stream=None) -> None:
-        """Raise if a persistent-path step gave up at a grid barrier since the last check."""
+        """Raise if a dataflow-chain wait gave up since the last check (the error is then cleared)."""
         check(lib().dflash_check_device(self._ctx, _stream(stream)))
+
+    def set_wait_limit(self, microseconds: int, stream=None) -> None:
+        """Wall-clock limit of each bounded wait of the dataflow chain (a test and tuning hook)."""
+        check(lib().dflash_set_wait_limit(self._ctx, int(microseconds), _stream(stream)))
 
     def replay_stage(self, stage: int, layer: int = 0, stream=None) -> None:
         """Re-run one weight-streaming stage of the last block step (a single-kernel timing hook)."""

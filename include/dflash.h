@@ -210,19 +210,27 @@ int dflash_quantize_fp8_rows(const float *w, int32_t rows, int32_t cols, uint8_t
                              void *stream);
 
 /* How a block step runs. DFLASH_PATH_KERNELS: one kernel per projection,
- * attention and combine (about six per layer). DFLASH_PATH_PERSISTENT: for a
- * single sequence (B == 1), the weight-streaming projections of a layer run
- * as one launch of a persistent kernel sized to the GPU (Wo, gate/up, down and
- * the next layer's q/k/v or the lm_head), with grid-wide barriers between
- * them; attention and combine stay separate kernels. Both paths compute the
- * same operations with the same operand splits; their reductions split at
+ * attention and combine (about six per layer). DFLASH_PATH_PERSISTENT, for a
+ * single sequence (B == 1): the dataflow chain, 2 * n_layer + 1 launches (the
+ * embedding with layer 0's q/k/v; per layer the attention, then one launch of
+ * Wo, gate/up, down and the next q/k/v or the lm_head). A chain launch holds
+ * as many workgroups as the GPU runs at once; each takes one column group and
+ * k-split of every projection in turn, issues its first weight loads, and
+ * waits only for the column groups that produce its slice of the input
+ * (per-group done flags), so one projection's tail overlaps the next one's
+ * weight stream. These waits are bounded in time (one second unless
+ * dflash_set_wait_limit says otherwise); a wait that gives up raises a sticky
+ * error that dflash_check_device reports. The dflash-ops card (Requirements
+ * and limits) names a fused whole-block persistent kernel as not implemented
+ * there; this is this library's form of it. Both paths compute the same
+ * operations with the same operand splits; their reductions may split at
  * different points, so results agree to fp32 rounding. DFLASH_PATH_AUTO (the
  * default) takes the faster path measured for this library, currently the
  * per-launch kernels. */
 typedef enum { DFLASH_PATH_AUTO = 0, DFLASH_PATH_KERNELS = 1, DFLASH_PATH_PERSISTENT = 2 } dflash_path;
 
 /* Choose the path of later block steps (and of graphs captured later).
- * EUNSUPPORTED for DFLASH_PATH_PERSISTENT when the persistent kernel does not
+ * EUNSUPPORTED for DFLASH_PATH_PERSISTENT when the dataflow chain does not
  * fit this configuration or device. */
 int dflash_set_path(dflash_ctx *ctx, int32_t path);
 
@@ -230,9 +238,8 @@ int dflash_set_path(dflash_ctx *ctx, int32_t path);
  * block_g / set_block_g and its per-width propose graphs): later block steps,
  * acceptance scans and graph captures use g tokens [id_last, mask x (g-1)]
  * and g-1 drafts. g is clamped into 2..block (16). A graph keeps the width it
- * was captured with. The persistent path runs full-width blocks only; at
- * g < 16 a step takes the per-launch kernels. dflash_block_width returns the
- * width in use (0 for a NULL ctx). */
+ * was captured with. dflash_block_width returns the width in use (0 for a
+ * NULL ctx). */
 int dflash_set_block_width(dflash_ctx *ctx, int32_t g);
 int32_t dflash_block_width(const dflash_ctx *ctx);
 
@@ -244,7 +251,7 @@ int32_t dflash_block_width(const dflash_ctx *ctx);
  * (Salmon et al., SC 2011) at counter (n_past[b] + i, vocab id, b, 0) under key
  * (seed & 0xffffffff, seed >> 32); ties to the lowest index. The logits output
  * stays the unperturbed logits. temperature must be finite and >= 0 (0:
- * greedy), else DFLASH_EINVAL. Sampling steps take the per-launch kernels. */
+ * greedy), else DFLASH_EINVAL. */
 int dflash_set_sampling(dflash_ctx *ctx, float temperature, uint64_t seed);
 
 /* Paged drafter KV (metrale dflash_head.rs page, DflashBatch: a drafter block
@@ -270,11 +277,21 @@ int dflash_pages_reset(dflash_ctx *ctx, int32_t first, int32_t count, void *stre
  * sequences takes now; -1 for a NULL ctx. */
 int32_t dflash_step_path(const dflash_ctx *ctx, int32_t B);
 
-/* Synchronise `stream` and report whether a persistent-path step gave up at
- * a grid barrier since the last check (a barrier waits at most one second,
- * e.g. when other work holds compute units): ESTATE if so, after which the
- * flag is cleared; that step's outputs are invalid. OK otherwise. */
+/* Synchronise `stream` and report whether a dataflow-chain wait gave up since
+ * the last check (e.g. when other work holds compute units so that not every
+ * chain workgroup is resident): ESTATE if so. The error word is sticky: every
+ * chain step after the failing one also gives up its waits at once and leaves
+ * invalid outputs, until this call reports the error, clears it and resets the
+ * chain's flags and counters, after which steps are valid again. OK
+ * otherwise. */
 int dflash_check_device(dflash_ctx *ctx, void *stream);
+
+/* Wall-clock limit of each bounded wait of the dataflow chain, in
+ * microseconds (default 1000000). A test and tuning hook: a limit of 0 makes
+ * every wait that is not satisfied at once give up, so failure handling can be
+ * exercised with every kernel ending normally. Synchronises `stream`.
+ * EUNSUPPORTED when the chain is not available. */
+int dflash_set_wait_limit(dflash_ctx *ctx, int64_t microseconds, void *stream);
 
 /* Stages of the block step that dflash_replay_stage can re-run. */
 typedef enum {

@@ -124,15 +124,31 @@ def test_per_width_graphs_replay_their_own_width(gpu):
     dr.set_block_width(16)
 
 
-def test_persistent_path_falls_back_below_full_width(gpu):
+def test_chain_serves_every_block_width_like_the_kernels(gpu):
+    """The dataflow chain runs steps of any block width; its logits rows 0..g-1 and drafts agree with the
+    per-launch kernels' at the same width."""
+    torch = _torch()
     spec = WL.Spec(synth.TINY, "bf16", "bf16", "bf16")
     dr, ring, fdev, _, raw, feats = _build(spec, 80)
-    dr.set_path(2)  # DFLASH_PATH_PERSISTENT
-    assert dr.step_path(1) == 2
-    dr.set_block_width(6)
-    assert dr.step_path(1) == 1  # the per-launch kernels
+    table = dr.ring_table([ring])
+    il = torch.tensor([17], dtype=torch.int32, device=dr.device)
+    npst = torch.tensor([80], dtype=torch.int32, device=dr.device)
+    for g in (6, 16):
+        dr.set_block_width(g)
+        out = {}
+        for path in (2, 1):  # DFLASH_PATH_PERSISTENT, DFLASH_PATH_KERNELS
+            dr.set_path(path)
+            assert dr.step_path(1) == path
+            print(f"[case] width {g} path {path}", flush=True)
+            logits, drafts = dr.block_step(table, il, npst)
+            torch.cuda.synchronize()
+            out[path] = (logits[:g].cpu().numpy().astype(np.float64), drafts.cpu().numpy())
+        dr.check_device()
+        tol = WL.LOGIT_ABS_F32 * max(1.0, float(np.std(out[1][0])))
+        assert np.abs(out[2][0] - out[1][0]).max() <= tol
+        np.testing.assert_array_equal(out[2][1], out[1][1])
     dr.set_block_width(16)
-    assert dr.step_path(1) == 2
+    dr.set_path(0)
 
 
 @pytest.mark.parametrize("g", [16, 5])

@@ -51,6 +51,7 @@ SYMBOLS = {
     "dflash_destroy": (None, [C.c_void_p]),
     "dflash_ring_reset": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "dflash_encode": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
+    "dflash_encode_static": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
     "dflash_inject": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p]),
     "dflash_block_step": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
                                     C.c_void_p, C.c_void_p]),

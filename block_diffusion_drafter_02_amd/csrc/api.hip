@@ -7,9 +7,16 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "dflash_internal.h"
+
+// Scratch of the allocation-free encode (dflash_encode_static): one array per GPU the library runs on,
+// allocated with the code object and held until the process ends. Host code never passes this name to a
+// kernel: it holds a host-side stand-in; the array's device address comes from hipGetSymbolAddress.
+constexpr size_t ENCODE_STATIC_SCRATCH_BYTES = 64ull << 20;
+static __device__ __align__(256) unsigned char scratch[ENCODE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -36,6 +43,24 @@ int hip_fail(hipError_t e, const char *what) {
     } while (0)
 
 size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Device address of `scratch` on each device, looked up once per device with that device current.
+std::mutex g_scratch_mu;
+constexpr int MAX_DEVICES = 64;
+void *g_scratch_dev[MAX_DEVICES];
+
+int bind_static_scratch(int device, void **out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (device < 0 || device >= MAX_DEVICES) return fail(DFLASH_EUNSUPPORTED, "device %d outside 0..%d", device, MAX_DEVICES - 1);
+    if (g_scratch_dev[device] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return fail(DFLASH_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_dev[device] = p;
+    }
+    *out = g_scratch_dev[device];
+    return DFLASH_OK;
+}
 
 // the q/k/v projection streams 64-column groups like every other projection
 // (its per-head RMSNorm and rope run in the attention kernel)
@@ -708,6 +733,10 @@ int dflash_create(const dflash_config *cfg, const dflash_weights *w, void *works
         delete x;
         return hip_fail(e, "hipGetDevice / compute unit count");
     }
+    if (bind_static_scratch(x->device, &x->static_scratch) != DFLASH_OK) {
+        delete x;
+        return DFLASH_EHIP;
+    }
     e = attention_set_smem_limit();
     if (e == hipSuccess) e = gemm_set_smem_limit();
     if (e != hipSuccess) {
@@ -771,43 +800,75 @@ int dflash_pages_reset(dflash_ctx *x, int32_t first, int32_t count, void *stream
     return DFLASH_OK;
 }
 
-int dflash_encode(dflash_ctx *x, const void *feats, int32_t T, float *h, void *stream) {
-    if (!x || !feats || !h) return fail(DFLASH_EINVAL, "ctx, feats or h is NULL");
-    if ((uintptr_t)feats % 16 || (uintptr_t)h % 16) return fail(DFLASH_EINVAL, "feats and h must be 16-byte aligned");
-    if (T < 1 || T > x->cfg.max_inject) return fail(DFLASH_ERANGE, "T=%d outside 1..max_inject=%d", T, x->cfg.max_inject);
-    hipStream_t s = (hipStream_t)stream;
-    const dflash_config &c = x->cfg;
+// Encode with caller-chosen scratch: `stage` holds the converted features (term planes of stage_rows
+// rows) when the feature and fc dtypes need a conversion, `parts` the split-K partials [S][T][E] of the fc
+// GEMM in at most parts_rows rows of E floats.
+int encode_with(dflash_ctx &x, const void *feats, int T, float *h, hipStream_t s, void *stage, int stage_rows,
+                float *parts, int parts_rows) {
+    const dflash_config &c = x.cfg;
     const void *act = feats;
     int fmt;
     int act_rows = T;
     if (c.aux_dtype == DFLASH_F32) {
         fmt = ACT_F32;
         if (c.feature_dtype == DFLASH_BF16) {
-            HIP_TRY(launch_bf16_to_f32((const uint16_t *)feats, (size_t)T * x->C, (float *)x->enc_act, s),
+            HIP_TRY(launch_bf16_to_f32((const uint16_t *)feats, (size_t)T * x.C, (float *)stage, s),
                     "feature conversion launch");
-            act = x->enc_act;
+            act = stage;
         }
     } else if (c.feature_dtype == DFLASH_BF16) {
         fmt = ACT_BF16;
     } else {
         fmt = ACT_SPLIT3;
-        act_rows = c.max_inject;
-        HIP_TRY(launch_split((const float *)feats, T, x->C, x->C, x->enc_act, ACT_SPLIT3, act_rows, s),
-                "feature split launch");
-        act = x->enc_act;
+        act_rows = stage_rows;
+        HIP_TRY(launch_split((const float *)feats, T, x.C, x.C, stage, ACT_SPLIT3, act_rows, s), "feature split launch");
+        act = stage;
     }
     GemmArgs g = {};
-    g.W = x->fc;
-    g.N = x->E;
-    g.K = x->C;
+    g.W = x.fc;
+    g.N = x.E;
+    g.K = x.C;
     g.M = T;
     g.act = act;
     g.act_rows = act_rows;
-    g.out = x->enc_y;
-    gemm_split(g, c.max_inject);
+    g.out = parts;
+    gemm_split(g, parts_rows);
     HIP_TRY(launch_gemm(c.aux_dtype, fmt, g, s), "encode GEMM launch");
-    HIP_TRY(launch_rmsnorm_rows(x->enc_y, g.S, T, x->E, x->hidden_norm, c.rms_eps, h, s), "encode norm launch");
+    HIP_TRY(launch_rmsnorm_rows(parts, g.S, T, x.E, x.hidden_norm, c.rms_eps, h, s), "encode norm launch");
     return DFLASH_OK;
+}
+
+int check_encode_args(const dflash_ctx *x, const void *feats, int32_t T, const float *h) {
+    if (!x || !feats || !h) return fail(DFLASH_EINVAL, "ctx, feats or h is NULL");
+    if ((uintptr_t)feats % 16 || (uintptr_t)h % 16) return fail(DFLASH_EINVAL, "feats and h must be 16-byte aligned");
+    if (T < 1 || T > x->cfg.max_inject) return fail(DFLASH_ERANGE, "T=%d outside 1..max_inject=%d", T, x->cfg.max_inject);
+    return DFLASH_OK;
+}
+
+// Bytes of converted-feature staging an encode of T positions needs (0 when the features are used as
+// they are): f32 copies of bf16 features, or the three-term bf16 split of f32 features.
+size_t encode_stage_bytes(const dflash_ctx &x, int T) {
+    const dflash_config &c = x.cfg;
+    if (c.aux_dtype == DFLASH_F32) return c.feature_dtype == DFLASH_BF16 ? 4ull * T * x.C : 0;
+    return c.feature_dtype == DFLASH_BF16 ? 0 : 6ull * T * x.C;
+}
+
+int dflash_encode(dflash_ctx *x, const void *feats, int32_t T, float *h, void *stream) {
+    TRY(check_encode_args(x, feats, T, h));
+    return encode_with(*x, feats, T, h, (hipStream_t)stream, x->enc_act, x->cfg.max_inject, x->enc_y,
+                       x->cfg.max_inject);
+}
+
+int dflash_encode_static(dflash_ctx *x, const void *feats, int32_t T, float *h, void *stream) {
+    TRY(check_encode_args(x, feats, T, h));
+    const size_t stage = a256(encode_stage_bytes(*x, T));
+    const size_t row = 4ull * x->E;  // one row of split-K partials
+    if (stage + row * T > ENCODE_STATIC_SCRATCH_BYTES)
+        return fail(DFLASH_ERANGE, "T=%d needs %zu bytes of static scratch, more than the %zu it holds", T,
+                    stage + row * T, ENCODE_STATIC_SCRATCH_BYTES);
+    char *base = (char *)x->static_scratch;  // this device's copy of `scratch`
+    const int parts_rows = (int)std::min<size_t>((ENCODE_STATIC_SCRATCH_BYTES - stage) / row, 1u << 30);
+    return encode_with(*x, feats, T, h, (hipStream_t)stream, base, T, (float *)(base + stage), parts_rows);
 }
 
 int dflash_inject(dflash_ctx *x, void *ring, const float *h, const int32_t *pos, int32_t T, void *stream) {

@@ -366,6 +366,7 @@ struct dflash_ctx {
     int chain_S[5];     // k-splits of the chain's q/k/v, Wo, gate/up, down and lm_head phases
     float *bpartial;    // split partials of the batched projections (null when max_batch == 1)
     int path;           // DFLASH_PATH_*
+    void *static_scratch;  // this device's address of the allocation-free encode's static scratch
 };
 
 // ---------------------------------------------------------------------------

@@ -220,6 +220,17 @@ class Drafter:
                                   _stream(stream)))
         return h
 
+    def encode_static(self, feats: torch.Tensor, h: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """encode() whose scratch is the library's static per-GPU array (for callers that cannot allocate;
+        calls on one GPU must not overlap)."""
+        T = feats.shape[0]
+        fdt = torch.float32 if self.feature_dtype == "f32" else torch.int16
+        if h is None:
+            h = torch.empty((T, self.shape.n_embd), dtype=torch.float32, device=self.device)
+        check(lib().dflash_encode_static(self._ctx, _dev(feats, fdt, "feats"), T, _dev(h, torch.float32, "h"),
+                                         _stream(stream)))
+        return h
+
     def inject(self, ring: torch.Tensor, h: torch.Tensor, positions: torch.Tensor, stream=None) -> None:
         T = h.shape[0]
         rdt = torch.int32 if getattr(self, "_paged", False) else torch.uint8

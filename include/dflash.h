@@ -144,6 +144,21 @@ int dflash_ring_reset(dflash_ctx *ctx, void *ring, void *stream);
  * (EINVAL otherwise). 1 <= T <= max_inject (ERANGE otherwise). */
 int dflash_encode(dflash_ctx *ctx, const void *feats, int32_t T, float *h, void *stream);
 
+/* dflash_encode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same operation and arguments, but its scratch -- the converted
+ * features and the fc GEMM's split-K partials -- lives in a static device
+ * array of 64 MiB that the library holds on every GPU it runs on until the
+ * process ends, instead of in the ctx's workspace. No call allocates (no
+ * hipMalloc, no allocating library routine). ERANGE when T positions need
+ * more than the 64 MiB (one f32 row of n_embd per position, plus n_capture *
+ * target_hidden * 4 bytes per position for bf16 features with f32 fc, or * 6
+ * for f32 features with bf16 fc). All calls on one GPU share the one array:
+ * calls that overlap on one GPU (other streams, other ctxs, other threads)
+ * race and must be serialised by the caller; nothing in the array needs to
+ * start at zero. */
+int dflash_encode_static(dflash_ctx *ctx, const void *feats, int32_t T, float *h, void *stream);
+
 /* KV injection (dflash-ops card, Method; Requirements and limits): for every
  * layer l, position t and kv head j, k = rope(RMSNorm(h_t . wk_l^T)[j] *
  * k_norm_l, pos_t) and v = (h_t . wv_l^T)[j], rounded to ring_dtype and stored

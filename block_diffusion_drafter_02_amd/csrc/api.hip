@@ -871,33 +871,47 @@ int dflash_encode_static(dflash_ctx *x, const void *feats, int32_t T, float *h, 
     return encode_with(*x, feats, T, h, (hipStream_t)stream, base, T, (float *)(base + stage), parts_rows);
 }
 
+// The fused K/V projection of T encoded rows (one GEMM over every layer's wk/wv) and the ring writes: to
+// `ring`, or (rings set) row t to rings[seq[t]].
+int inject_rows(dflash_ctx &x, void *ring, void *const *rings, const int32_t *seq, int n_seq, const float *h,
+                const int32_t *pos, int T, hipStream_t s) {
+    const void *act = h;
+    int act_rows = T;
+    if (x.act_fmt == ACT_SPLIT3) {
+        act_rows = x.cfg.max_inject;
+        HIP_TRY(launch_split(h, T, x.E, x.E, x.inj_act, ACT_SPLIT3, act_rows, s), "inject split launch");
+        act = x.inj_act;
+    }
+    GemmArgs g = {};
+    g.W = x.kv;
+    g.wscale = x.s_kv;
+    g.N = x.L * 2 * x.kvdim;
+    g.K = x.E;
+    g.M = T;
+    g.act = act;
+    g.act_rows = act_rows;
+    g.out = x.inj_kv;
+    gemm_split(g, x.cfg.max_inject);
+    HIP_TRY(launch_gemm(x.cfg.weight_dtype, x.act_fmt, g, s), "inject GEMM launch");
+    HIP_TRY(launch_inject(&x, ring, rings, seq, n_seq, pos, T, g.S, s), "inject launch");
+    return DFLASH_OK;
+}
+
 int dflash_inject(dflash_ctx *x, void *ring, const float *h, const int32_t *pos, int32_t T, void *stream) {
     if (!x || !ring || !h || !pos) return fail(DFLASH_EINVAL, "ctx, ring, h or pos is NULL");
     if ((uintptr_t)ring % (x->paged.pool ? 4 : 256))
         return fail(DFLASH_EINVAL, x->paged.pool ? "block table must be 4-byte aligned" : "ring must be 256-byte aligned");
     if (T < 1 || T > x->W || T > x->cfg.max_inject)
         return fail(DFLASH_ERANGE, "T=%d outside 1..min(window=%d, max_inject=%d)", T, x->W, x->cfg.max_inject);
-    hipStream_t s = (hipStream_t)stream;
-    const void *act = h;
-    int act_rows = T;
-    if (x->act_fmt == ACT_SPLIT3) {
-        act_rows = x->cfg.max_inject;
-        HIP_TRY(launch_split(h, T, x->E, x->E, x->inj_act, ACT_SPLIT3, act_rows, s), "inject split launch");
-        act = x->inj_act;
-    }
-    GemmArgs g = {};
-    g.W = x->kv;
-    g.wscale = x->s_kv;
-    g.N = x->L * 2 * x->kvdim;
-    g.K = x->E;
-    g.M = T;
-    g.act = act;
-    g.act_rows = act_rows;
-    g.out = x->inj_kv;
-    gemm_split(g, x->cfg.max_inject);
-    HIP_TRY(launch_gemm(x->cfg.weight_dtype, x->act_fmt, g, s), "inject GEMM launch");
-    HIP_TRY(launch_inject(x, ring, pos, T, g.S, s), "inject launch");
-    return DFLASH_OK;
+    return inject_rows(*x, ring, nullptr, nullptr, 0, h, pos, T, (hipStream_t)stream);
+}
+
+int dflash_inject_batch(dflash_ctx *x, void *const *rings, int32_t n_seq, const int32_t *seq, const float *h,
+                        const int32_t *pos, int32_t T, void *stream) {
+    if (!x || !rings || !seq || !h || !pos) return fail(DFLASH_EINVAL, "ctx, rings, seq, h or pos is NULL");
+    if (n_seq < 1) return fail(DFLASH_ERANGE, "n_seq=%d must be >= 1", n_seq);
+    if (T < 1 || T > x->cfg.max_inject) return fail(DFLASH_ERANGE, "T=%d outside 1..max_inject=%d", T, x->cfg.max_inject);
+    return inject_rows(*x, nullptr, rings, seq, n_seq, h, pos, T, (hipStream_t)stream);
 }
 
 int dflash_block_step(dflash_ctx *x, void *const *rings, const int32_t *id_last, const int32_t *n_past, int32_t B,

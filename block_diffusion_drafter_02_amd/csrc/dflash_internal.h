@@ -470,7 +470,8 @@ hipError_t launch_split(const float *src, int rows, int K, int ld_src, void *dst
                         hipStream_t s);
 hipError_t launch_bf16_to_f32(const uint16_t *src, size_t n, float *dst, hipStream_t s);
 hipError_t launch_rmsnorm_rows(const float *y, int S, int T, int E, const float *w, float eps, float *h, hipStream_t s);
-hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, int T, int S, hipStream_t s);
+hipError_t launch_inject(const dflash_ctx *c, void *ring, void *const *rings, const int32_t *seq, int n_seq,
+                         const int32_t *pos, int T, int S, hipStream_t s);
 hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32_t *block_ids, const int32_t *n_past,
                         int B, hipStream_t s);
 hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, const int32_t *n_past, int B,

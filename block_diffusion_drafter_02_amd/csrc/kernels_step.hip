@@ -188,16 +188,24 @@ __device__ __forceinline__ void head_norm_rope(float (&x)[D / 64], const float *
 // each kvdim wide. Wave w handles kv heads w, w+4, ... The rope angle is
 // pos * inv_freq[f] in fp64 and its sine and cosine are taken in fp64.
 template <int D>
-// kv holds S k-split partials [S][T][L*2*Hkv*D] of the projection, summed here in split order.
+// kv holds S k-split partials [S][T][L*2*Hkv*D] of the projection, summed here in split order. With `rings`
+// set (a batched injection), row t goes to sequence seq[t]'s ring (or block table) rings[seq[t]] and a row
+// whose sequence index lies outside 0..n_seq-1 is skipped; otherwise every row goes to `ring`.
 __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ kv, int S, int T, int L, int Hkv, int W,
                                                      const int32_t *__restrict__ pos,
                                                      const double *__restrict__ inv_freq,
                                                      const float *__restrict__ k_norm_all, float eps, void *ring,
+                                                     void *const *rings, const int32_t *__restrict__ seq, int n_seq,
                                                      int ring_dtype, PagedPool pp) {
     const int t = blockIdx.x, l = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = pos[t];
     if (p < 0) return;
+    if (rings != nullptr) {
+        const int q = seq[t];
+        if (q < 0 || q >= n_seq) return;
+        ring = rings[q];
+    }
     const RingLoc loc = ring_locate(ring, pp, W, p % W);
     if (!loc.ok) return;  // a page id outside the pool: the write is dropped
     const int slot = loc.slot;
@@ -242,15 +250,16 @@ __global__ __launch_bounds__(256) void inject_kernel(const float *__restrict__ k
     }
 }
 
-hipError_t launch_inject(const dflash_ctx *c, void *ring, const int32_t *pos, int T, int S, hipStream_t s) {
+hipError_t launch_inject(const dflash_ctx *c, void *ring, void *const *rings, const int32_t *seq, int n_seq,
+                         const int32_t *pos, int T, int S, hipStream_t s) {
     dim3 grid(T, c->L);
     const float eps = c->cfg.rms_eps;
     if (c->D == 128)
         hipLaunchKernelGGL(inject_kernel<128>, grid, dim3(256), 0, s, c->inj_kv, S, T, c->L, c->Hkv, c->W, pos, c->inv_freq,
-                           c->k_norm, eps, ring, c->cfg.ring_dtype, c->paged);
+                           c->k_norm, eps, ring, rings, seq, n_seq, c->cfg.ring_dtype, c->paged);
     else if (c->D == 64)
         hipLaunchKernelGGL(inject_kernel<64>, grid, dim3(256), 0, s, c->inj_kv, S, T, c->L, c->Hkv, c->W, pos, c->inv_freq,
-                           c->k_norm, eps, ring, c->cfg.ring_dtype, c->paged);
+                           c->k_norm, eps, ring, rings, seq, n_seq, c->cfg.ring_dtype, c->paged);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -237,6 +237,14 @@ class Drafter:
         check(lib().dflash_inject(self._ctx, _dev(ring, rdt, "ring"), _dev(h, torch.float32, "h"),
                                   _dev(positions, torch.int32, "positions"), T, _stream(stream)))
 
+    def inject_batch(self, ring_table: torch.Tensor, seq: torch.Tensor, h: torch.Tensor, positions: torch.Tensor,
+                     stream=None) -> None:
+        """One fused K/V projection over rows of several sequences: row t goes to ring_table[seq[t]]."""
+        T = h.shape[0]
+        check(lib().dflash_inject_batch(self._ctx, _dev(ring_table, torch.int64, "rings"), ring_table.shape[0],
+                                        _dev(seq, torch.int32, "seq"), _dev(h, torch.float32, "h"),
+                                        _dev(positions, torch.int32, "positions"), T, _stream(stream)))
+
     def ring_table(self, rings) -> torch.Tensor:
         return torch.tensor([r.data_ptr() for r in rings], dtype=torch.int64, device=self.device)
 

@@ -168,6 +168,22 @@ int dflash_encode_static(dflash_ctx *ctx, const void *feats, int32_t T, float *h
  * is skipped. */
 int dflash_inject(dflash_ctx *ctx, void *ring, const float *h, const int32_t *pos, int32_t T, void *stream);
 
+/* Batched context precompute (metrale dflash_head.rs page, PRECOMPUTE_BATCH_ROWS
+ * and batched_precompute_enabled: one fc + fused-KV pass over every
+ * sequence's uncommitted context rows): the injection of dflash_inject for T
+ * rows that belong to several sequences, with one fused K/V projection over
+ * all of them. Row t (h[t], pos[t]) goes to the ring (in paged mode: the block
+ * table) rings[seq[t]]; rings is a device array [n_seq] of ring pointers (or
+ * of int32 block-table pointers), seq [T] int32 device. Encode the rows
+ * beforehand with one dflash_encode call over their concatenated features.
+ * 1 <= T <= max_inject (ERANGE otherwise); n_seq >= 1. Device preconditions
+ * (not checked): the rows of one sequence map to distinct slots; a row with a
+ * negative position or a sequence index outside 0..n_seq-1 is skipped. Each
+ * ring's result equals injecting its own rows with dflash_inject (up to fp32
+ * summation order of the projection). */
+int dflash_inject_batch(dflash_ctx *ctx, void *const *rings, int32_t n_seq, const int32_t *seq, const float *h,
+                        const int32_t *pos, int32_t T, void *stream);
+
 /* The drafter block step for B sequences (rows sequence-major, 16 per
  * sequence). rings: device array [B] of ring pointers; id_last [B] and
  * n_past [B] int32 (device, so a graph replays with fresh values). With the

@@ -132,9 +132,10 @@ def test_real_f32_wrapped_ring_step(gpu):
 def test_real_bf16_batch8_all_sequences(gpu):
     """Eight sequences with n_past ~ U[64, 6000] (partial and wrapped rings), rows sequence-major; every
     sequence's logits, drafts and acceptance count against the oracle's batched forward, each with a target
-    planted from its own oracle drafts. The rings are filled by injecting seeded context rows directly (the
-    encoder is covered by the other real-dimension cases); slot tables of every ring are compared exactly and
-    ring values of the shortest and the longest."""
+    planted from its own oracle drafts. The rings are filled by the batched context precompute (seeded context
+    rows of all eight sequences, shuffled, injected 2048 rows per call; the encoder is covered by the other
+    real-dimension cases); slot tables of every ring are compared exactly and ring values of the shortest and
+    the longest."""
     torch = _torch()
     from block_diffusion_drafter_02_amd.drafter import Drafter
 
@@ -145,17 +146,27 @@ def test_real_bf16_batch8_all_sequences(gpu):
     w = O.Weights(raw, "bf16")
     n_pasts = [int(v) for v in synth.batch_n_past(8, seed=0)]
     order = np.argsort(n_pasts)
-    rings, orings = [], []
+    rings = [dr.new_ring() for _ in n_pasts]
+    orings = []
+    seqs, poss, hs = [], [], []
     for b, n in enumerate(n_pasts):
         pos = np.arange(max(0, n - REAL.window), n)
         h = synth.hidden(REAL, len(pos), seed=0, tag=f"real.batch.h{b}")
-        ring = dr.new_ring()
-        dr.inject(ring, torch.from_numpy(h).to(dr.device), torch.from_numpy(pos.astype(np.int32)).to(dr.device))
         oring = O.Ring(cfg)
         O.inject(cfg, w, oring, h.astype(np.float64), pos)
-        rings.append(ring)
         orings.append(oring)
+        seqs.append(np.full(len(pos), b, np.int32)), poss.append(pos.astype(np.int32)), hs.append(h)
+    # the batched context precompute: every sequence's rows in one shuffled list, injected max_inject rows
+    # per call, each call one fused K/V projection over rows of several sequences
+    perm = np.random.default_rng(8).permutation(sum(len(p) for p in poss))
+    seq_all, pos_all, h_all = np.concatenate(seqs)[perm], np.concatenate(poss)[perm], np.concatenate(hs)[perm]
+    table_all = dr.ring_table(rings)
+    for c0 in range(0, len(perm), REAL.window):
+        sl = slice(c0, c0 + REAL.window)
+        dr.inject_batch(table_all, torch.from_numpy(seq_all[sl]).to(dr.device), torch.from_numpy(h_all[sl]).to(dr.device),
+                        torch.from_numpy(pos_all[sl]).to(dr.device))
     torch.cuda.synchronize()
+    del h_all
     for b in range(8):
         np.testing.assert_array_equal(dr.ring_views(rings[b])[2].cpu().numpy(), orings[b].slot_pos.astype(np.int32))
     for b in (int(order[0]), int(order[-1])):

@@ -6,7 +6,9 @@ attention, output norm, lm_head, greedy drafts) plus the device-side
 acceptance scan, on inputs already resident in HBM. Default workload: real
 drafter dimensions (5 layers, n_embd 6656, heads 32/8, head_dim 128, n_ff
 19968, window 2048, block 16, vocab 8192), bf16 weights and bf16 ring, ring full
-(positions 0..2047 injected), n_past 2048, a fresh id_last and target per step.
+(positions 0..2047 injected), n_past 2048; every step gets a fresh id_last and a
+target that copies that step's drafts up to a planted mismatch index (learned
+in an untimed pass over the same step sequence).
 
 Prints one JSON line: value = achieved HBM GB/s of the whole step (algorithmic
 bytes / step time), with the step time in ms_per_step and step_us, a roofline
@@ -171,11 +173,26 @@ def write_counters(fetch_dir: str, write_dir: str, copy_mib: int, commands: list
     return out
 
 
-def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes, inject_feats=None, min_seconds=10.0,
-                 max_seconds=30.0, block_width=16):
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's processor string."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes, inject_feats=None, runs=3, block_width=16):
     """The oracle, as it stands, for block steps of one sequence at the same dimensions on a synthetic ring
-    with the same fill (each preceded by encoding and injecting ``inject_feats`` when given); returns the rate
-    in the metric's unit (algorithmic GB/s)."""
+    with the same fill (each preceded by encoding and injecting ``inject_feats`` when given): the median of
+    ``runs`` steps with the BLAS thread pool as configured, then one step on a single thread. Returns the
+    rates in the metric's unit (algorithmic GB/s)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     from oracle import dflash_oracle as O
 
     cfg = dataclasses.replace(O.Config.from_shape(shape, rdt), block=block_width)
@@ -188,38 +205,89 @@ def cpu_baseline(shape, raw, wdt, rdt, n_past, total_bytes, inject_feats=None, m
     held = np.arange(max(0, n_past - cfg.window), n_past)
     ring.slot_pos[held % cfg.window] = held
     ring.written[held % cfg.window] = True
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     if wdt == "fp8":
         # the GPU quantises at setup, outside its clock; so does the oracle here
         for l in range(cfg.n_layer):
             for name in O.Weights.MATS:
                 w.fp8_codes((l, name))
         w.fp8_codes("lm_head")
-    np_cur = n_past
-    steps, t0 = 0, time.perf_counter()
-    while True:
+    state = {"np": n_past, "k": 0}
+
+    def one_step() -> float:
+        t0 = time.perf_counter()
         if inject_feats is not None:
             T = inject_feats.shape[0]
-            O.inject(cfg, w, ring, O.encode(cfg, w, inject_feats), np.arange(np_cur, np_cur + T))
-            np_cur += T
-        O.block_forward(cfg, w, ring, O.block_ids(cfg, 1 + steps), np_cur)
-        steps += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or dt / steps * (steps + 1) > max_seconds:
-            break
-    per = dt / steps
-    return {"value": round(total_bytes / per / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seconds_per_step": round(per, 3), "steps": steps,
-            "sample": f"{steps} block steps of one sequence (5 layers + lm_head, block width {cfg.block}) at the same "
-                      f"dimensions and dtypes"
-                      f"{', each after injecting %d positions' % inject_feats.shape[0] if inject_feats is not None else ''}, "
-                      f"ring filled to n_past={n_past} with synthetic values (content does not change the cost); "
-                      f"the rate is this workload's algorithmic bytes per step over the oracle's time per step"}
+            O.inject(cfg, w, ring, O.encode(cfg, w, inject_feats), np.arange(state["np"], state["np"] + T))
+            state["np"] += T
+        O.block_forward(cfg, w, ring, O.block_ids(cfg, 1 + state["k"]), state["np"])
+        state["k"] += 1
+        return time.perf_counter() - t0
+
+    per = [one_step() for _ in range(runs)]
+    med = float(np.median(per))
+    with threadpool_limits(limits=1):
+        single = one_step()
+    inj = f", each after injecting {inject_feats.shape[0]} positions" if inject_feats is not None else ""
+    return {"value": round(total_bytes / med / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "seconds_per_step_median": round(med, 3),
+            "seconds_per_step": [round(t, 3) for t in per],
+            "single_thread": {"value": round(total_bytes / single / 1e9, 4), "seconds_per_step": round(single, 3)},
+            "sample": f"{runs} block steps of one sequence (5 layers + lm_head, block width {cfg.block}) at the same "
+                      f"dimensions and dtypes{inj}, ring filled to n_past={n_past} with synthetic values (content does "
+                      f"not change the cost), median taken, then one more step on one thread; the rate is this "
+                      f"workload's algorithmic bytes per step over the oracle's time per step"}
+
+
+# Figures the dflash-ops card (Measured) reports for its own build on an RTX 6000 Ada (sm89): context for
+# this GPU's numbers, not a target on the same machine.
+PAGE_CONTEXT = {
+    "source": "dflash-ops card, Measured (RTX 6000 Ada, real dims, ring 2048, vocab 8192)",
+    "gemm_weight_stream_gbs": [720, 736],
+    "read_bandwidth_gbs": 771,
+    "non_gemm_share": {"fp32_weights": 0.18, "bf16_weights": 0.30},
+}
+
+# Kernels of a block step that stream no weights (the rest are the weight-streaming projections).
+NON_GEMM = ("attn_partial_kernel", "attn_combine_kernel", "embed_kernel", "accept_kernel")
+STEP_FIRST = ("embed_kernel", "chain_head_kernel")  # the first kernel of every block step
+
+
+def summarize_trace(run_dir: str, skip_replays: int = 5) -> dict:
+    """Per-kernel durations, per-replay span (first kernel start to last kernel end of one block step) and
+    the non-GEMM share of kernel time from a rocprofv3 --kernel-trace CSV of bench runs. Steps are cut at
+    the first kernel of each step; setup kernels before the first step and after the last are dropped, and
+    so are the first ``skip_replays`` steps."""
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in csv.DictReader(open(f))]
+    rows.sort()
+    starts = [i for i, r in enumerate(rows) if r[2].startswith(STEP_FIRST)]
+    if len(starts) < skip_replays + 2:
+        raise SystemExit(f"{run_dir}: {len(starts)} block steps in the trace")
+    spans, per_kernel, gemm_t, other_t = [], {}, 0.0, 0.0
+    for a, b in zip(starts[skip_replays:-1], starts[skip_replays + 1:]):
+        step = [r for r in rows[a:b] if not r[2].startswith("__amd_rocclr")]
+        # a step ends with the projection that writes the logits; later kernels belong to the host loop
+        spans.append((max(r[1] for r in step) - step[0][0]) / 1e3)
+        for t0, t1, name in step:
+            short = name.split("(")[0].replace("void ", "")
+            per_kernel.setdefault(short, []).append((t1 - t0) / 1e3)
+            if short.startswith(NON_GEMM):
+                other_t += (t1 - t0) / 1e3
+            else:
+                gemm_t += (t1 - t0) / 1e3
+    n = len(spans)
+    kern = {k: {"calls_per_step": round(len(v) / n, 2), "median_us": round(float(np.median(v)), 2),
+                "us_per_step": round(sum(v) / n, 2)} for k, v in sorted(per_kernel.items(), key=lambda kv: -sum(kv[1]))}
+    return {"steps": n, "span_us_median": round(float(np.median(spans)), 2),
+            "span_us_p10": round(float(np.percentile(spans, 10)), 2),
+            "span_us_p90": round(float(np.percentile(spans, 90)), 2),
+            "kernel_us_per_step": round((gemm_t + other_t) / n, 2),
+            "non_gemm_share": round(other_t / (gemm_t + other_t), 4), "kernels": kern}
 
 
 def main() -> int:
@@ -234,10 +302,16 @@ def main() -> int:
                     help="block-step path (auto: the per-launch kernels; persistent: the opt-in persistent chain)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (five times) to calibrate byte counters")
+    ap.add_argument("--summarize-trace", metavar="RUN_DIR",
+                    help="summarise a rocprofv3 --kernel-trace run of this bench (per-kernel times, per-replay span, "
+                         "non-GEMM share) as JSON, then exit (no GPU needed)")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="reduce two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy-mib bench "
                          "into the committed gate/up traffic figures, then exit (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace)), flush=True)
+        return 0
     if args.write_counters:
         mib = args.calibrate_copy_mib or 1024
         cmd = ("rocprofv3 --pmc {c} -d {d} -o run --output-format csv -- python3 -u bench.py --steps 3 --warmup 1 "
@@ -275,18 +349,28 @@ def main() -> int:
         n_tab = shape.window // dr.PAGE_SLOTS
         pool = dr.new_pool(n_tab * B)
         page_ids = np.random.default_rng(0).permutation(n_tab * B).astype(np.int32)
-    for b, n in enumerate(n_pasts):
-        ring = (torch.from_numpy(page_ids[b * n_tab:(b + 1) * n_tab]).to(dr.device) if paged else dr.new_ring())
-        first = max(0, n - (n // shape.window + 1) * shape.window) if wdt == "f32" else max(0, n - shape.window)
-        pos = np.arange(first, n, dtype=np.int32)
-        feats = to_device(synth.features(shape, len(pos), fdt, seed=0, tag=f"bench.feats{b}"), dr.device)
-        for c0 in range(0, len(pos), shape.window):
-            sl = slice(c0, c0 + shape.window)
-            h = dr.encode(feats[sl])
-            dr.inject(ring, h, torch.from_numpy(pos[sl]).to(dr.device))
-        del feats
-        rings.append(ring)
-    torch.cuda.synchronize()
+    for b in range(B):
+        rings.append(torch.from_numpy(page_ids[b * n_tab:(b + 1) * n_tab]).to(dr.device) if paged else dr.new_ring())
+
+    def fill_rings():
+        """Reset every ring and inject its context: the last window of positions before n_past (f32: from
+        the start of the window before, so the ring wraps)."""
+        if paged:
+            dr.pages_reset(0, n_tab * B)
+        for b, n in enumerate(n_pasts):
+            if not paged:
+                dr.ring_reset(rings[b])
+            first = max(0, n - (n // shape.window + 1) * shape.window) if wdt == "f32" else max(0, n - shape.window)
+            pos = np.arange(first, n, dtype=np.int32)
+            feats = to_device(synth.features(shape, len(pos), fdt, seed=0, tag=f"bench.feats{b}"), dr.device)
+            for c0 in range(0, len(pos), shape.window):
+                sl = slice(c0, c0 + shape.window)
+                h = dr.encode(feats[sl])
+                dr.inject(rings[b], h, torch.from_numpy(pos[sl]).to(dr.device))
+            del feats
+        torch.cuda.synchronize()
+
+    fill_rings()
     table = dr.ring_table(rings)
     n_vis = [visible_slots(n, shape.window, shape.block) for n in n_pasts]
     nb = step_bytes(shape, wdt, rdt, n_vis)
@@ -304,7 +388,11 @@ def main() -> int:
     ids_all = torch.from_numpy(synth.integers(0, "bench.id_last", (W + K, B), 0, shape.n_vocab)).to(dr.device)
     dr.set_block_width(g)
     dr.set_sampling(temp, 0x5EED)
-    tgt_all = torch.from_numpy(synth.integers(0, "bench.target", (W + K, B, g - 1), 0, shape.n_vocab)).to(dr.device)
+    # per step and sequence: a fresh id_last and a planted mismatch index m ~ U{0..g-1} (m = g-1: none); the
+    # target copies that step's drafts before m, differs at m, and is uniform filler after it
+    mism_all = synth.integers(0, "bench.mismatch", (W + K, B), 0, g)
+    fill_all = synth.integers(0, "bench.target", (W + K, B, g - 1), 0, shape.n_vocab)
+    tgt_all = torch.from_numpy(fill_all).to(dr.device)
     # per-step inputs side by side ([id_last (B) | target (B x (g-1))]), so one copy refreshes both
     inputs_all = torch.cat([ids_all, tgt_all.reshape(W + K, B * (g - 1))], dim=1).contiguous()
     inputs = inputs_all[0].clone()
@@ -316,32 +404,48 @@ def main() -> int:
     n_ok = torch.empty((B,), dtype=torch.int32, device=dr.device)
     stream = torch.cuda.Stream()
     graph = dr.capture_step(table, il, npst, logits, drafts, target, n_ok, stream=stream)
-    setup_s = time.perf_counter() - t_setup
 
     def inject_step(k):
         dr.encode(pool[k % FEATURE_POOL], h_inj, stream=stream)
         dr.inject(rings[0], h_inj, pos_all[k], stream=stream)
         npst.copy_(np_all[k])
 
-    with torch.cuda.stream(stream):
-        def step(k):
-            if T_inj:
-                inject_step(k)
-            inputs.copy_(inputs_all[k])
-            graph.launch(stream)
+    def step(k):
+        if T_inj:
+            inject_step(k)
+        inputs.copy_(inputs_all[k])
+        graph.launch(stream)
 
+    # untimed pass over the same step sequence: learn each step's drafts and plant its target
+    print("[bench] planting per-step targets", file=sys.stderr, flush=True)
+    with torch.cuda.stream(stream):
+        for k in range(W + K):
+            step(k)
+            stream.synchronize()
+            planted = synth.planted_targets(drafts.cpu().numpy(), mism_all[k], fill_all[k], shape.n_vocab)
+            inputs_all[k, B:] = torch.from_numpy(planted.reshape(-1)).to(dr.device)
+    if T_inj:  # the injections advanced the context: start again from the same state
+        fill_rings()
+        npst.copy_(torch.tensor(n_pasts, dtype=torch.int32))
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    with torch.cuda.stream(stream):
         for k in range(W):
             step(k)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
         t0 = time.perf_counter()
-        e0.record(stream)
         for k in range(K):
+            ev[k].record(stream)
             step(W + k)
-        e1.record(stream)
+        ev[K].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ev_ms = e0.elapsed_time(e1) / K
+        per_step_us = np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(K)])
+        ev_ms = ev[0].elapsed_time(ev[K]) / K
+        n_ok_last = n_ok.cpu().numpy()
+        accept_ok = bool(np.array_equal(n_ok_last, mism_all[W + K - 1]))
         # replays alone, without the per-step input refresh
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record(stream)
@@ -375,6 +479,8 @@ def main() -> int:
             e[2].record(stream)
             torch.cuda.synchronize()
             inj = {"inject_us": e[0].elapsed_time(e[1]) / reps * 1e3, "encode_us": e[1].elapsed_time(e[2]) / reps * 1e3}
+    if args.path == "persistent" or dr.step_path(B) == _lib.PATH_PERSISTENT:
+        dr.check_device(stream)  # raises if a bounded wait of the chain gave up during the run
 
     ms = wall * 1e3 / K
     total = nb["total"] + (ib["total"] if ib else 0)
@@ -396,6 +502,9 @@ def main() -> int:
         "step_us": round(ms * 1e3, 2),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "event_ms_per_step": round(ev_ms, 5),
+        "step_us_median": round(float(np.median(per_step_us)), 2),
+        "step_us_p10": round(float(np.percentile(per_step_us, 10)), 2),
+        "step_us_p90": round(float(np.percentile(per_step_us, 90)), 2),
         "graph_only_ms_per_step": round(graph_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -428,6 +537,8 @@ def main() -> int:
             "avg_launch_us": round(gu_ms * 1e3, 3),
             "algorithmic_bytes_per_launch": gu_bytes,
         },
+        "accept": {"planted_mismatch_per_step": True, "last_step_n_ok_equals_planted": accept_ok},
+        "context": PAGE_CONTEXT,
         "setup_s": round(setup_s, 1),
     }
     if T_inj:

@@ -184,8 +184,11 @@ int dflash_inject(dflash_ctx *ctx, void *ring, const float *h, const int32_t *po
 int dflash_inject_batch(dflash_ctx *ctx, void *const *rings, int32_t n_seq, const int32_t *seq, const float *h,
                         const int32_t *pos, int32_t T, void *stream);
 
-/* The drafter block step for B sequences (rows sequence-major, 16 per
- * sequence). rings: device array [B] of ring pointers; id_last [B] and
+/* The drafter block step (dflash-ops card, Usage: the step on the noise block
+ * [id_last, mask x 15] returns logits [16, n_vocab] and greedy drafts at block
+ * positions 1..15; Method: the block attends non-causally to itself and to the
+ * ring, whose window masks only the deep past) for B sequences (rows
+ * sequence-major, 16 per sequence; metrale dflash_head.rs page, DflashBatch). rings: device array [B] of ring pointers; id_last [B] and
  * n_past [B] int32 (device, so a graph replays with fresh values). With the
  * block width g of dflash_set_block_width (16 unless set), block row i < g of
  * sequence b holds [id_last, mask...][i] at position n_past[b] + i and
@@ -199,7 +202,9 @@ int dflash_block_step(dflash_ctx *ctx, void *const *rings, const int32_t *id_las
                       float *logits, int32_t *drafts, void *stream);
 
 /* As dflash_block_step but with explicit block ids [B, 16] (device) instead
- * of id_last: a hook for testing joint (non-causal) denoising. */
+ * of id_last: a hook for testing joint (non-causal) denoising (dflash-ops
+ * card, Correctness: a change at a later block position must move the logits
+ * of earlier positions). */
 int dflash_block_forward(dflash_ctx *ctx, void *const *rings, const int32_t *block_ids, const int32_t *n_past,
                          int32_t B, float *logits, int32_t *drafts, void *stream);
 
@@ -222,7 +227,8 @@ int dflash_accept_bonus(dflash_ctx *ctx, const int32_t *drafts, const int32_t *t
 
 /* Capture the block step (and, when target and n_ok are non-NULL, the
  * acceptance scan) for fixed pointers into a HIP graph by stream capture on
- * `stream`. Nothing is allocated inside the capture; every intermediate
+ * `stream` (dflash-ops card, Usage: capture_step; Method: the captured step
+ * allocates nothing and a replay reads fresh inputs from fixed buffers). Nothing is allocated inside the capture; every intermediate
  * lives in the workspace. Replay with dflash_step_graph_launch after writing
  * fresh values into id_last / n_past / target. The graph reads the ctx's
  * workspace, so the ctx must outlive it and no other call on the same ctx may

@@ -80,3 +80,28 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_trace_summary_spans_and_non_gemm_share(tmp_path):
+    """Three block steps of a synthetic kernel trace (embed, a projection, attention, combine, a projection;
+    then a host-loop copy) after one setup kernel: spans run from each step's first kernel to the end of its
+    last one, copies are not counted, and the non-GEMM share is attention + combine + embed over all."""
+    path = tmp_path / "t"
+    os.makedirs(path)
+    rows, t = [("tile_weights_kernel(x)", 0, 50)], 100
+    for _ in range(3):
+        for name, d in (("embed_kernel(EmbedArgs)", 5), ("void gemv_kernel<1>(GemvArgs)", 20),
+                        ("void attn_partial_kernel<128>(AttnArgs)", 10), ("attn_combine_kernel(CombArgs)", 5),
+                        ("void gemv_kernel<2>(GemvArgs)", 60), ("__amd_rocclr_copyBuffer", 2)):
+            rows.append((name, t, t + d))
+            t += d + 1
+    with open(path / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for name, a, b in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": a * 1000, "End_Timestamp": b * 1000})
+    out = bench.summarize_trace(str(path), skip_replays=0)
+    assert out["steps"] == 2  # the last step has no following step start and is dropped
+    assert out["span_us_median"] == 5 + 1 + 20 + 1 + 10 + 1 + 5 + 1 + 60
+    assert out["non_gemm_share"] == round(20 / 100, 4)
+    assert out["kernels"]["gemv_kernel<2>"]["us_per_step"] == 60

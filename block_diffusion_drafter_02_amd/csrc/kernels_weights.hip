@@ -303,7 +303,15 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 2, wc = wave & 3;  // rows 64wr.., column group g0 + wc
     const int G = a.N / GROUP_N;
-    const int g0 = blockIdx.x * GEMM_GROUPS, r0 = blockIdx.y * BM, sp = blockIdx.z;
+    // One-dimensional grid in an L2-friendly order: the row tiles that share a (column tile, k-split) are
+    // consecutive in launch order and eight apart in it, so that the round-robin placement of workgroups
+    // on the eight XCDs puts them on one XCD at about the same time, and its L2 serves their common weight
+    // tiles once: L = (q * Y + y) * 8 + c with column-tile-and-split index xz = 8 q + c.
+    const int X = (G + GEMM_GROUPS - 1) / GEMM_GROUPS, Y = (a.M + BM - 1) / BM;
+    const int Lc = blockIdx.x % 8, Lr = blockIdx.x / 8;
+    const int xz = (Lr / Y) * 8 + Lc;
+    if (xz >= X * a.S) return;
+    const int g0 = (xz % X) * GEMM_GROUPS, r0 = (Lr % Y) * BM, sp = xz / X;
     const int KB = a.K / KBLK;
     const int kb0 = sp * a.kbps, kb1 = min(KB, kb0 + a.kbps);
     float *out = a.out + (size_t)sp * a.M * a.N;
@@ -428,8 +436,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 template <int WT, int AF, bool ALANES>
 static hipError_t gemm_go(const GemmArgs &a, hipStream_t s) {
     using Sh = GemmShape<WT, AF, ALANES>;
-    dim3 grid((a.N / GROUP_N + GEMM_GROUPS - 1) / GEMM_GROUPS, (a.M + GEMM_BM - 1) / GEMM_BM, a.S);
-    hipLaunchKernelGGL((gemm_kernel<WT, AF, ALANES>), grid, dim3(GEMM_THREADS), Sh::LDS, s, a);
+    const int X = (a.N / GROUP_N + GEMM_GROUPS - 1) / GEMM_GROUPS, Y = (a.M + GEMM_BM - 1) / GEMM_BM;
+    const int n = (X * a.S + 7) / 8 * 8 * Y;  // see the kernel's decoding of blockIdx.x
+    hipLaunchKernelGGL((gemm_kernel<WT, AF, ALANES>), dim3(n), dim3(GEMM_THREADS), Sh::LDS, s, a);
     return hipGetLastError();
 }
 

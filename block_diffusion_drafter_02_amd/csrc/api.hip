@@ -250,10 +250,10 @@ size_t carve(dflash_ctx &x, char *base) {
     x.partial = cv.take<float>(4 * pmax);
     x.partial_floats = pmax;
     x.counters = cv.take<int>(4ull * 2 * gmax);  // half-group launches count per 32 columns
+    x.written = cv.take<int>(4ull * 2 * gmax);
     x.pf_sink = cv.take<unsigned>(64);
     x.n_counters = 2 * gmax;
-    x.am_val = cv.take<float>(4ull * (V / 32) * Mmax);
-    x.am_idx = cv.take<int>(4ull * (V / 32) * Mmax);
+    x.am_key = cv.take<unsigned long long>(8ull * (V / 32) * Mmax);
     x.am_counter = cv.take<int>(4);
     x.ids = cv.take<int32_t>(4ull * Mmax);
 
@@ -406,6 +406,7 @@ int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
     TRY(tile_matrix(w->lm_head, V, E, esw, x.lm, 0, 0, 0, s));
     TRY(tile_scales(w->s_lm_head, V, x.s_lm, 0, 0, 0, s));
     HIP_TRY(launch_fill_i32(x.counters, 0, x.n_counters, s), "counter reset");
+    HIP_TRY(launch_fill_i32(x.written, 0, x.n_counters, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.am_counter, 0, 1, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.csync, 0, x.n_csync, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.csync, 1, 1, s), "epoch reset");  // epoch 1: flags hold 0 until first set
@@ -481,8 +482,7 @@ int prepare_chain(dflash_ctx &x, hipStream_t s) {
     a.done_down = a.done_gu + (size_t)x.L * (2 * x.F / GROUP_N);
     if (a.done_down + (size_t)x.L * x.G_E != x.csync + x.n_csync)
         return fail(DFLASH_EHIP, "internal: chain flag layout");
-    a.am_val = x.am_val;
-    a.am_idx = x.am_idx;
+    a.am_key = x.am_key;
     a.spin_ticks = (long long)rate_khz * 1000;  // one second
     HIP_TRY(hipMemcpyAsync(x.cargs, &a, sizeof a, hipMemcpyHostToDevice, s), "chain argument upload");
     HIP_TRY(hipStreamSynchronize(s), "chain argument upload");
@@ -569,6 +569,8 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     }
     a.partial = x.partial;
     a.counters = x.counters;
+    a.written = x.written;
+    a.err = x.csync + 1;
     a.epi = epi;
     if (G > x.n_counters) return fail(DFLASH_EINVAL, "GEMV with %d column groups exceeds the counter table", G);
     HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), WN, nwv, cw, dim3(G, a.S), a, s),
@@ -635,8 +637,7 @@ int stage_lm(const dflash_ctx &x, int M, float *logits, int32_t *drafts, const i
     e.ss_groups = x.E / gemv_col_width(x, x.E, M, 1, EPI_RESID);  // written by the last down
     e.out = logits;
     e.ld_out = x.V;
-    e.am_val = x.am_val;
-    e.am_idx = x.am_idx;
+    e.am_key = x.am_key;
     e.am_counter = x.am_counter;
     e.drafts = drafts;
     e.target = target;
@@ -1049,9 +1050,10 @@ int dflash_check_device(dflash_ctx *x, void *stream) {
         HIP_TRY(launch_fill_i32(x->csync, 0, x->n_csync, s), "chain state reset");
         HIP_TRY(launch_fill_i32(x->csync, 1, 1, s), "chain state reset");
         HIP_TRY(launch_fill_i32(x->counters, 0, x->n_counters, s), "counter reset");
+        HIP_TRY(launch_fill_i32(x->written, 0, x->n_counters, s), "counter reset");
         HIP_TRY(hipStreamSynchronize(s), "chain state reset");
-        return fail(DFLASH_ESTATE, "a bounded wait of the dataflow chain gave up; the outputs of the steps since "
-                                   "the last check are invalid");
+        return fail(DFLASH_ESTATE, "a bounded wait on the device (the dataflow chain, or a split-K hand-off) gave "
+                                   "up; the outputs of the steps since the last check are invalid");
     }
     return DFLASH_OK;
 }

@@ -213,8 +213,7 @@ struct EpiArgs {
     int block;  // rows per sequence
     int gamma;  // block width in use: drafts and acceptance cover rows 1..gamma-1
     // EPI_LOGITS: argmax across groups
-    float *am_val;
-    int *am_idx;
+    unsigned long long *am_key;  // [G][ss_stride] per-group argmax keys (argmax_key)
     int *am_counter;
     int32_t *drafts;      // [B][gamma-1]
     const int32_t *target;  // [B][gamma-1] or null
@@ -267,7 +266,9 @@ struct GemvArgs {
     int S;          // k-splits
     int kb_per_split;
     float *partial; // [S][G][Mp][64]
-    int *counters;  // [G], zero between launches
+    int *counters;  // [G] arrivals, zero between launches
+    int *written;   // [G] partials stored, zero between launches
+    int *err;       // sticky device error word (a bounded wait gave up)
     EpiArgs epi;
 };
 
@@ -346,9 +347,9 @@ struct dflash_ctx {
     float *partial;
     size_t partial_floats;
     int *counters;
+    int *written;  // split-K partials stored per group (the hand-off of the per-launch kernels)
     int n_counters;
-    float *am_val;
-    int *am_idx;
+    unsigned long long *am_key;  // [G][ss_stride] per-group argmax keys (argmax_key)
     int *am_counter;
     int32_t *ids;       // [Mmax] block ids
     // encode / inject buffers
@@ -418,8 +419,7 @@ struct ChainArgs {
     // and lm_head outputs are read only by later launches)
     int *done_embed;          // [G_E]
     int *done_o, *done_gu, *done_down;  // [L][groups of that projection]
-    float *am_val;
-    int *am_idx;
+    unsigned long long *am_key;  // [G][ss_stride] per-group argmax keys (argmax_key)
     int *am_counter;
     unsigned *epoch;          // the step's flag value; advanced by the step's last workgroup
     int *err;                 // sticky: a bounded wait gave up

@@ -257,6 +257,82 @@ __device__ __forceinline__ bool splitk_last(float *tile, float *mine, const floa
     return true;
 }
 
+// Split-K hand-off in which only the earlier arrivals store their partial tile.
+// Writes issued while the weight stream saturates HBM cost far more than their
+// size (measured: a 4 KB store per workgroup of a 1248-workgroup, 532 MB read
+// stream adds 4.7 us), so the last arrival keeps its own partial in LDS. Each
+// workgroup first bumps `arrive`; one that is not last stores its tile to
+// `mine` with device-coherent stores, waits for them and bumps `written`. The
+// last one polls `written` (tid 0, bounded: on giving up it sets *err, which
+// dflash_check_device reports) until the other nparts - 1 partials are out,
+// then sums the nparts partials in split order, its own (split s) from LDS, so
+// the result is the same as when every split stores its partial. It re-arms
+// both counters and returns true; the others return false.
+constexpr int SPLITK_POLL_LIMIT = 1 << 22;
+
+template <int EPT>
+__device__ __forceinline__ bool splitk_hand_off(float *tile, float *mine, const float *parts, size_t stride,
+                                                int nparts, int s, int *arrive, int *written, int *err, int *flag_s) {
+    const int tid = threadIdx.x;
+    if (tid == 0)
+        *flag_s = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
+    __syncthreads();
+    if (!*flag_s) {
+        for (int k = 0; k < EPT; ++k)
+            __hip_atomic_store((uint32_t *)(mine + tid + 256 * k), __float_as_uint(tile[tid + 256 * k]),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(written, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+    }
+    if (tid == 0) {
+        int polls = 0;
+        while (__hip_atomic_load(written, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nparts - 1) {
+            if (++polls > SPLITK_POLL_LIMIT) {
+                __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    __syncthreads();
+    constexpr int UB = EPT <= 4 ? 16 : (EPT <= 8 ? 8 : (EPT <= 16 ? 4 : 2));  // partials in flight together
+    float sum[EPT], own[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        sum[k] = 0.0f;
+        own[k] = tile[tid + 256 * k];
+    }
+    for (int s0 = 0; s0 < nparts; s0 += UB) {  // summed in partial order
+        float v[UB][EPT];
+#pragma unroll
+        for (int u = 0; u < UB; ++u)
+#pragma unroll
+            for (int k = 0; k < EPT; ++k)
+                v[u][k] = s0 + u < nparts && s0 + u != s
+                              ? __uint_as_float(__hip_atomic_load(
+                                    (const uint32_t *)(parts + (size_t)(s0 + u) * stride + tid + 256 * k),
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                              : own[k];
+#pragma unroll
+        for (int u = 0; u < UB; ++u)
+#pragma unroll
+            for (int k = 0; k < EPT; ++k)
+                if (s0 + u < nparts) sum[k] += v[u][k];
+    }
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) tile[tid + 256 * k] = sum[k];  // each thread rewrites only its own elements
+    if (tid == 0) {
+        __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(written, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // Sampling noise: Philox-4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw,
 // SC 2011) -- its first output word at counter (c0, c1, c2, c3) under key
@@ -338,8 +414,23 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs &e, int g, EpiPre &p)
     }
 }
 
+// Argmax across the groups of one launch: every group stores its (value,
+// column) maximum of row m as one 64-bit key that orders by value, then by
+// lower column (values that compare equal, +0 and -0 among them, give the same
+// upper word), so the largest key of a row names the first column of the row
+// maximum whatever the order the keys are compared in. (One shared key per row
+// updated with 64-bit atomic max was measured slower: 128 groups contend on
+// the same two cache lines.)
+__device__ __forceinline__ unsigned long long argmax_key(float v, int col) {
+    uint32_t b = __float_as_uint(v);
+    if (b == 0x80000000u) b = 0u;  // -0 ranks as +0
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((unsigned long long)ord << 32) | (uint32_t)~(uint32_t)col;
+}
+__device__ __forceinline__ int argmax_key_index(unsigned long long k) { return (int)~(uint32_t)(k & 0xffffffffull); }
+
 // CW: columns of group g (64, or 32 for half groups; lanes >= CW idle). The
-// G groups of one launch write ss_out / am_val rows 0..G-1.
+// G groups of one launch write ss_out rows 0..G-1.
 template <int EPI, int MT, int WN, bool PF = false, int CW = GROUP_N>  // PF: operands from epi_prefetch (MT = 1)
 __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, float *tile, float *rs_s, int *flag_s,
                                               int *best_s, const EpiPre &pre = EpiPre{}) {
@@ -414,6 +505,40 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
     } else if constexpr (EPI == EPI_SWIGLU) {
         const float sg = PF ? pre.sc : (e.wscale && lane < 32 ? e.wscale[g * GROUP_N + lane] : 1.0f);
         const float su = PF ? pre.sc2 : (e.wscale && lane < 32 ? e.wscale[g * GROUP_N + 32 + lane] : 1.0f);
+        if constexpr (MT == 1 && CW == GROUP_N) {
+            if (e.act_fmt == ACT_SPLIT3 && M == 16) {
+                // The group's 16 x 32 outputs, as three bf16 planes in the lane-ordered layout, are six
+                // runs of 32 16-byte words (plane, word v of k-block g / 2, lanes 32 (g % 2) ..): staged in
+                // LDS in that order, then stored as contiguous dwords instead of one 2-byte store per term
+                // and value.
+                __shared__ uint32_t stage[6 * 128];
+                uint16_t *st16 = (uint16_t *)stage;
+                for (int m = wave; m < 16; m += 4) {
+                    if (lane < 32) {
+                        float gv = tile[m * GN + lane] * rs_s[m];
+                        float uv = tile[m * GN + lane + 32] * rs_s[m];
+                        if (e.wscale) {
+                            gv *= sg;
+                            uv *= su;
+                        }
+                        uint16_t t[3];
+                        split3(gv / (1.0f + expf(-gv)) * uv, t[0], t[1], t[2]);
+                        const int v = (lane % 16) / 8, ll = m + 16 * (lane / 16), i = lane % 8;
+#pragma unroll
+                        for (int p = 0; p < 3; ++p) st16[((p * 2 + v) * 32 + ll) * 8 + i] = t[p];
+                    }
+                }
+                __syncthreads();
+                const size_t plane = (size_t)e.act_rows * e.act_K;
+                const int kb = g / 2, h = g % 2;
+                for (int d = tid; d < 6 * 128; d += 256) {
+                    const int run = d / 128, p = run / 2, v = run % 2;
+                    const size_t el = (size_t)p * plane + (((size_t)kb * 2 + v) * 64 + 32 * h) * 8;
+                    st_i32((int32_t *)((uint16_t *)e.act_out + el) + d % 128, (int32_t)stage[d]);
+                }
+                return;
+            }
+        }
         for (int m = wave; m < M; m += 4) {
             if (lane < 32) {
                 float gv = tile[m * GN + lane] * rs_s[m];
@@ -450,10 +575,9 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                     bi = oi;
                 }
             }
-            if (lane == 0) {
-                st_f32(e.am_val + (size_t)g * e.ss_stride + m, bv);
-                st_i32(e.am_idx + (size_t)g * e.ss_stride + m, bi);
-            }
+            if (lane == 0)
+                __hip_atomic_store(e.am_key + (size_t)g * e.ss_stride + m, argmax_key(bv, bi), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0);
@@ -463,31 +587,30 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
             *flag_s = __hip_atomic_fetch_add(e.am_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
         __syncthreads();
         if (!*flag_s) return;
+        // every group's key is in: 16 threads per row take the largest key of the
+        // groups sub, sub + 16, ... with the loads of a batch issued together,
+        // then a 16-lane reduction (the order does not change a maximum)
+        constexpr int KU = 8;
         for (int m0 = 0; m0 < M; m0 += 16) {
             const int m = m0 + (tid >> 4), sub = tid & 15;
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
+            unsigned long long best = 0ull;
             if (m < M)
-                for (int gg = sub; gg < G; gg += 16) {
-                    const float v = __uint_as_float(__hip_atomic_load(
-                        (const uint32_t *)(e.am_val + (size_t)gg * e.ss_stride + m), __ATOMIC_RELAXED,
-                        __HIP_MEMORY_SCOPE_AGENT));
-                    const int i = __hip_atomic_load(e.am_idx + (size_t)gg * e.ss_stride + m, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-                    if (v > bv || (v == bv && i < bi)) {
-                        bv = v;
-                        bi = i;
-                    }
+                for (int g0 = sub; g0 < G; g0 += 16 * KU) {
+                    unsigned long long k[KU];
+#pragma unroll
+                    for (int u = 0; u < KU; ++u)
+                        k[u] = g0 + 16 * u < G ? __hip_atomic_load(e.am_key + (size_t)(g0 + 16 * u) * e.ss_stride + m,
+                                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                               : 0ull;
+#pragma unroll
+                    for (int u = 0; u < KU; ++u) best = k[u] > best ? k[u] : best;
                 }
             for (int o = 8; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
+                const unsigned long long ok = __shfl_xor(best, o, 64);
+                best = ok > best ? ok : best;
             }
             if (sub == 0 && m < M) {
+                const int bi = argmax_key_index(best);
                 best_s[m] = bi;
                 const int b = m / e.block, i = m % e.block;
                 if (i > 0 && i < e.gamma) st_i32(e.drafts + (size_t)b * (e.gamma - 1) + i - 1, bi);

@@ -290,8 +290,7 @@ __device__ __forceinline__ void chain_layer(const ChainArgs *__restrict__ ap, co
         e.ss_groups = a.G_E;
         e.out = io.logits;
         e.ld_out = a.V;
-        e.am_val = a.am_val;
-        e.am_idx = a.am_idx;
+        e.am_key = a.am_key;
         e.am_counter = a.am_counter;
         e.drafts = io.drafts;
         e.target = io.target;

@@ -187,9 +187,19 @@ __global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
     }
     if (a.S > 1) {
         constexpr int TE = MP * GN;
-        if (!splitk_last<TE / 256>(tile, a.partial + ((size_t)s * G + g) * TE, a.partial + (size_t)g * TE,
-                                   (size_t)G * TE, a.S, &a.counters[g], &flag_s))
-            return;
+        // Many four-wave workgroups: only the earlier arrivals store their partial
+        // (gate/up at the real dimensions: 96.5 -> 94.9 us). One workgroup per
+        // compute unit: the splits of a group finish together, so the last one
+        // would wait on the other's stores; every split stores its partial first.
+        if constexpr (NWV == 4) {
+            if (!splitk_hand_off<TE / 256>(tile, a.partial + ((size_t)s * G + g) * TE, a.partial + (size_t)g * TE,
+                                           (size_t)G * TE, a.S, s, &a.counters[g], &a.written[g], a.err, &flag_s))
+                return;
+        } else {
+            if (!splitk_last<TE / 256>(tile, a.partial + ((size_t)s * G + g) * TE, a.partial + (size_t)g * TE,
+                                       (size_t)G * TE, a.S, &a.counters[g], &flag_s))
+                return;
+        }
     }
     gemv_epilogue<EPI, MT, WN, PF, CW>(a.epi, g, G, tile, rs_s, &flag_s, best_s, pre);
 }

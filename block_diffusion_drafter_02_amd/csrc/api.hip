@@ -313,6 +313,7 @@ void derive(dflash_ctx &x) {
     x.Mmax = 16 * c.max_batch;
     x.G_E = x.E / GROUP_N;
     x.act_fmt = c.weight_dtype == DFLASH_F32 ? ACT_F32 : ACT_SPLIT3;
+    x.blk_fmt = x.act_fmt;
     x.wbytes_el = dtype_bytes(c.weight_dtype);
 }
 
@@ -511,7 +512,7 @@ EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
     e.seed_lo = (uint32_t)x.seed;
     e.seed_hi = (uint32_t)(x.seed >> 32);
     e.act_rows = x.Mmax;
-    e.act_fmt = x.act_fmt;
+    e.act_fmt = x.blk_fmt;
     return e;
 }
 
@@ -543,7 +544,7 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
         g.act_rows = x.Mmax;
         g.out = x.bpartial;
         batch_split(N, K, g.S, g.kbps);
-        HIP_TRY(launch_gemm(x.cfg.weight_dtype, x.act_fmt, g, s, true), "batched projection launch");
+        HIP_TRY(launch_gemm(x.cfg.weight_dtype, x.blk_fmt, g, s, true), "batched projection launch");
         HIP_TRY(launch_batch_epi(x.bpartial, g.S, g.M, N, epi, s), "batched epilogue launch");
         return DFLASH_OK;
     }
@@ -573,7 +574,7 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     a.err = x.csync + 1;
     a.epi = epi;
     if (G > x.n_counters) return fail(DFLASH_EINVAL, "GEMV with %d column groups exceeds the counter table", G);
-    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.act_fmt, mt_for(epi.M), WN, nwv, cw, dim3(G, a.S), a, s),
+    HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.blk_fmt, mt_for(epi.M), WN, nwv, cw, dim3(G, a.S), a, s),
             "block-step GEMV launch");
     return DFLASH_OK;
 }
@@ -651,6 +652,9 @@ int stage_lm(const dflash_ctx &x, int M, float *logits, int32_t *drafts, const i
 int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const int32_t *block_ids,
              const int32_t *n_past, int B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
              hipStream_t s) {
+    // one sequence on the per-launch kernels: f32 activations split at load (4 bytes per value written and
+    // read instead of 6); the batched projections and the chain read three bf16 planes
+    x.blk_fmt = (B == 1 && !use_chain(x, B)) ? ACT_F32 : x.act_fmt;
     if (use_chain(x, B)) {
         // dataflow chain: head (embed + q/k/v of layer 0); per layer attention, then Wo .. q/k/v(l+1) or lm_head
         ChainIO io{id_last, block_ids, n_past, logits, drafts, target, n_ok, x.gamma, x.temp, (uint32_t)x.seed,

@@ -307,7 +307,9 @@ struct dflash_ctx {
     dflash_config cfg;
     int device;
     int E, H, Hkv, D, F, W, L, V, C, qdim, kvdim, nqkv, Mmax, G_E;
-    int act_fmt;       // activation format of the step GEMVs
+    int act_fmt;       // activation format of the batched projections, the dataflow chain, encode and inject
+    int blk_fmt;       // activation format of the block rows in the step being issued: f32 lane words (split
+                       // at load) for one sequence on the per-launch kernels, else act_fmt
     int last_B;        // batch of the last block step (0 before the first)
     int gamma;         // block width of the steps (2..block; rows gamma.. of each sequence are padding)
     PagedPool paged;   // paged drafter KV (pool null: contiguous rings)

@@ -143,6 +143,43 @@ __device__ __forceinline__ void load_act_lanes(const void *act, int act_rows, in
     }
 }
 
+// MFMA operand format of an activation format: f32 lane words feeding bf16 or
+// fp8 weights are split at load into the three bf16 terms of the exact split
+// (the terms a three-plane activation would hold), so a producer writes 4
+// bytes per value instead of 6 and a consumer reads a third less.
+template <int WT, int AF>
+struct ActOp {
+    static constexpr int AFO = (WT != DFLASH_F32 && AF == ACT_F32) ? ACT_SPLIT3 : AF;
+};
+
+template <int WT, int AF>
+__device__ __forceinline__ void load_act_operands(const void *act, int act_rows, int K, int mt, bool live, int kb,
+                                                  int lane, u32x4 (&a)[AFTraits<ActOp<WT, AF>::AFO>::NW]) {
+    if constexpr (WT != DFLASH_F32 && AF == ACT_F32) {
+        u32x4 f[4];
+        load_act_lanes<ACT_F32>(act, act_rows, K, mt, live, kb, lane, f);
+        // f32 words 0-1 hold elements 0-7 (the first MFMA of the k-block), words 2-3 elements 8-15;
+        // term t of half h goes where the three-plane layout keeps it, a[2t + h]
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float v[8] = {__uint_as_float(f[2 * h].x),     __uint_as_float(f[2 * h].y),
+                                __uint_as_float(f[2 * h].z),     __uint_as_float(f[2 * h].w),
+                                __uint_as_float(f[2 * h + 1].x), __uint_as_float(f[2 * h + 1].y),
+                                __uint_as_float(f[2 * h + 1].z), __uint_as_float(f[2 * h + 1].w)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t w0, w1, w2;
+                split3_pair(v[2 * i], v[2 * i + 1], w0, w1, w2);
+                a[h][i] = w0;
+                a[2 + h][i] = w1;
+                a[4 + h][i] = w2;
+            }
+        }
+    } else {
+        load_act_lanes<AF>(act, act_rows, K, mt, live, kb, lane, a);
+    }
+}
+
 // acc += A(16 rows x 64 k) * W(16 cols x 64 k)^T for one tile
 template <int WT, int AF>
 __device__ __forceinline__ void tile_mfma(const u32x4 (&w)[WTraits<WT>::NV], const u32x4 (&a)[AFTraits<AF>::NW],
@@ -489,6 +526,12 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
             wn = col_ok ? e.wnext[n] : 0.0f;
         }
         float *xo = e.x_out ? e.x_out : e.x;
+        // a whole 64-column group of 16 rows: the next projection's activations for k-block g are one
+        // contiguous block (4 KB of f32 words, or 2 KB in each bf16 plane), staged in LDS and stored as
+        // contiguous dwords
+        constexpr bool STAGE_OK = MT == 1 && CW == GROUP_N;
+        __shared__ uint32_t stage[STAGE_OK ? 6 * 256 : 1];
+        const bool staged = STAGE_OK && M == 16 && (e.act_fmt == ACT_SPLIT3 || e.act_fmt == ACT_F32);
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             const int m = wave + 4 * r;
@@ -496,23 +539,50 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                 const float xn = col_ok ? xv[r] + tile[m * GN + lane] * sc : 0.0f;
                 if (col_ok) {
                     st_f32(xo + (size_t)m * e.ld_x + n, xn);
-                    write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, n, xn * wn);
+                    if (staged) {
+                        const int ll = m + 16 * (lane / 16);
+                        if (e.act_fmt == ACT_F32) {
+                            stage[(((lane % 16) / 4) * 64 + ll) * 4 + lane % 4] = __float_as_uint(xn * wn);
+                        } else {
+                            uint16_t t[3];
+                            split3(xn * wn, t[0], t[1], t[2]);
+                            const int v = (lane % 16) / 8, i = lane % 8;
+#pragma unroll
+                            for (int p = 0; p < 3; ++p) ((uint16_t *)stage)[((p * 2 + v) * 64 + ll) * 8 + i] = t[p];
+                        }
+                    } else {
+                        write_act(e.act_out, e.act_fmt, e.act_rows, e.act_K, m, n, xn * wn);
+                    }
                 }
                 const float sq = wave_sum(xn * xn);
                 if (lane == 0) st_f32(e.ss_out + (size_t)g * e.ss_stride + m, sq);
+            }
+        }
+        if (staged) {
+            __syncthreads();
+            if (e.act_fmt == ACT_F32) {
+                int32_t *dst = (int32_t *)e.act_out + (size_t)g * 1024;  // k-block g: 4 words x 64 lanes x 4
+                for (int d = tid; d < 1024; d += 256) st_i32(dst + d, (int32_t)stage[d]);
+            } else {
+                const size_t plane = (size_t)e.act_rows * e.act_K;
+                for (int d = tid; d < 3 * 512; d += 256) {  // plane p: 2 words x 64 lanes x 8 bf16
+                    const int p = d / 512;
+                    st_i32((int32_t *)((uint16_t *)e.act_out + (size_t)p * plane + (size_t)g * 1024) + d % 512,
+                           (int32_t)stage[d]);
+                }
             }
         }
     } else if constexpr (EPI == EPI_SWIGLU) {
         const float sg = PF ? pre.sc : (e.wscale && lane < 32 ? e.wscale[g * GROUP_N + lane] : 1.0f);
         const float su = PF ? pre.sc2 : (e.wscale && lane < 32 ? e.wscale[g * GROUP_N + 32 + lane] : 1.0f);
         if constexpr (MT == 1 && CW == GROUP_N) {
-            if (e.act_fmt == ACT_SPLIT3 && M == 16) {
-                // The group's 16 x 32 outputs, as three bf16 planes in the lane-ordered layout, are six
-                // runs of 32 16-byte words (plane, word v of k-block g / 2, lanes 32 (g % 2) ..): staged in
-                // LDS in that order, then stored as contiguous dwords instead of one 2-byte store per term
-                // and value.
+            if (M == 16 && (e.act_fmt == ACT_SPLIT3 || e.act_fmt == ACT_F32)) {
+                // The group's 16 x 32 outputs in the lane-ordered layout are runs of 32 16-byte words
+                // (word v of k-block g / 2, lanes 32 (g % 2) ..): f32, 4 words per lane; three bf16
+                // planes, 2 words per lane each. They are staged in LDS in that order, then stored as
+                // contiguous dwords instead of one store per value (and term).
                 __shared__ uint32_t stage[6 * 128];
-                uint16_t *st16 = (uint16_t *)stage;
+                const bool f32 = e.act_fmt == ACT_F32;
                 for (int m = wave; m < 16; m += 4) {
                     if (lane < 32) {
                         float gv = tile[m * GN + lane] * rs_s[m];
@@ -521,20 +591,34 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                             gv *= sg;
                             uv *= su;
                         }
-                        uint16_t t[3];
-                        split3(gv / (1.0f + expf(-gv)) * uv, t[0], t[1], t[2]);
-                        const int v = (lane % 16) / 8, ll = m + 16 * (lane / 16), i = lane % 8;
+                        const float act = gv / (1.0f + expf(-gv)) * uv;
+                        const int ll = m + 16 * (lane / 16);
+                        if (f32) {
+                            stage[(((lane % 16) / 4) * 32 + ll) * 4 + lane % 4] = __float_as_uint(act);
+                        } else {
+                            uint16_t t[3];
+                            split3(act, t[0], t[1], t[2]);
+                            const int v = (lane % 16) / 8, i = lane % 8;
 #pragma unroll
-                        for (int p = 0; p < 3; ++p) st16[((p * 2 + v) * 32 + ll) * 8 + i] = t[p];
+                            for (int p = 0; p < 3; ++p) ((uint16_t *)stage)[((p * 2 + v) * 32 + ll) * 8 + i] = t[p];
+                        }
                     }
                 }
                 __syncthreads();
-                const size_t plane = (size_t)e.act_rows * e.act_K;
                 const int kb = g / 2, h = g % 2;
-                for (int d = tid; d < 6 * 128; d += 256) {
-                    const int run = d / 128, p = run / 2, v = run % 2;
-                    const size_t el = (size_t)p * plane + (((size_t)kb * 2 + v) * 64 + 32 * h) * 8;
-                    st_i32((int32_t *)((uint16_t *)e.act_out + el) + d % 128, (int32_t)stage[d]);
+                if (f32) {
+                    for (int d = tid; d < 4 * 128; d += 256) {  // run v: 128 floats
+                        const int v = d / 128;
+                        const size_t el = (((size_t)kb * 4 + v) * 64 + 32 * h) * 4 + d % 128;
+                        st_i32((int32_t *)e.act_out + el, (int32_t)stage[d]);
+                    }
+                } else {
+                    const size_t plane = (size_t)e.act_rows * e.act_K;
+                    for (int d = tid; d < 6 * 128; d += 256) {  // run (p, v): 128 dwords
+                        const int run = d / 128, p = run / 2, v = run % 2;
+                        const size_t el = (size_t)p * plane + (((size_t)kb * 2 + v) * 64 + 32 * h) * 8;
+                        st_i32((int32_t *)((uint16_t *)e.act_out + el) + d % 128, (int32_t)stage[d]);
+                    }
                 }
                 return;
             }

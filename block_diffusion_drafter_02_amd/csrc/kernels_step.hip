@@ -334,7 +334,7 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
     a.n_past = n_past;
     a.x = c->x;
     a.act_a = c->act_a;
-    a.act_fmt = c->act_fmt;
+    a.act_fmt = c->blk_fmt;
     a.act_rows = c->Mmax;
     a.attn_norm0 = c->attn_norm;
     a.ss_a = c->ss_a;
@@ -988,7 +988,7 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     cb.D = c->D;
     cb.block = c->cfg.block;
     cb.act_o = c->act_o;
-    cb.act_fmt = c->act_fmt;
+    cb.act_fmt = c->blk_fmt;
     cb.act_rows = c->Mmax;
     cb.qdim = c->qdim;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(c->H, B, c->D / 32), dim3(256), 0, s, cb);

@@ -100,12 +100,18 @@ hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *code
 // waves are summed through LDS in a fixed order, then the first four waves
 // carry on as above. With it, CW = 32 narrows a workgroup to half a column
 // group (two of its four tiles), which doubles the workgroups without a k-split.
+// Occupancy: a four-wave one-tile workgroup with bf16 or fp8 weights must fit
+// five per compute unit (five waves per SIMD), so that the gate/up grid of
+// about five workgroups per compute unit is resident at once (real-dims bf16
+// gate/up: 93.8 us at four per SIMD, 88.8 us at five); f32 weight tiles need
+// the registers (five per SIMD spills). A 16-wave workgroup needs four per SIMD.
 template <int WT, int AF, int MT, int EPI, int WN, int NWV = 4, int CW = GROUP_N>
-__global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(64 * NWV, NWV == 16 ? 4 : (MT == 1 && WT != DFLASH_F32 ? 5 : 1)) void gemv_kernel(GemvArgs a) {
     static_assert(NWV == 4 || (NWV == 16 && MT == 1 && WN == 1), "wide workgroups take one tile group");
     static_assert(CW == GROUP_N || (CW == 32 && NWV == 16 && EPI != EPI_SWIGLU), "half groups: 16 waves, no SwiGLU");
     constexpr int NV = WTraits<WT>::NV;
-    constexpr int NW = AFTraits<AF>::NW;
+    constexpr int AFO = ActOp<WT, AF>::AFO;  // MFMA operand format
+    constexpr int NW = AFTraits<AFO>::NW;
     constexpr int MP = MT * 16;
     constexpr int TPW = CW / 16;     // 16-column tiles per workgroup and wave column
     constexpr int GN = CW * WN;      // columns per group
@@ -143,9 +149,9 @@ __global__ __launch_bounds__(64 * NWV) void gemv_kernel(GemvArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
             u32x4 av[NW];
-            load_act_lanes<AF>(a.act, a.act_rows, a.K, mt, mt * 16 < M, kb, lane, av);
+            load_act_operands<WT, AF>(a.act, a.act_rows, a.K, mt, mt * 16 < M, kb, lane, av);
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) tile_mfma<WT, AF>(w[t], av, acc[mt][t]);
+            for (int t = 0; t < TPW; ++t) tile_mfma<WT, AFO>(w[t], av, acc[mt][t]);
         }
     }
 
@@ -249,6 +255,10 @@ hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, int CW,
         return launch_gemv_epi<DFLASH_BF16, ACT_SPLIT3>(MT, WN, NWV, CW, grid, a, s);
     if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_SPLIT3)
         return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_SPLIT3>(MT, WN, NWV, CW, grid, a, s);
+    if (wdtype == DFLASH_BF16 && act_fmt == ACT_F32)  // split at load
+        return launch_gemv_epi<DFLASH_BF16, ACT_F32>(MT, WN, NWV, CW, grid, a, s);
+    if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_F32)
+        return launch_gemv_epi<DFLASH_FP8_E4M3, ACT_F32>(MT, WN, NWV, CW, grid, a, s);
     return hipErrorInvalidValue;
 }
 

@@ -41,3 +41,15 @@ def test_attention_occupancy(usage):
     assert attn
     for n, u in attn.items():
         assert u["occupancy"] >= 2, (n, u)
+
+
+def test_gate_up_grid_resident(usage):
+    # The one-tile four-wave GEMV with bf16 or fp8 weights carries the gate/up projection of one sequence,
+    # about five workgroups per compute unit: all of them must be resident at once (five wavefronts per
+    # SIMD), otherwise the last ones start only when earlier ones finish.
+    import re
+    pat = re.compile(r"gemv_kernelILi([12])ELi(\d+)ELi1ELi(\d)ELi1ELi4ELi64E")
+    hits = {n: u for n, u in usage.items() if pat.search(n)}
+    assert hits
+    low = {n: u["occupancy"] for n, u in hits.items() if u["occupancy"] < 5}
+    assert not low, low

@@ -291,19 +291,36 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     const int g = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = g * GROUP_N + lane;
-    for (int i = wave; i < a.block; i += 4) {
-        const int m = b * a.block + i;
-        const int id = a.block_ids ? a.block_ids[m] : (i == 0 ? a.id_last[b] : a.mask_id);
-        float v = 0.0f;
-        if (id >= 0 && id < a.V) {
-            const size_t off = (size_t)id * a.E + n;
-            v = a.aux_dtype == DFLASH_BF16 ? bf16_to_f32(((const uint16_t *)a.tok_embd)[off])
-                                           : ((const float *)a.tok_embd)[off];
+    // four rows per wave at a time: their ids, then their embedding values, then the stores, so the
+    // dependent loads of the rows overlap instead of running one row after another
+    const float wn = a.attn_norm0[n];
+    for (int i0 = wave; i0 < a.block; i0 += 16) {
+        int id[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 4 * r;
+            id[r] = i >= a.block ? -1 : a.block_ids ? a.block_ids[b * a.block + i] : (i == 0 ? a.id_last[b] : a.mask_id);
         }
-        a.x[(size_t)m * a.E + n] = v;
-        write_act(a.act_a, a.act_fmt, a.act_rows, a.E, m, n, v * a.attn_norm0[n]);
-        const float sq = wave_sum(v * v);
-        if (lane == 0) a.ss_a[(size_t)g * a.ss_stride + m] = sq;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            v[r] = 0.0f;
+            if (id[r] >= 0 && id[r] < a.V) {
+                const size_t off = (size_t)id[r] * a.E + n;
+                v[r] = a.aux_dtype == DFLASH_BF16 ? bf16_to_f32(((const uint16_t *)a.tok_embd)[off])
+                                                  : ((const float *)a.tok_embd)[off];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = i0 + 4 * r;
+            if (i >= a.block) break;
+            const int m = b * a.block + i;
+            a.x[(size_t)m * a.E + n] = v[r];
+            write_act(a.act_a, a.act_fmt, a.act_rows, a.E, m, n, v[r] * wn);
+            const float sq = wave_sum(v[r] * v[r]);
+            if (lane == 0) a.ss_a[(size_t)g * a.ss_stride + m] = sq;
+        }
     }
     {  // the rope table's block * D/2 entries, spread over the sequence's workgroups
         const int half = a.D / 2;

@@ -114,7 +114,7 @@ def read_traffic(bytes_per_launch_alg: float):
     return c.get("hbm_bytes_per_launch")
 
 
-GU_KERNEL = "gemv_kernel<1, 0, 1, 2, 1, 4, 64>"  # bf16 weights, split activations, one row tile, SwiGLU, 4 waves, 64 columns
+GU_KERNEL = "gemv_kernel<1, 1, 1, 2, 1, 4, 64>"  # bf16 weights, f32 activations split at load, one row tile, SwiGLU, 4 waves, 64 columns
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 

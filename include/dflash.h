@@ -314,12 +314,15 @@ int dflash_pages_reset(dflash_ctx *ctx, int32_t first, int32_t count, void *stre
  * sequences takes now; -1 for a NULL ctx. */
 int32_t dflash_step_path(const dflash_ctx *ctx, int32_t B);
 
-/* Synchronise `stream` and report whether a dataflow-chain wait gave up since
- * the last check (e.g. when other work holds compute units so that not every
- * chain workgroup is resident): ESTATE if so. The error word is sticky: every
+/* Synchronise `stream` and report whether a bounded device wait gave up since
+ * the last check: a dataflow-chain wait (e.g. when other work holds compute
+ * units so that not every chain workgroup is resident), or the wait of a
+ * per-launch gate/up projection's last k-split for the other splits' partial
+ * tiles (which those splits store right after taking their place, so it ends
+ * unless the device is faulty): ESTATE if so. The error word is sticky: every
  * chain step after the failing one also gives up its waits at once and leaves
  * invalid outputs, until this call reports the error, clears it and resets the
- * chain's flags and counters, after which steps are valid again. OK
+ * flags and split-K counters, after which steps are valid again. OK
  * otherwise. */
 int dflash_check_device(dflash_ctx *ctx, void *stream);
 

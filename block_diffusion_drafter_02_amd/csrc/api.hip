@@ -418,7 +418,11 @@ int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
 int prepare_chain(dflash_ctx &x, hipStream_t s) {
     x.chain_wg = 0;
     x.path = DFLASH_PATH_AUTO;
-    const int nwg = std::min(chain_grid(&x), CHAIN_MAX_WG);
+    // At most three workgroups per compute unit (fewer weight bytes in flight keep the phases' hand-off round
+    // trips short: real-dims bf16 step 1248 us at five per compute unit, 1219 at four, 1169 at three), but at
+    // least one per column group of the widest phase, so every phase fits in one pass.
+    const int cap = std::max(3 * x.cus, std::max(std::max(x.nqkv, x.E), std::max(2 * x.F, x.V)) / GROUP_N);
+    const int nwg = std::min(std::min(chain_grid(&x), CHAIN_MAX_WG), cap);
     if (nwg < 1) return DFLASH_OK;  // the per-launch kernels serve every step
     int rate_khz = 0;
     HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, x.device), "wall clock rate query");

@@ -251,6 +251,8 @@ size_t carve(dflash_ctx &x, char *base) {
     x.partial_floats = pmax;
     x.counters = cv.take<int>(4ull * 2 * gmax);  // half-group launches count per 32 columns
     x.written = cv.take<int>(4ull * 2 * gmax);
+    x.n_xslot = (nqkv / GROUP_N) * 16 * GROUP_N;
+    x.xslot = cv.take<uint32_t>(4ull * x.n_xslot);
     x.pf_sink = cv.take<unsigned>(64);
     x.n_counters = 2 * gmax;
     x.am_key = cv.take<unsigned long long>(8ull * (V / 32) * Mmax);
@@ -408,6 +410,7 @@ int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
     TRY(tile_scales(w->s_lm_head, V, x.s_lm, 0, 0, 0, s));
     HIP_TRY(launch_fill_i32(x.counters, 0, x.n_counters, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.written, 0, x.n_counters, s), "counter reset");
+    HIP_TRY(launch_fill_i32((int *)x.xslot, (int)XSLOT_EMPTY, x.n_xslot, s), "exchange slot reset");
     HIP_TRY(launch_fill_i32(x.am_counter, 0, 1, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.csync, 0, x.n_csync, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.csync, 1, 1, s), "epoch reset");  // epoch 1: flags hold 0 until first set
@@ -576,6 +579,7 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     a.counters = x.counters;
     a.written = x.written;
     a.err = x.csync + 1;
+    a.xslot = (epi.kind == EPI_SCALED && (size_t)G * 16 * GROUP_N <= (size_t)x.n_xslot) ? x.xslot : nullptr;
     a.epi = epi;
     if (G > x.n_counters) return fail(DFLASH_EINVAL, "GEMV with %d column groups exceeds the counter table", G);
     HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.blk_fmt, mt_for(epi.M), WN, nwv, cw, dim3(G, a.S), a, s),
@@ -1059,6 +1063,7 @@ int dflash_check_device(dflash_ctx *x, void *stream) {
         HIP_TRY(launch_fill_i32(x->csync, 1, 1, s), "chain state reset");
         HIP_TRY(launch_fill_i32(x->counters, 0, x->n_counters, s), "counter reset");
         HIP_TRY(launch_fill_i32(x->written, 0, x->n_counters, s), "counter reset");
+        HIP_TRY(launch_fill_i32((int *)x->xslot, (int)XSLOT_EMPTY, x->n_xslot, s), "exchange slot reset");
         HIP_TRY(hipStreamSynchronize(s), "chain state reset");
         return fail(DFLASH_ESTATE, "a bounded wait on the device (the dataflow chain, or a split-K hand-off) gave "
                                    "up; the outputs of the steps since the last check are invalid");

@@ -258,6 +258,9 @@ __device__ __forceinline__ void prefetch_slice(Prefetch f, int p, int P) {
     if (acc == 0x9e3779b9u && f.sink != nullptr) *f.sink = acc;
 }
 
+// Contents of an idle q/k/v exchange slot (scaled_exchange): a NaN payload that a finite partial sum never takes.
+constexpr uint32_t XSLOT_EMPTY = 0x7fbadbadu;
+
 struct GemvArgs {
     const void *W;  // tiled weights
     int N, K;       // output columns (multiple of 64), reduction length (multiple of 64)
@@ -269,6 +272,7 @@ struct GemvArgs {
     int *counters;  // [G] arrivals, zero between launches
     int *written;   // [G] partials stored, zero between launches
     int *err;       // sticky device error word (a bounded wait gave up)
+    uint32_t *xslot;  // [G][16*64] exchange slots of two-split q/k/v launches (XSLOT_EMPTY between launches)
     EpiArgs epi;
 };
 
@@ -350,6 +354,8 @@ struct dflash_ctx {
     size_t partial_floats;
     int *counters;
     int *written;  // split-K partials stored per group (the hand-off of the per-launch kernels)
+    uint32_t *xslot;  // exchange slots of the two-split q/k/v projection, nqkv / 64 groups x 1024
+    int n_xslot;
     int n_counters;
     unsigned long long *am_key;  // [G][ss_stride] per-group argmax keys (argmax_key)
     int *am_counter;

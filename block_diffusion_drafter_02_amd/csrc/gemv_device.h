@@ -451,6 +451,52 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs &e, int g, EpiPre &p)
     }
 }
 
+// Two k-splits meeting through per-element exchange slots (a q/k/v group: 16
+// rows x 64 columns, whose epilogue is per element). Each split swaps its
+// partial value into the element's slot, which holds XSLOT_EMPTY between
+// launches: the split that receives XSLOT_EMPTY is first and leaves its value
+// there; the other receives it, adds (IEEE addition is commutative, so the sum
+// does not depend on which split came first), re-arms the slot and writes the
+// output element. One device round trip instead of the counter hand-off's
+// store, wait, counter and load.
+template <bool PF>
+__device__ __forceinline__ void scaled_exchange(const EpiArgs &e, int g, const float *tile, float *rs_s, uint32_t *slot,
+                                                const EpiPre &pre) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int M = e.M;
+    {  // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps), as in gemv_epilogue
+        const int m = tid >> 4, sub = tid & 15;
+        float part = 0.0f;
+        if (PF && pre.ss_ok) {
+#pragma unroll
+            for (int j = 0; j < EpiPre::SSN; ++j) part += pre.ss[j];
+        } else if (e.ss != nullptr && m < M) {
+            for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
+        }
+        for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+        if (sub == 0) rs_s[m] = (e.ss != nullptr && m < M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
+    }
+    __syncthreads();
+    const int n = g * GROUP_N + lane;
+    const float sc = PF ? pre.sc : (e.wscale ? e.wscale[n] : 1.0f);
+    uint32_t old[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)  // all four exchanges in flight together
+        old[k] = __hip_atomic_exchange(slot + tid + 256 * k, __float_as_uint(tile[tid + 256 * k]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (old[k] == XSLOT_EMPTY) continue;  // first split: its value waits in the slot
+        __hip_atomic_store(slot + tid + 256 * k, XSLOT_EMPTY, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int m = wave + 4 * k;  // element tid + 256 k of the [16][64] tile
+        if (m < M) {
+            float v = (__uint_as_float(old[k]) + tile[tid + 256 * k]) * rs_s[m];
+            if (e.wscale) v *= sc;
+            st_f32(e.out + (size_t)m * e.ld_out + n, v);
+        }
+    }
+}
+
 // Argmax across the groups of one launch: every group stores its (value,
 // column) maximum of row m as one 64-bit key that orders by value, then by
 // lower column (values that compare equal, +0 and -0 among them, give the same

@@ -193,6 +193,12 @@ __global__ __launch_bounds__(64 * NWV, NWV == 16 ? 4 : (MT == 1 && WT != DFLASH_
     }
     if (a.S > 1) {
         constexpr int TE = MP * GN;
+        if constexpr (NWV == 16 && EPI == EPI_SCALED && CW == GROUP_N) {
+            if (a.S == 2 && a.xslot) {  // per-element epilogue: the splits meet through exchange slots
+                scaled_exchange<PF>(a.epi, g, tile, rs_s, a.xslot + (size_t)g * TE, pre);
+                return;
+            }
+        }
         // Many four-wave workgroups: only the earlier arrivals store their partial
         // (gate/up at the real dimensions: 96.5 -> 94.9 us). One workgroup per
         // compute unit: the splits of a group finish together, so the last one

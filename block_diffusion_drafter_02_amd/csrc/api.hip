@@ -251,7 +251,7 @@ size_t carve(dflash_ctx &x, char *base) {
     x.partial_floats = pmax;
     x.counters = cv.take<int>(4ull * 2 * gmax);  // half-group launches count per 32 columns
     x.written = cv.take<int>(4ull * 2 * gmax);
-    x.n_xslot = (nqkv / GROUP_N) * 16 * GROUP_N;
+    x.n_xslot = (std::max(nqkv, V) / GROUP_N) * 16 * GROUP_N;  // q/k/v and lm_head groups
     x.xslot = cv.take<uint32_t>(4ull * x.n_xslot);
     x.pf_sink = cv.take<unsigned>(64);
     x.n_counters = 2 * gmax;
@@ -579,7 +579,11 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
     a.counters = x.counters;
     a.written = x.written;
     a.err = x.csync + 1;
-    a.xslot = (epi.kind == EPI_SCALED && (size_t)G * 16 * GROUP_N <= (size_t)x.n_xslot) ? x.xslot : nullptr;
+    // exchange slots for the per-element epilogues (q/k/v; lm_head, whose argmax keys take 2G slots)
+    a.xslot = ((epi.kind == EPI_SCALED || (epi.kind == EPI_LOGITS && 2 * G <= x.V / 32)) &&
+               (size_t)G * 16 * GROUP_N <= (size_t)x.n_xslot)
+                  ? x.xslot
+                  : nullptr;
     a.epi = epi;
     if (G > x.n_counters) return fail(DFLASH_EINVAL, "GEMV with %d column groups exceeds the counter table", G);
     HIP_TRY(launch_gemv(x.cfg.weight_dtype, x.blk_fmt, mt_for(epi.M), WN, nwv, cw, dim3(G, a.S), a, s),

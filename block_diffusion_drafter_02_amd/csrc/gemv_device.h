@@ -459,26 +459,27 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs &e, int g, EpiPre &p)
 // does not depend on which split came first), re-arms the slot and writes the
 // output element. One device round trip instead of the counter hand-off's
 // store, wait, counter and load.
+// rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps) of one 16-row tile into LDS (256 threads, as in gemv_epilogue)
 template <bool PF>
-__device__ __forceinline__ void scaled_exchange(const EpiArgs &e, int g, const float *tile, float *rs_s, uint32_t *slot,
-                                                const EpiPre &pre) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int M = e.M;
-    {  // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps), as in gemv_epilogue
-        const int m = tid >> 4, sub = tid & 15;
-        float part = 0.0f;
-        if (PF && pre.ss_ok) {
+__device__ __forceinline__ void tile_row_scales(const EpiArgs &e, float *rs_s, const EpiPre &pre) {
+    const int tid = threadIdx.x;
+    const int m = tid >> 4, sub = tid & 15;
+    float part = 0.0f;
+    if (PF && pre.ss_ok) {
 #pragma unroll
-            for (int j = 0; j < EpiPre::SSN; ++j) part += pre.ss[j];
-        } else if (e.ss != nullptr && m < M) {
-            for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
-        }
-        for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-        if (sub == 0) rs_s[m] = (e.ss != nullptr && m < M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
+        for (int j = 0; j < EpiPre::SSN; ++j) part += pre.ss[j];
+    } else if (e.ss != nullptr && m < e.M) {
+        for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
     }
+    for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (sub == 0) rs_s[m] = (e.ss != nullptr && m < e.M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
     __syncthreads();
-    const int n = g * GROUP_N + lane;
-    const float sc = PF ? pre.sc : (e.wscale ? e.wscale[n] : 1.0f);
+}
+
+// Both splits swap their four elements into the slots at once; returns, per element, whether this split
+// received the other's value (and so owns the element) and the sum in v[k]. Owners re-arm their slots.
+__device__ __forceinline__ void exchange_tile(const float *tile, uint32_t *slot, float (&v)[4], bool (&own)[4]) {
+    const int tid = threadIdx.x;
     uint32_t old[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)  // all four exchanges in flight together
@@ -486,13 +487,30 @@ __device__ __forceinline__ void scaled_exchange(const EpiArgs &e, int g, const f
                                        __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        if (old[k] == XSLOT_EMPTY) continue;  // first split: its value waits in the slot
-        __hip_atomic_store(slot + tid + 256 * k, XSLOT_EMPTY, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        own[k] = old[k] != XSLOT_EMPTY;
+        v[k] = own[k] ? __uint_as_float(old[k]) + tile[tid + 256 * k] : 0.0f;
+        if (own[k]) __hip_atomic_store(slot + tid + 256 * k, XSLOT_EMPTY, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <bool PF>
+__device__ __forceinline__ void scaled_exchange(const EpiArgs &e, int g, const float *tile, float *rs_s, uint32_t *slot,
+                                                const EpiPre &pre) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int M = e.M;
+    tile_row_scales<PF>(e, rs_s, pre);
+    const int n = g * GROUP_N + lane;
+    const float sc = PF ? pre.sc : (e.wscale ? e.wscale[n] : 1.0f);
+    float v[4];
+    bool own[4];
+    exchange_tile(tile, slot, v, own);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
         const int m = wave + 4 * k;  // element tid + 256 k of the [16][64] tile
-        if (m < M) {
-            float v = (__uint_as_float(old[k]) + tile[tid + 256 * k]) * rs_s[m];
-            if (e.wscale) v *= sc;
-            st_f32(e.out + (size_t)m * e.ld_out + n, v);
+        if (own[k] && m < M) {
+            float r = v[k] * rs_s[m];
+            if (e.wscale) r *= sc;
+            st_f32(e.out + (size_t)m * e.ld_out + n, r);
         }
     }
 }
@@ -511,6 +529,101 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int col) {
     return ((unsigned long long)ord << 32) | (uint32_t)~(uint32_t)col;
 }
 __device__ __forceinline__ int argmax_key_index(unsigned long long k) { return (int)~(uint32_t)(k & 0xffffffffull); }
+
+// The argmax's last stage: once a workgroup's keys for rows 0..M-1 are stored in key slots 0..NK-1
+// (am_key[slot][row]), it counts itself in; the last of the NK arrivals takes every row's largest key,
+// writes the drafts, runs the acceptance scan and re-arms the counter.
+__device__ __forceinline__ void argmax_finish(const EpiArgs &e, int NK, int *flag_s, int *best_s) {
+    const int tid = threadIdx.x;
+    const int M = e.M;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __syncthreads();
+    if (tid == 0)
+        *flag_s = __hip_atomic_fetch_add(e.am_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == NK - 1;
+    __syncthreads();
+    if (!*flag_s) return;
+    // every group's key is in: 16 threads per row take the largest key of the
+    // groups sub, sub + 16, ... with the loads of a batch issued together,
+    // then a 16-lane reduction (the order does not change a maximum)
+    constexpr int KU = 8;
+    for (int m0 = 0; m0 < M; m0 += 16) {
+        const int m = m0 + (tid >> 4), sub = tid & 15;
+        unsigned long long best = 0ull;
+        if (m < M)
+            for (int g0 = sub; g0 < NK; g0 += 16 * KU) {
+                unsigned long long k[KU];
+#pragma unroll
+                for (int u = 0; u < KU; ++u)
+                    k[u] = g0 + 16 * u < NK ? __hip_atomic_load(e.am_key + (size_t)(g0 + 16 * u) * e.ss_stride + m,
+                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                           : 0ull;
+#pragma unroll
+                for (int u = 0; u < KU; ++u) best = k[u] > best ? k[u] : best;
+            }
+        for (int o = 8; o > 0; o >>= 1) {
+            const unsigned long long ok = __shfl_xor(best, o, 64);
+            best = ok > best ? ok : best;
+        }
+        if (sub == 0 && m < M) {
+            const int bi = argmax_key_index(best);
+            best_s[m] = bi;
+            const int b = m / e.block, i = m % e.block;
+            if (i > 0 && i < e.gamma) st_i32(e.drafts + (size_t)b * (e.gamma - 1) + i - 1, bi);
+        }
+    }
+    __syncthreads();
+    if (e.target != nullptr && tid < M / e.block) {
+        const int b = tid;
+        int n = 0;
+        while (n < e.gamma - 1 && best_s[b * e.block + 1 + n] == e.target[(size_t)b * (e.gamma - 1) + n]) ++n;
+        st_i32(e.n_ok + b, n);
+    }
+    if (tid == 0) __hip_atomic_store(e.am_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The lm_head's two k-splits meet through exchange slots (as q/k/v): each split
+// finishes the logits it owns, and stores per row the argmax key of those
+// columns in key slot 2g + s (0 for a row where it owns none), so the argmax's
+// last stage reduces 2G key slots. The logits and the maximum do not depend on
+// which split owns which element.
+template <bool PF>
+__device__ __forceinline__ void logits_exchange(const EpiArgs &e, int g, int G, int s, const float *tile, float *rs_s,
+                                                uint32_t *slot, const EpiPre &pre, int *flag_s, int *best_s) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int M = e.M;
+    tile_row_scales<PF>(e, rs_s, pre);
+    const int n = g * GROUP_N + lane;
+    const float sc = PF ? pre.sc : (e.wscale ? e.wscale[n] : 1.0f);
+    float v[4];
+    bool own[4];
+    exchange_tile(tile, slot, v, own);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int m = wave + 4 * k;
+        if (m >= M) continue;  // uniform over the wave
+        unsigned long long key = 0ull;
+        if (own[k]) {
+            float r = v[k] * rs_s[m];
+            if (e.wscale) r *= sc;
+            st_f32(e.out + (size_t)m * e.ld_out + n, r);
+            if (e.temp > 0.0f) {  // the draft is a sample: the argmax runs on logit / T + Gumbel noise
+                const int b = m / e.block;
+                r = r / e.temp + gumbel_noise(e.seed_lo, e.seed_hi, b, e.n_past[b] + m % e.block, n);
+            }
+            key = argmax_key(r, n);
+        }
+        for (int o = 32; o > 0; o >>= 1) {
+            const unsigned long long ok = __shfl_xor(key, o, 64);
+            key = ok > key ? ok : key;
+        }
+        if (lane == 0)
+            __hip_atomic_store(e.am_key + (size_t)(2 * g + s) * e.ss_stride + m, key, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    argmax_finish(e, 2 * G, flag_s, best_s);
+}
 
 // CW: columns of group g (64, or 32 for half groups; lanes >= CW idle). The
 // G groups of one launch write ss_out rows 0..G-1.
@@ -709,50 +822,6 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                 __hip_atomic_store(e.am_key + (size_t)g * e.ss_stride + m, argmax_key(bv, bi), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __syncthreads();
-        if (tid == 0)
-            *flag_s = __hip_atomic_fetch_add(e.am_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1;
-        __syncthreads();
-        if (!*flag_s) return;
-        // every group's key is in: 16 threads per row take the largest key of the
-        // groups sub, sub + 16, ... with the loads of a batch issued together,
-        // then a 16-lane reduction (the order does not change a maximum)
-        constexpr int KU = 8;
-        for (int m0 = 0; m0 < M; m0 += 16) {
-            const int m = m0 + (tid >> 4), sub = tid & 15;
-            unsigned long long best = 0ull;
-            if (m < M)
-                for (int g0 = sub; g0 < G; g0 += 16 * KU) {
-                    unsigned long long k[KU];
-#pragma unroll
-                    for (int u = 0; u < KU; ++u)
-                        k[u] = g0 + 16 * u < G ? __hip_atomic_load(e.am_key + (size_t)(g0 + 16 * u) * e.ss_stride + m,
-                                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                               : 0ull;
-#pragma unroll
-                    for (int u = 0; u < KU; ++u) best = k[u] > best ? k[u] : best;
-                }
-            for (int o = 8; o > 0; o >>= 1) {
-                const unsigned long long ok = __shfl_xor(best, o, 64);
-                best = ok > best ? ok : best;
-            }
-            if (sub == 0 && m < M) {
-                const int bi = argmax_key_index(best);
-                best_s[m] = bi;
-                const int b = m / e.block, i = m % e.block;
-                if (i > 0 && i < e.gamma) st_i32(e.drafts + (size_t)b * (e.gamma - 1) + i - 1, bi);
-            }
-        }
-        __syncthreads();
-        if (e.target != nullptr && tid < M / e.block) {
-            const int b = tid;
-            int n = 0;
-            while (n < e.gamma - 1 && best_s[b * e.block + 1 + n] == e.target[(size_t)b * (e.gamma - 1) + n]) ++n;
-            st_i32(e.n_ok + b, n);
-        }
-        if (tid == 0) __hip_atomic_store(e.am_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        argmax_finish(e, G, flag_s, best_s);
     }
 }

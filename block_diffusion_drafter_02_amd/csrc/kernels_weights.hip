@@ -199,6 +199,12 @@ __global__ __launch_bounds__(64 * NWV, NWV == 16 ? 4 : (MT == 1 && WT != DFLASH_
                 return;
             }
         }
+        if constexpr (NWV == 16 && EPI == EPI_LOGITS && CW == GROUP_N) {
+            if (a.S == 2 && a.xslot) {
+                logits_exchange<PF>(a.epi, g, G, s, tile, rs_s, a.xslot + (size_t)g * TE, pre, &flag_s, best_s);
+                return;
+            }
+        }
         // Many four-wave workgroups: only the earlier arrivals store their partial
         // (gate/up at the real dimensions: 96.5 -> 94.9 us). One workgroup per
         // compute unit: the splits of a group finish together, so the last one

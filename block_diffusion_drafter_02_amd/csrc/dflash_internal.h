@@ -489,12 +489,15 @@ hipError_t attention_set_smem_limit();
 // sequence, whose chunks alone leave most compute units idle; 256 threads for
 // several sequences, so that two workgroups share a compute unit.
 inline int attn_threads(int B) { return B == 1 ? 512 : 256; }
-// ring slots per attention chunk (one workgroup per chunk and kv head): for a
-// bf16 ring 128 with 512 threads (64 when the window is not a multiple of 128)
-// and 64 with 256; 32 for an f32 ring (its values take three planes of LDS)
+// ring slots per attention chunk (one workgroup per chunk and kv head): with 512
+// threads 128 (64, then 32, when the window is not a multiple of 128); with 256
+// threads 64 for a bf16 ring and 32 for an f32 ring (whose values take three
+// planes of LDS). For an f32 ring 128 slots measured fastest at the real
+// dimensions (step 1950 us at 32 slots, 1909 at 64, 1872 at 128): fewer chunk
+// partials for the combine launch to merge.
 inline int attn_chunk(int ring_dtype, int W, int B) {
-    if (ring_dtype != DFLASH_BF16) return 32;
-    return attn_threads(B) == 512 && W % 128 == 0 ? 128 : 64;
+    if (attn_threads(B) == 512) return W % 128 == 0 ? 128 : (W % 64 == 0 ? 64 : 32);
+    return ring_dtype == DFLASH_BF16 ? 64 : 32;
 }
 hipError_t launch_accept(const int32_t *drafts, const int32_t *target, int B, int n, int32_t *n_ok, hipStream_t s,
                          int32_t *bonus = nullptr);

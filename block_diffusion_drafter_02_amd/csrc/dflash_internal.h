@@ -214,6 +214,9 @@ struct EpiArgs {
     int gamma;  // block width in use: drafts and acceptance cover rows 1..gamma-1
     // EPI_LOGITS: argmax across groups
     unsigned long long *am_key;  // [G][ss_stride] per-group argmax keys (argmax_key)
+    int row0;      // first row of this tile within the step's rows (argmax keys, noise, drafts); 0 if whole
+    int rows_all;  // rows of the whole step for the argmax's last stage (0: M)
+    int arrivals;  // workgroups that count in for the argmax's last stage (0: the key slots)
     int *am_counter;
     int32_t *drafts;      // [B][gamma-1]
     const int32_t *target;  // [B][gamma-1] or null

@@ -530,18 +530,20 @@ __device__ __forceinline__ unsigned long long argmax_key(float v, int col) {
 }
 __device__ __forceinline__ int argmax_key_index(unsigned long long k) { return (int)~(uint32_t)(k & 0xffffffffull); }
 
-// The argmax's last stage: once a workgroup's keys for rows 0..M-1 are stored in key slots 0..NK-1
-// (am_key[slot][row]), it counts itself in; the last of the NK arrivals takes every row's largest key,
-// writes the drafts, runs the acceptance scan and re-arms the counter.
+// The argmax's last stage: once a workgroup's keys for its rows are stored in key slots 0..NK-1
+// (am_key[slot][row]), it counts itself in; the last of the arrivals (NK unless e.arrivals is set) takes
+// the largest key of every row of the step (e.rows_all, else M), writes the drafts, runs the acceptance
+// scan and re-arms the counter. best_s holds one int per row of the step.
 __device__ __forceinline__ void argmax_finish(const EpiArgs &e, int NK, int *flag_s, int *best_s) {
     const int tid = threadIdx.x;
-    const int M = e.M;
+    const int M = e.rows_all ? e.rows_all : e.M;
+    const int arrivals = e.arrivals ? e.arrivals : NK;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
     if (tid == 0)
-        *flag_s = __hip_atomic_fetch_add(e.am_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == NK - 1;
+        *flag_s = __hip_atomic_fetch_add(e.am_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == arrivals - 1;
     __syncthreads();
     if (!*flag_s) return;
     // every group's key is in: 16 threads per row take the largest key of the
@@ -798,14 +800,15 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
         const int n = g * CW + lane;
         const float sc = PF ? pre.sc : (e.wscale && col_ok ? e.wscale[n] : 1.0f);
         for (int m = wave; m < M; m += 4) {
+            const int mg = e.row0 + m;  // row within the step
             float v = -INFINITY;
             if (col_ok) {
                 v = tile[m * GN + lane] * rs_s[m];
                 if (e.wscale) v *= sc;
                 st_f32(e.out + (size_t)m * e.ld_out + n, v);
                 if (e.temp > 0.0f) {  // the draft is a sample: the argmax runs on logit / T + Gumbel noise
-                    const int b = m / e.block;
-                    v = v / e.temp + gumbel_noise(e.seed_lo, e.seed_hi, b, e.n_past[b] + m % e.block, n);
+                    const int b = mg / e.block;
+                    v = v / e.temp + gumbel_noise(e.seed_lo, e.seed_hi, b, e.n_past[b] + mg % e.block, n);
                 }
             }
             float bv = v;
@@ -819,7 +822,7 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                 }
             }
             if (lane == 0)
-                __hip_atomic_store(e.am_key + (size_t)g * e.ss_stride + m, argmax_key(bv, bi), __ATOMIC_RELAXED,
+                __hip_atomic_store(e.am_key + (size_t)g * e.ss_stride + mg, argmax_key(bv, bi), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
         argmax_finish(e, G, flag_s, best_s);

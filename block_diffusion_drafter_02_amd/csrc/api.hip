@@ -664,9 +664,9 @@ int stage_lm(const dflash_ctx &x, int M, float *logits, int32_t *drafts, const i
 int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const int32_t *block_ids,
              const int32_t *n_past, int B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
              hipStream_t s) {
-    // the per-launch kernels and the batched projections: f32 activations split at load (4 bytes per value
-    // written and read instead of 6); the chain reads three bf16 planes
-    x.blk_fmt = use_chain(x, B) ? x.act_fmt : ACT_F32;
+    // one sequence on the per-launch kernels: f32 activations split at load (4 bytes per value written and
+    // read instead of 6); the batched projections and the chain read three bf16 planes
+    x.blk_fmt = (B == 1 && !use_chain(x, B)) ? ACT_F32 : x.act_fmt;
     if (use_chain(x, B)) {
         // dataflow chain: head (embed + q/k/v of layer 0); per layer attention, then Wo .. q/k/v(l+1) or lm_head
         ChainIO io{id_last, block_ids, n_past, logits, drafts, target, n_ok, x.gamma, x.temp, (uint32_t)x.seed,

@@ -307,15 +307,10 @@ constexpr int GEMM_BM = 128, GEMM_GROUPS = 4, GEMM_THREADS = 512;
 // ALANES: the activations are in the block rows' lane-ordered layout (act_offset;
 // planes of act_rows rows) instead of row-major; a 16-row k-block tile of a plane
 // is then one contiguous run of 64-lane words, staged to LDS in the same order.
-// SPLIT: lane-ordered f32 activations feeding bf16 or fp8 weights; the staging
-// splits them into the three bf16 terms, so LDS holds the three-plane layout
-// (a k-block reads 32 KB of activations instead of 48).
 template <int WT, int AF, bool ALANES>
 struct GemmShape {
-    static constexpr bool SPLIT = ALANES && AF == ACT_F32 && WT != DFLASH_F32;
-    static constexpr int AFL = SPLIT ? ACT_SPLIT3 : AF;  // activation format in LDS
     static constexpr int NV = WTraits<WT>::NV;
-    static constexpr int TERMS = GemmA<AFL>::TERMS, ES = GemmA<AFL>::ES, ROWB = GemmA<AFL>::ROWB;
+    static constexpr int TERMS = GemmA<AF>::TERMS, ES = GemmA<AF>::ES, ROWB = GemmA<AF>::ROWB;
     static constexpr int WPR = 64 * ES / 16;                     // 16-byte words per row of a k-block
     static constexpr int A_WORDS = TERMS * GEMM_BM * WPR;        // per k-block
     static constexpr int A_PT = A_WORDS / GEMM_THREADS;          // per thread
@@ -330,9 +325,7 @@ struct GemmShape {
 template <int WT, int AF, bool ALANES>
 __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     using Sh = GemmShape<WT, AF, ALANES>;
-    constexpr bool SPLIT = Sh::SPLIT;
-    constexpr int AFL = Sh::AFL;
-    constexpr int NV = Sh::NV, NW = AFTraits<AFL>::NW, TERMS = Sh::TERMS, ES = Sh::ES, ROWB = Sh::ROWB;
+    constexpr int NV = Sh::NV, NW = AFTraits<AF>::NW, TERMS = Sh::TERMS, ES = Sh::ES, ROWB = Sh::ROWB;
     constexpr int BM = GEMM_BM, WPR = Sh::WPR, A_PT = Sh::A_PT, B_GROUP = Sh::B_GROUP, B_PT = Sh::B_PT;
     constexpr int LW = Sh::LW;
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -356,17 +349,8 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     float *out = a.out + (size_t)sp * a.M * a.N;
     const bool wave_live = g0 + wc < G;
 
-    u32x4 sa[SPLIT ? 4 : A_PT], sb[B_PT];
+    u32x4 sa[A_PT], sb[B_PT];
     auto load_stage = [&](int kb) {
-        if constexpr (SPLIT) {
-            // thread t stages lane t % 64 of 16-row tile t / 64: its four f32 words of the k-block
-            static_assert(GEMM_THREADS == 8 * 64, "one thread per (row tile, lane)");
-            const int mtg = r0 / 16 + tid / 64;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                sa[v] = mtg * 16 < a.M ? ((const u32x4 *)a.act)[((size_t)mtg * KB + kb) * 256 + v * 64 + lane]
-                                       : u32x4{0u, 0u, 0u, 0u};
-        } else {
 #pragma unroll
         for (int i = 0; i < A_PT; ++i) {
             const int w = tid + GEMM_THREADS * i;
@@ -390,7 +374,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
                     sa[i] = u32x4{0u, 0u, 0u, 0u};
             }
         }
-        }
 #pragma unroll
         for (int i = 0; i < B_PT; ++i) {
             const int w = tid + GEMM_THREADS * i;
@@ -402,27 +385,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
         }
     };
     auto store_stage = [&]() {
-        if constexpr (SPLIT) {
-            // f32 words 0-1 hold elements 0-7 (word 0 of each term), words 2-3 elements 8-15 (word 1)
-            const int mt = tid / 64;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                u32x4 t0, t1, t2;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 &f = sa[2 * h + i / 2];
-                    const float x0 = __uint_as_float(f[(2 * i) % 4]), x1 = __uint_as_float(f[(2 * i + 1) % 4]);
-                    uint32_t w0, w1, w2;
-                    split3_pair(x0, x1, w0, w1, w2);
-                    t0[i] = w0;
-                    t1[i] = w1;
-                    t2[i] = w2;
-                }
-                ((u32x4 *)A_s)[((0 * 8 + mt) * 2 + h) * 64 + lane] = t0;
-                ((u32x4 *)A_s)[((1 * 8 + mt) * 2 + h) * 64 + lane] = t1;
-                ((u32x4 *)A_s)[((2 * 8 + mt) * 2 + h) * 64 + lane] = t2;
-            }
-        } else {
 #pragma unroll
         for (int i = 0; i < A_PT; ++i) {
             const int w = tid + GEMM_THREADS * i;
@@ -432,7 +394,6 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
                 const int t = w / (BM * WPR), rem = w % (BM * WPR), row = rem / WPR, cw = rem % WPR;
                 *(u32x4 *)(A_s + (t * BM + row) * ROWB + cw * 16) = sa[i];
             }
-        }
         }
 #pragma unroll
         for (int i = 0; i < B_PT; ++i) B_s[tid + GEMM_THREADS * i] = sb[i];
@@ -465,7 +426,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 #pragma unroll
                         for (int v = 0; v < LW; ++v)
                             av[t * LW + v] = ((const u32x4 *)A_s)[((t * 8 + mt) * LW + v) * 64 + lane];
-                } else if constexpr (AFL == ACT_F32) {
+                } else if constexpr (AF == ACT_F32) {
                     const int row = mt * 16 + (lane & 15);
 #pragma unroll
                     for (int v = 0; v < 4; ++v) av[v] = *(const u32x4 *)(A_s + row * ROWB + (lane >> 4) * 64 + v * 16);
@@ -478,7 +439,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
                             av[2 * t + h] = *(const u32x4 *)(A_s + (t * BM + row) * ROWB + (lane >> 4) * 32 + h * 16);
                 }
 #pragma unroll
-                for (int t = 0; t < 4; ++t) tile_mfma<WT, AFL>(w[t], av, acc[rt][t]);
+                for (int t = 0; t < 4; ++t) tile_mfma<WT, AF>(w[t], av, acc[rt][t]);
             }
         }
         __syncthreads();
@@ -527,8 +488,6 @@ hipError_t gemm_set_smem_limit() {
     if ((e = gemm_attr<DFLASH_BF16, ACT_SPLIT3, false>()) != hipSuccess) return e;
     if ((e = gemm_attr<DFLASH_BF16, ACT_SPLIT3, true>()) != hipSuccess) return e;
     if ((e = gemm_attr<DFLASH_FP8_E4M3, ACT_SPLIT3, false>()) != hipSuccess) return e;
-    if ((e = gemm_attr<DFLASH_BF16, ACT_F32, true>()) != hipSuccess) return e;
-    if ((e = gemm_attr<DFLASH_FP8_E4M3, ACT_F32, true>()) != hipSuccess) return e;
     return gemm_attr<DFLASH_FP8_E4M3, ACT_SPLIT3, true>();
 }
 
@@ -542,9 +501,6 @@ hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s
     if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_SPLIT3)
         return lanes ? gemm_go<DFLASH_FP8_E4M3, ACT_SPLIT3, true>(a, s)
                      : gemm_go<DFLASH_FP8_E4M3, ACT_SPLIT3, false>(a, s);
-    // lane-ordered f32 block rows, split into the three terms as they are staged
-    if (wdtype == DFLASH_BF16 && act_fmt == ACT_F32 && lanes) return gemm_go<DFLASH_BF16, ACT_F32, true>(a, s);
-    if (wdtype == DFLASH_FP8_E4M3 && act_fmt == ACT_F32 && lanes) return gemm_go<DFLASH_FP8_E4M3, ACT_F32, true>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -318,7 +318,10 @@ struct GemmShape {
     static constexpr int B_WORDS = GEMM_GROUPS * B_GROUP;
     static constexpr int B_PT = B_WORDS / GEMM_THREADS;
     static constexpr int A_LDS = ALANES ? A_WORDS * 16 : TERMS * GEMM_BM * ROWB;
-    static constexpr int LDS = A_LDS + B_WORDS * 16;
+    static constexpr int STAGE = A_LDS + B_WORDS * 16;
+    // two LDS stages where they fit the compute unit's 160 KB
+    static constexpr bool DB = 2 * STAGE <= 160 * 1024;
+    static constexpr int LDS = DB ? 2 * STAGE : STAGE;
     static constexpr int LW = ES == 2 ? 2 : 4;                   // lane-ordered words per lane per tile
 };
 
@@ -331,6 +334,10 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     char *A_s = lds;
     u32x4 *B_s = (u32x4 *)(lds + Sh::A_LDS);
+    auto use_stage = [&](int buf) {
+        A_s = lds + buf * Sh::STAGE;
+        B_s = (u32x4 *)(lds + buf * Sh::STAGE + Sh::A_LDS);
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wr = wave >> 2, wc = wave & 3;  // rows 64wr.., column group g0 + wc
@@ -405,11 +412,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[rt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    load_stage(kb0);
-    store_stage();
-    __syncthreads();
-    for (int kb = kb0; kb < kb1; ++kb) {
-        if (kb + 1 < kb1) load_stage(kb + 1);
+    auto mult_stage = [&]() {
         if (wave_live) {
             u32x4 w[4][NV];
 #pragma unroll
@@ -442,10 +445,39 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
                 for (int t = 0; t < 4; ++t) tile_mfma<WT, AF>(w[t], av, acc[rt][t]);
             }
         }
+    };
+    if constexpr (Sh::DB) {
+        // LDS stage (kb - kb0) % 2 holds kb while k-block kb + 1 goes from the
+        // registers to the other stage and the loads of kb + 2 are in flight:
+        // the HBM latency of a k-block is hidden behind a whole k-block of MFMAs
+        load_stage(kb0);
+        use_stage(0);
+        store_stage();
+        if (kb0 + 1 < kb1) load_stage(kb0 + 1);
         __syncthreads();
-        if (kb + 1 < kb1) {
-            store_stage();
+        for (int kb = kb0; kb < kb1; ++kb) {
+            const int c = (kb - kb0) & 1;
+            if (kb + 1 < kb1) {
+                use_stage(c ^ 1);
+                store_stage();  // the other stage was last read before the previous barrier
+            }
+            if (kb + 2 < kb1) load_stage(kb + 2);
+            use_stage(c);
+            mult_stage();
             __syncthreads();
+        }
+    } else {
+        load_stage(kb0);
+        store_stage();
+        __syncthreads();
+        for (int kb = kb0; kb < kb1; ++kb) {
+            if (kb + 1 < kb1) load_stage(kb + 1);
+            mult_stage();
+            __syncthreads();
+            if (kb + 1 < kb1) {
+                store_stage();
+                __syncthreads();
+            }
         }
     }
     if (!wave_live) return;

@@ -713,19 +713,23 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // ring key: a written slot whose position lies in [qpos - W + 1, qpos]; block key: < gamma
-                const bool vis = kt < nkt && (is_block ? key0 + i < a.gamma
-                                                       : kpv[i] >= 0 && (unsigned)(qpos - kpv[i]) < (unsigned)a.W);
-                if (!vis) st[kt][i] = -INFINITY;
+                // (evaluated without short-circuits, so the mask is selects rather than branches)
+                const bool ring_vis = (kpv[i] >= 0) & ((unsigned)(qpos - kpv[i]) < (unsigned)a.W);
+                const bool vis = (kt < nkt) & (is_block ? key0 + i < a.gamma : ring_vis);
+                st[kt][i] = vis ? st[kt][i] : -INFINITY;
                 mx = fmaxf(mx, st[kt][i]);
             }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // exp(-inf) is 0, so a masked key needs no test; with no visible key (mx
+        // = -inf) every score is -inf and 0 stands in for the maximum
+        const float mxs = mx == -INFINITY ? 0.0f : mx;
 #pragma clang loop unroll(full)
         for (int kt = 0; kt < HKT; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = (mx == -INFINITY || st[kt][i] == -INFINITY) ? 0.0f : expf(st[kt][i] - mx);
+                const float p = expf(st[kt][i] - mxs);
                 st[kt][i] = p;
                 lsum += p;
             }
@@ -819,9 +823,9 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
     {
         const float *xp = xch + ((size_t)hh * 64 + lane) * XS;
         const float m2 = xp[DT * 4], l2 = xp[DT * 4 + 1];
-        const float mn = fmaxf(mx, m2);
-        const float a1 = mn == -INFINITY ? 0.0f : expf(mx - mn);
-        const float a2 = mn == -INFINITY ? 0.0f : expf(m2 - mn);
+        const float mn = fmaxf(mx, m2), mns = mn == -INFINITY ? 0.0f : mn;  // exp(-inf) = 0, as above
+        const float a1 = expf(mx - mns);
+        const float a2 = expf(m2 - mns);
         lsum = lsum * a1 + l2 * a2;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)

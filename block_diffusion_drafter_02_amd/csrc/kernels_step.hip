@@ -925,9 +925,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombArgs a) {
         lsum *= alpha;
         o0 *= alpha;
         o1 *= alpha;
+        // a chunk without visible keys (m = -inf, sum and output 0) gets weight
+        // exp(-inf) = 0 and adds exactly nothing, so it needs no test
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-            if (c0 + u < nc && mlb[u].x != -INFINITY) {  // a chunk without visible keys adds nothing
+            if (c0 + u < nc) {
                 const float w = expf(mlb[u].x - mn);
                 lsum += w * mlb[u].y;
                 o0 += w * ovb[u].x;

@@ -514,8 +514,8 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
     uint16_t *ksh = (uint16_t *)smem;                              // [CH][KROW] bf16 ring keys
     uint16_t *vt = ksh + (bf16_ring ? a.CH * KROW : 0);            // [planes][D][CHP] V^T in bf16 terms
     int *kpos = (int *)(vt + a.vt_elems);                          // [CH] positions of the chunk's slots
-    float *xch = (float *)(kpos + a.CH);                           // [4][64][DT*4 + 2] second-half results (NHALF 2)
-    float *wsh = xch + (NHALF > 1 ? 4 * 64 * (DT * 4 + 2) : 0);     // [2][D] q_norm, k_norm
+    float4 *xch = (float4 *)(kpos + a.CH);                         // [4][DT + 1][64] second-half results (NHALF 2)
+    float *wsh = (float *)(xch + (NHALF > 1 ? 4 * (DT + 1) * 64 : 0)); // [2][D] q_norm, k_norm
     float *csh = wsh + 2 * D;                                       // [block][D + 4] rope (cos, sin) pairs
 
     const int es = bf16_ring ? 2 : 4;
@@ -808,29 +808,32 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
     if constexpr (NHALF == 1) {
         if (!active) return;
     } else {
-    constexpr int XS = DT * 4 + 2;
+    // slot c of lane l of q head hh at xch[(hh * (DT + 1) + c) * 64 + l]: the
+    // output tile dt in slot dt, (max, sum) in slot DT; each slot of a wave is
+    // one contiguous 1 KB run of 16-byte words
+    float4 *xw = xch + (size_t)hh * (DT + 1) * 64 + lane;
     if (half == 1 && active) {
-        float *xp = xch + ((size_t)hh * 64 + lane) * XS;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xp[dt * 4 + i] = ot[dt][i];
-        xp[DT * 4] = mx;
-        xp[DT * 4 + 1] = lsum;
+        for (int dt = 0; dt < DT; ++dt) xw[dt * 64] = make_float4(ot[dt][0], ot[dt][1], ot[dt][2], ot[dt][3]);
+        xw[DT * 64] = make_float4(mx, lsum, 0.0f, 0.0f);
     }
     __syncthreads();
     if (half == 1 || !active) return;
     {
-        const float *xp = xch + ((size_t)hh * 64 + lane) * XS;
-        const float m2 = xp[DT * 4], l2 = xp[DT * 4 + 1];
+        const float4 ml2 = xw[DT * 64];
+        const float m2 = ml2.x, l2 = ml2.y;
         const float mn = fmaxf(mx, m2), mns = mn == -INFINITY ? 0.0f : mn;  // exp(-inf) = 0, as above
         const float a1 = expf(mx - mns);
         const float a2 = expf(m2 - mns);
         lsum = lsum * a1 + l2 * a2;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ot[dt][i] = ot[dt][i] * a1 + xp[dt * 4 + i] * a2;
+        for (int dt = 0; dt < DT; ++dt) {
+            const float4 o2 = xw[dt * 64];
+            ot[dt][0] = ot[dt][0] * a1 + o2.x * a2;
+            ot[dt][1] = ot[dt][1] * a1 + o2.y * a2;
+            ot[dt][2] = ot[dt][2] * a1 + o2.z * a2;
+            ot[dt][3] = ot[dt][3] * a1 + o2.w * a2;
+        }
         mx = mn;
     }
     }
@@ -848,7 +851,7 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
 // LDS of the partial kernel: for a bf16 ring the chunk's keys [CH][D+8] bf16;
 // the V^T planes (one bf16 plane of CH keys for a bf16 ring, three planes for
 // f32 values, the block padded to 32 keys; every row +4 elements); the chunk's
-// slot positions; the second-half exchange [4][64][D/16*4 + 2] f32 (512
+// slot positions; the second-half exchange [4][D/16 + 1][64] float4 (512
 // threads only); the q and k norm weights [2][D] and the block rows' rope
 // pairs [block][D + 4] f32.
 int attn_vt_elems(int D, int CH, int ring_dtype) {
@@ -858,7 +861,7 @@ int attn_vt_elems(int D, int CH, int ring_dtype) {
 size_t attn_smem_bytes(int D, int CH, int ring_dtype, int block, int NT) {
     const size_t kbytes = ring_dtype == DFLASH_BF16 ? (size_t)CH * (D + 8) * 2 : 0;
     return kbytes + (size_t)attn_vt_elems(D, CH, ring_dtype) * 2 + (size_t)CH * 4 +
-           (NT > 256 ? (size_t)4 * 64 * (D / 16 * 4 + 2) * 4 : 0) + (size_t)(2 * D + block * (D + 4)) * 4;
+           (NT > 256 ? (size_t)4 * (D / 16 + 1) * 64 * 16 : 0) + (size_t)(2 * D + block * (D + 4)) * 4;
 }
 
 template <int D, int KT, int NT>

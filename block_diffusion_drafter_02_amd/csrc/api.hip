@@ -467,6 +467,7 @@ int prepare_chain(dflash_ctx &x, hipStream_t s) {
     a.qkv_out = x.qkv_out;
     a.rope_cs = x.rope_cs;
     a.ss_stride = x.Mmax;
+    a.ss_gs = 2 * x.G_E;
     const int slot_shape[CS_N][2] = {{x.nqkv, x.E}, {x.E, x.qdim}, {2 * x.F, x.E}, {x.E, x.F}, {x.V, x.E}};
     float *pp = x.cpartial;
     int *sync = x.csync;
@@ -511,6 +512,7 @@ EpiArgs epi_base(const dflash_ctx &x, int kind, int M) {
     e.kind = kind;
     e.M = M;
     e.ss_stride = x.Mmax;
+    e.ss_gs = 2 * x.G_E;  // half-group launches write two sums per 64 columns
     e.inv_E = 1.0f / (float)x.E;
     e.eps = x.cfg.rms_eps;
     e.block = x.cfg.block;

@@ -191,10 +191,11 @@ struct EpiArgs {
     int kind;
     int M;                // live rows (16 * B)
     const float *wscale;  // fp8 per-column scales in tiled column order, or null
-    // row normalisation folded into the consumer: rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps)
-    const float *ss;      // [ss_groups][Mstride] partial sums of squares, or null
+    // row normalisation folded into the consumer: rs[m] = 1/sqrt(sum_g ss[m][g] / E + eps)
+    const float *ss;      // [rows][ss_gs] partial sums of squares, a row's groups contiguous, or null
     int ss_groups;
-    int ss_stride;        // Mstride of ss
+    int ss_gs;            // row stride of ss and ss_out (groups)
+    int ss_stride;        // row stride of the per-group argmax keys (am_key: [G][ss_stride])
     float inv_E, eps;
     // EPI_SCALED / EPI_LOGITS output [M][ld_out]
     float *out;
@@ -209,7 +210,7 @@ struct EpiArgs {
     int act_fmt;
     int act_rows;         // row stride of act_out (Mmax)
     int act_K;
-    float *ss_out;        // [G][ss_stride] sums of squares of the updated x
+    float *ss_out;        // [rows][ss_gs] sums of squares of the updated x, one per group
     int block;  // rows per sequence
     int gamma;  // block width in use: drafts and acceptance cover rows 1..gamma-1
     // EPI_LOGITS: argmax across groups
@@ -422,7 +423,7 @@ struct ChainArgs {
     float *x, *x2;
     void *act_a, *act_f, *act_d, *act_o;
     float *ss_a, *ss_f, *qkv_out, *rope_cs;
-    int ss_stride;
+    int ss_stride, ss_gs;
     int S[CS_N];              // k-splits per phase slot
     float *partial[CS_N];     // [S][G][16*64] per phase slot
     int *counters[CS_N];      // [G] split-K arrival counters per phase slot (zero between uses)

@@ -431,7 +431,7 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs &e, int g, EpiPre &p)
 #pragma unroll
         for (int j = 0; j < EpiPre::SSN; ++j) {
             const int gg = sub + 16 * j;
-            p.ss[j] = (e.ss != nullptr && m < M && gg < e.ss_groups) ? e.ss[(size_t)gg * e.ss_stride + m] : 0.0f;
+            p.ss[j] = (e.ss != nullptr && m < M && gg < e.ss_groups) ? e.ss[(size_t)m * e.ss_gs + gg] : 0.0f;
         }
     }
     if constexpr (EPI == EPI_SWIGLU) {
@@ -459,7 +459,7 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs &e, int g, EpiPre &p)
 // does not depend on which split came first), re-arms the slot and writes the
 // output element. One device round trip instead of the counter hand-off's
 // store, wait, counter and load.
-// rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps) of one 16-row tile into LDS (256 threads, as in gemv_epilogue)
+// rs[m] = 1/sqrt(sum_g ss[m][g] / E + eps) of one 16-row tile into LDS (256 threads, as in gemv_epilogue)
 template <bool PF>
 __device__ __forceinline__ void tile_row_scales(const EpiArgs &e, float *rs_s, const EpiPre &pre) {
     const int tid = threadIdx.x;
@@ -469,7 +469,7 @@ __device__ __forceinline__ void tile_row_scales(const EpiArgs &e, float *rs_s, c
 #pragma unroll
         for (int j = 0; j < EpiPre::SSN; ++j) part += pre.ss[j];
     } else if (e.ss != nullptr && m < e.M) {
-        for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
+        for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)m * e.ss_gs + gg];
     }
     for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
     if (sub == 0) rs_s[m] = (e.ss != nullptr && m < e.M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
@@ -639,7 +639,7 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
     constexpr int GN = CW * WN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int M = e.M;
-    // rs[m] = 1/sqrt(sum_g ss[g][m] / E + eps): 16 threads per row, each summing
+    // rs[m] = 1/sqrt(sum_g ss[m][g] / E + eps): 16 threads per row, each summing
     // groups sub, sub + 16, ... in order, then a fixed-order tree
     if (EPI != EPI_RESID || !PF) {
         for (int m0 = 0; m0 < MP; m0 += 16) {
@@ -649,7 +649,7 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
 #pragma unroll
                 for (int j = 0; j < EpiPre::SSN; ++j) part += pre.ss[j];
             } else if (e.ss != nullptr && m < M) {
-                for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)gg * e.ss_stride + m];
+                for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)m * e.ss_gs + gg];
             }
             for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
             if (sub == 0) rs_s[m] = (e.ss != nullptr && m < M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
@@ -716,7 +716,7 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                     }
                 }
                 const float sq = wave_sum(xn * xn);
-                if (lane == 0) st_f32(e.ss_out + (size_t)g * e.ss_stride + m, sq);
+                if (lane == 0) st_f32(e.ss_out + (size_t)m * e.ss_gs + g, sq);
             }
         }
         if (staged) {

@@ -160,6 +160,7 @@ __device__ __forceinline__ EpiArgs epi_base(const ChainArgs &a, const ChainIO &i
     e.kind = kind;
     e.M = 16;
     e.ss_stride = a.ss_stride;
+    e.ss_gs = a.ss_gs;
     e.inv_E = a.inv_E;
     e.eps = a.eps;
     e.block = a.block;
@@ -201,7 +202,7 @@ __device__ __forceinline__ void embed_group(const ChainArgs &a, const ChainIO &i
         st_f32(a.x + (size_t)i * a.E + n, v);
         write_act(a.act_a, a.act_fmt, a.act_rows, a.E, i, n, v * a.attn_norm[n]);
         const float sq = wave_sum(v * v);
-        if (lane == 0) st_f32(a.ss_a + (size_t)g * a.ss_stride + i, sq);
+        if (lane == 0) st_f32(a.ss_a + (size_t)i * a.ss_gs + g, sq);
     }
 }
 

@@ -270,7 +270,7 @@ hipError_t launch_inject(const dflash_ctx *c, void *ring, void *const *rings, co
 // Usage), first layer's norm input, and the block's rope table.
 // ---------------------------------------------------------------------------
 // Grid (E/64, B), 256 threads. Writes x [M][E], act_a = x * attn_norm_0 in the
-// activation format, ss_a[g][m] = sum of x^2 over the group's 64 columns.
+// activation format, ss_a[m][g] = sum of x^2 over the group's 64 columns.
 // The workgroups of sequence b also write rope_cs[b][i][f] = (cos, sin)((n_past
 // + i) * inv_freq[f]), computed in fp64, one entry per thread.
 struct EmbedArgs {
@@ -282,7 +282,7 @@ struct EmbedArgs {
     int act_fmt, act_rows;
     const float *attn_norm0;
     float *ss_a;
-    int ss_stride;
+    int ss_gs;  // row stride of ss_a (groups)
     float *rope_cs;
     const double *inv_freq;
 };
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
             a.x[(size_t)m * a.E + n] = v[r];
             write_act(a.act_a, a.act_fmt, a.act_rows, a.E, m, n, v[r] * wn);
             const float sq = wave_sum(v[r] * v[r]);
-            if (lane == 0) a.ss_a[(size_t)g * a.ss_stride + m] = sq;
+            if (lane == 0) a.ss_a[(size_t)m * a.ss_gs + g] = sq;
         }
     }
     {  // the rope table's block * D/2 entries, spread over the sequence's workgroups
@@ -355,7 +355,7 @@ hipError_t launch_embed(const dflash_ctx *c, const int32_t *id_last, const int32
     a.act_rows = c->Mmax;
     a.attn_norm0 = c->attn_norm;
     a.ss_a = c->ss_a;
-    a.ss_stride = c->Mmax;
+    a.ss_gs = 2 * c->G_E;
     a.rope_cs = c->rope_cs;
     a.inv_freq = c->inv_freq;
     hipLaunchKernelGGL(embed_kernel, dim3(c->G_E, B), dim3(256), 0, s, a);

@@ -566,11 +566,11 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
     }
     if (row0 > 0) {
         const size_t es = e.act_fmt == ACT_F32 ? 4 : 2;
-        if (el.ss) el.ss += row0;
+        if (el.ss) el.ss += (size_t)row0 * e.ss_gs;
         if (el.out) el.out += (size_t)row0 * e.ld_out;
         if (el.x) el.x += (size_t)row0 * e.ld_x;
         if (el.x_out) el.x_out += (size_t)row0 * e.ld_x;
-        if (el.ss_out) el.ss_out += row0;
+        if (el.ss_out) el.ss_out += (size_t)row0 * e.ss_gs;
         if (el.act_out) el.act_out = (char *)el.act_out + (size_t)row0 * e.act_K * es;
     }
     EpiPre pre;

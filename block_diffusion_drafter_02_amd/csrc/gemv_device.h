@@ -84,37 +84,6 @@ struct AFTraits<ACT_BF16> {
     static constexpr int NW = 2;
 };
 
-// Row-major activation planes (the large-M GEMM reads caller inputs and its
-// own row-major staging).
-template <int AF>
-__device__ __forceinline__ void load_act(const void *act, int act_rows, int K, int row, int M, int kb, int lane,
-                                         u32x4 (&a)[AFTraits<AF>::NW]) {
-    constexpr int NW = AFTraits<AF>::NW;
-    if (row >= M) {
-#pragma unroll
-        for (int i = 0; i < NW; ++i) a[i] = u32x4{0, 0, 0, 0};
-        return;
-    }
-    const int col = kb * KBLK + LANE_ELEMS * (lane >> 4);
-    if constexpr (AF == ACT_SPLIT3) {
-        const uint16_t *base = (const uint16_t *)act;
-#pragma unroll
-        for (int t = 0; t < 3; ++t) {
-            const u32x4 *p = (const u32x4 *)(base + ((size_t)t * act_rows + row) * K + col);
-            a[2 * t] = p[0];
-            a[2 * t + 1] = p[1];
-        }
-    } else if constexpr (AF == ACT_F32) {
-        const u32x4 *p = (const u32x4 *)((const float *)act + (size_t)row * K + col);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = p[i];
-    } else {
-        const u32x4 *p = (const u32x4 *)((const uint16_t *)act + (size_t)row * K + col);
-        a[0] = p[0];
-        a[1] = p[1];
-    }
-}
-
 // Lane-ordered activation planes (act_offset): one k-block of one 16-row tile
 // is 1 KB per plane word, read by one contiguous wavefront load.
 template <int AF>

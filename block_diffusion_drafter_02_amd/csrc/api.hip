@@ -286,6 +286,7 @@ size_t carve(dflash_ctx &x, char *base) {
     }
     // split partials of the batched projections (16*B rows, B > 1)
     x.bpartial = nullptr;
+    x.brs = nullptr;
     if (c.max_batch > 1) {
         size_t bmax = 0;
         for (auto &sh : shapes) {
@@ -294,6 +295,7 @@ size_t carve(dflash_ctx &x, char *base) {
             bmax = std::max(bmax, (size_t)S * Mmax * sh[0]);
         }
         x.bpartial = cv.take<float>(4 * bmax);
+        x.brs = cv.take<float>(4ull * Mmax);
     }
     return cv.off;
 }
@@ -553,8 +555,21 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
         g.act_rows = x.Mmax;
         g.out = x.bpartial;
         batch_split(N, K, g.S, g.kbps);
+        EpiArgs e = epi;
+        if (epi.ss != nullptr && epi.kind != EPI_RESID && epi.M <= 128 && epi.ss_groups <= 256 &&
+            gemm_workgroups(g) % x.cus != 0) {
+            // the row scales once per launch, by an extra GEMM workgroup on a compute unit the GEMM's last
+            // round leaves free, instead of in every epilogue workgroup
+            g.rs_ss = epi.ss;
+            g.rs_groups = epi.ss_groups;
+            g.rs_gs = epi.ss_gs;
+            g.rs_inv_E = epi.inv_E;
+            g.rs_eps = epi.eps;
+            g.rs_out = x.brs;
+            e.rs = x.brs;
+        }
         HIP_TRY(launch_gemm(x.cfg.weight_dtype, x.blk_fmt, g, s, true), "batched projection launch");
-        HIP_TRY(launch_batch_epi(x.bpartial, g.S, g.M, N, epi, s), "batched epilogue launch");
+        HIP_TRY(launch_batch_epi(x.bpartial, g.S, g.M, N, e, s), "batched epilogue launch");
         return DFLASH_OK;
     }
     GemvArgs a = {};

@@ -195,6 +195,7 @@ struct EpiArgs {
     const float *ss;      // [rows][ss_gs] partial sums of squares, a row's groups contiguous, or null
     int ss_groups;
     int ss_gs;            // row stride of ss and ss_out (groups)
+    const float *rs;      // the row scales already computed from ss (one per row), or null
     int ss_stride;        // row stride of the per-group argmax keys (am_key: [G][ss_stride])
     float inv_E, eps;
     // EPI_SCALED / EPI_LOGITS output [M][ld_out]
@@ -288,6 +289,12 @@ struct GemmArgs {
     int act_rows;   // row stride between terms (for ACT_SPLIT3)
     float *out;     // [S][M][N] f32: split s sums k-blocks [s * kbps, (s + 1) * kbps)
     int S, kbps;
+    // rs_out set: one extra workgroup writes the row scales of the epilogue that
+    // follows, rs_out[m] = 1/sqrt(sum_g rs_ss[m][g] * rs_inv_E + rs_eps), m < M
+    const float *rs_ss;
+    int rs_groups, rs_gs;
+    float rs_inv_E, rs_eps;
+    float *rs_out;
 };
 
 // ---------------------------------------------------------------------------
@@ -378,6 +385,7 @@ struct dflash_ctx {
     int chain_wg;       // workgroups per chain launch (0: chain unavailable)
     int chain_S[5];     // k-splits of the chain's q/k/v, Wo, gate/up, down and lm_head phases
     float *bpartial;    // split partials of the batched projections (null when max_batch == 1)
+    float *brs;         // [Mmax] row scales of a batched epilogue (null when max_batch == 1)
     int path;           // DFLASH_PATH_*
     void *static_scratch;  // this device's address of the allocation-free encode's static scratch
 };
@@ -473,6 +481,7 @@ hipError_t launch_tile_scales(const float *src, int src_rows, float *dst, int ro
 hipError_t launch_vec_to_f32(const void *src, int dtype, int n, float *dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t *p, int32_t v, size_t n, hipStream_t s);
 hipError_t launch_quantize_fp8(const float *w, int rows, int cols, uint8_t *codes, float *scales, hipStream_t s);
+int gemm_workgroups(const GemmArgs &a);  // main workgroups of a launch_gemm grid
 hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, int CW, dim3 grid, const GemvArgs &a,
                        hipStream_t s);
 hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s, bool lanes = false);

@@ -340,6 +340,35 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (a.rs_out != nullptr && blockIdx.x == 0) {
+        // the first workgroup: row scales for the epilogue that follows (16
+        // threads per row, groups summed in the order the epilogue would), the
+        // loads of up to 128 rows (four rows per thread) issued together
+        constexpr int RPT = 4, GPT = 16;  // rows per thread, groups per thread and row (rs_groups <= 256)
+        const int sub = tid & 15;
+        float v[RPT][GPT];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int m = r * (GEMM_THREADS / 16) + (tid >> 4);
+#pragma unroll
+            for (int j = 0; j < GPT; ++j) {
+                const int gg = sub + 16 * j;
+                v[r][j] = (m < a.M && gg < a.rs_groups) ? a.rs_ss[(size_t)m * a.rs_gs + gg] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int m = r * (GEMM_THREADS / 16) + (tid >> 4);
+            float part = 0.0f;
+#pragma unroll
+            for (int j = 0; j < GPT; ++j)
+                if (sub + 16 * j < a.rs_groups) part += v[r][j];
+            for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+            if (sub == 0 && m < a.M) a.rs_out[m] = 1.0f / sqrtf(part * a.rs_inv_E + a.rs_eps);
+        }
+        return;
+    }
+    const int bid = blockIdx.x - (a.rs_out != nullptr);  // the main workgroups' index
     const int wr = wave >> 2, wc = wave & 3;  // rows 64wr.., column group g0 + wc
     const int G = a.N / GROUP_N;
     // One-dimensional grid in an L2-friendly order: the row tiles that share a (column tile, k-split) are
@@ -347,7 +376,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
     // on the eight XCDs puts them on one XCD at about the same time, and its L2 serves their common weight
     // tiles once: L = (q * Y + y) * 8 + c with column-tile-and-split index xz = 8 q + c.
     const int X = (G + GEMM_GROUPS - 1) / GEMM_GROUPS, Y = (a.M + BM - 1) / BM;
-    const int Lc = blockIdx.x % 8, Lr = blockIdx.x / 8;
+    const int Lc = bid % 8, Lr = bid / 8;
     const int xz = (Lr / Y) * 8 + Lc;
     if (xz >= X * a.S) return;
     const int g0 = (xz % X) * GEMM_GROUPS, r0 = (Lr % Y) * BM, sp = xz / X;
@@ -497,11 +526,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_kernel(GemmArgs a) {
             }
 }
 
+int gemm_workgroups(const GemmArgs &a) {
+    const int X = (a.N / GROUP_N + GEMM_GROUPS - 1) / GEMM_GROUPS, Y = (a.M + GEMM_BM - 1) / GEMM_BM;
+    return (X * a.S + 7) / 8 * 8 * Y;  // see the kernel's decoding of blockIdx.x
+}
+
 template <int WT, int AF, bool ALANES>
 static hipError_t gemm_go(const GemmArgs &a, hipStream_t s) {
     using Sh = GemmShape<WT, AF, ALANES>;
-    const int X = (a.N / GROUP_N + GEMM_GROUPS - 1) / GEMM_GROUPS, Y = (a.M + GEMM_BM - 1) / GEMM_BM;
-    const int n = (X * a.S + 7) / 8 * 8 * Y;  // see the kernel's decoding of blockIdx.x
+    if (a.rs_out != nullptr && (a.M > 128 || a.rs_groups > 256)) return hipErrorInvalidValue;
+    const int n = gemm_workgroups(a) + (a.rs_out != nullptr);
     hipLaunchKernelGGL((gemm_kernel<WT, AF, ALANES>), dim3(n), dim3(GEMM_THREADS), Sh::LDS, s, a);
     return hipGetLastError();
 }
@@ -567,6 +601,7 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
     if (row0 > 0) {
         const size_t es = e.act_fmt == ACT_F32 ? 4 : 2;
         if (el.ss) el.ss += (size_t)row0 * e.ss_gs;
+        if (el.rs) el.rs += row0;
         if (el.out) el.out += (size_t)row0 * e.ld_out;
         if (el.x) el.x += (size_t)row0 * e.ld_x;
         if (el.x_out) el.x_out += (size_t)row0 * e.ld_x;
@@ -599,7 +634,8 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
 #pragma unroll
     for (int j = 0; j < PT; ++j) *(f32x4 *)(tile + 4 * (tid + 256 * j)) = acc[j];
     __syncthreads();
-    gemv_epilogue<EPI, MT, 1, MT == 1>(el, g, G, tile, rs_s, &flag_s, best_s, pre);
+    // the logits' last stage covers every row of the step (up to 128): four 16-row chunks per load round
+    gemv_epilogue<EPI, MT, 1, MT == 1, GROUP_N, EPI == EPI_LOGITS ? 4 : 1>(el, g, G, tile, rs_s, &flag_s, best_s, pre);
 }
 
 hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, hipStream_t s) {

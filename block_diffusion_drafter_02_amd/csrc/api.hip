@@ -555,8 +555,8 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
         g.act_rows = x.Mmax;
         g.out = x.bpartial;
         batch_split(N, K, g.S, g.kbps);
-        EpiArgs e = epi;
-        if (epi.ss != nullptr && epi.kind != EPI_RESID && epi.M <= 128 && epi.ss_groups <= 256 &&
+        const float *rs = nullptr;
+        if (epi.ss != nullptr && (epi.kind == EPI_SCALED || epi.kind == EPI_SWIGLU) && epi.M <= 128 && epi.ss_groups <= 256 &&
             gemm_workgroups(g) % x.cus != 0) {
             // the row scales once per launch, by an extra GEMM workgroup on a compute unit the GEMM's last
             // round leaves free, instead of in every epilogue workgroup
@@ -566,10 +566,10 @@ int gemv(const dflash_ctx &x, const void *W, int N, int K, const void *act, cons
             g.rs_inv_E = epi.inv_E;
             g.rs_eps = epi.eps;
             g.rs_out = x.brs;
-            e.rs = x.brs;
+            rs = x.brs;
         }
         HIP_TRY(launch_gemm(x.cfg.weight_dtype, x.blk_fmt, g, s, true), "batched projection launch");
-        HIP_TRY(launch_batch_epi(x.bpartial, g.S, g.M, N, e, s), "batched epilogue launch");
+        HIP_TRY(launch_batch_epi(x.bpartial, g.S, g.M, N, epi, rs, s), "batched epilogue launch");
         return DFLASH_OK;
     }
     GemvArgs a = {};

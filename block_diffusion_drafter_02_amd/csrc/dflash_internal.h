@@ -195,7 +195,6 @@ struct EpiArgs {
     const float *ss;      // [rows][ss_gs] partial sums of squares, a row's groups contiguous, or null
     int ss_groups;
     int ss_gs;            // row stride of ss and ss_out (groups)
-    const float *rs;      // the row scales already computed from ss (one per row), or null
     int ss_stride;        // row stride of the per-group argmax keys (am_key: [G][ss_stride])
     float inv_E, eps;
     // EPI_SCALED / EPI_LOGITS output [M][ld_out]
@@ -485,7 +484,8 @@ int gemm_workgroups(const GemmArgs &a);  // main workgroups of a launch_gemm gri
 hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, int CW, dim3 grid, const GemvArgs &a,
                        hipStream_t s);
 hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s, bool lanes = false);
-hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, hipStream_t s);
+// rs: the row scales already computed from e.ss (one per row, rows 0..M-1; scaled and SwiGLU epilogues), or null
+hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, const float *rs, hipStream_t s);
 hipError_t gemm_set_smem_limit();
 hipError_t launch_split(const float *src, int rows, int K, int ld_src, void *dst, int act_fmt, int act_rows,
                         hipStream_t s);

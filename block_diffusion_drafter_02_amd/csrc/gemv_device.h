@@ -396,11 +396,11 @@ __device__ __forceinline__ void epi_prefetch(const EpiArgs &e, int g, EpiPre &p)
     const int M = e.M;
     if constexpr (EPI != EPI_RESID) {
         const int m = tid >> 4, sub = tid & 15;
-        p.ss_ok = e.rs == nullptr && e.ss_groups <= 16 * EpiPre::SSN;
+        p.ss_ok = e.ss_groups <= 16 * EpiPre::SSN;
 #pragma unroll
         for (int j = 0; j < EpiPre::SSN; ++j) {
             const int gg = sub + 16 * j;
-            p.ss[j] = (p.ss_ok && e.ss != nullptr && m < M && gg < e.ss_groups) ? e.ss[(size_t)m * e.ss_gs + gg] : 0.0f;
+            p.ss[j] = (e.ss != nullptr && m < M && gg < e.ss_groups) ? e.ss[(size_t)m * e.ss_gs + gg] : 0.0f;
         }
     }
     if constexpr (EPI == EPI_SWIGLU) {
@@ -503,9 +503,6 @@ __device__ __forceinline__ int argmax_key_index(unsigned long long k) { return (
 // (am_key[slot][row]), it counts itself in; the last of the arrivals (NK unless e.arrivals is set) takes
 // the largest key of every row of the step (e.rows_all, else M), writes the drafts, runs the acceptance
 // scan and re-arms the counter. best_s holds one int per row of the step.
-// MU 16-row chunks of rows have their key loads in flight together (the batched
-// path's 128 rows: 8 chunks).
-template <int MU = 1>
 __device__ __forceinline__ void argmax_finish(const EpiArgs &e, int NK, int *flag_s, int *best_s) {
     const int tid = threadIdx.x;
     const int M = e.rows_all ? e.rows_all : e.M;
@@ -522,42 +519,29 @@ __device__ __forceinline__ void argmax_finish(const EpiArgs &e, int NK, int *fla
     // groups sub, sub + 16, ... with the loads of a batch issued together,
     // then a 16-lane reduction (the order does not change a maximum)
     constexpr int KU = 8;
-    for (int m0 = 0; m0 < M; m0 += 16 * MU) {
-        const int sub = tid & 15;
-        unsigned long long best[MU];
-#pragma unroll
-        for (int mu = 0; mu < MU; ++mu) best[mu] = 0ull;
-        for (int g0 = sub; g0 < NK; g0 += 16 * KU) {
-            unsigned long long k[MU][KU];
-#pragma unroll
-            for (int mu = 0; mu < MU; ++mu) {
-                const int m = m0 + 16 * mu + (tid >> 4);
+    for (int m0 = 0; m0 < M; m0 += 16) {
+        const int m = m0 + (tid >> 4), sub = tid & 15;
+        unsigned long long best = 0ull;
+        if (m < M)
+            for (int g0 = sub; g0 < NK; g0 += 16 * KU) {
+                unsigned long long k[KU];
 #pragma unroll
                 for (int u = 0; u < KU; ++u)
-                    k[mu][u] = (m < M && g0 + 16 * u < NK)
-                                   ? __hip_atomic_load(e.am_key + (size_t)(g0 + 16 * u) * e.ss_stride + m,
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                   : 0ull;
+                    k[u] = g0 + 16 * u < NK ? __hip_atomic_load(e.am_key + (size_t)(g0 + 16 * u) * e.ss_stride + m,
+                                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                           : 0ull;
+#pragma unroll
+                for (int u = 0; u < KU; ++u) best = k[u] > best ? k[u] : best;
             }
-#pragma unroll
-            for (int mu = 0; mu < MU; ++mu)
-#pragma unroll
-                for (int u = 0; u < KU; ++u) best[mu] = k[mu][u] > best[mu] ? k[mu][u] : best[mu];
+        for (int o = 8; o > 0; o >>= 1) {
+            const unsigned long long ok = __shfl_xor(best, o, 64);
+            best = ok > best ? ok : best;
         }
-#pragma unroll
-        for (int mu = 0; mu < MU; ++mu) {
-            const int m = m0 + 16 * mu + (tid >> 4);
-            unsigned long long bv = best[mu];
-            for (int o = 8; o > 0; o >>= 1) {
-                const unsigned long long ok = __shfl_xor(bv, o, 64);
-                bv = ok > bv ? ok : bv;
-            }
-            if (sub == 0 && m < M) {
-                const int bi = argmax_key_index(bv);
-                best_s[m] = bi;
-                const int b = m / e.block, i = m % e.block;
-                if (i > 0 && i < e.gamma) st_i32(e.drafts + (size_t)b * (e.gamma - 1) + i - 1, bi);
-            }
+        if (sub == 0 && m < M) {
+            const int bi = argmax_key_index(best);
+            best_s[m] = bi;
+            const int b = m / e.block, i = m % e.block;
+            if (i > 0 && i < e.gamma) st_i32(e.drafts + (size_t)b * (e.gamma - 1) + i - 1, bi);
         }
     }
     __syncthreads();
@@ -614,8 +598,8 @@ __device__ __forceinline__ void logits_exchange(const EpiArgs &e, int g, int G, 
 
 // CW: columns of group g (64, or 32 for half groups; lanes >= CW idle). The
 // G groups of one launch write ss_out rows 0..G-1.
-// AMU: row chunks of the argmax's last stage loaded together (argmax_finish).
-template <int EPI, int MT, int WN, bool PF = false, int CW = GROUP_N, int AMU = 1>  // PF: operands from epi_prefetch (MT = 1)
+// RSR: rs_s already holds the row scales (the batched epilogue's precomputed ones).
+template <int EPI, int MT, int WN, bool PF = false, int CW = GROUP_N, bool RSR = false>  // PF: operands from epi_prefetch (MT = 1)
 __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, float *tile, float *rs_s, int *flag_s,
                                               int *best_s, const EpiPre &pre = EpiPre{}) {
     static_assert(!PF || MT == 1, "prefetched epilogue operands cover one row tile");
@@ -627,22 +611,18 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
     const int M = e.M;
     // rs[m] = 1/sqrt(sum_g ss[m][g] / E + eps): 16 threads per row, each summing
     // groups sub, sub + 16, ... in order, then a fixed-order tree
-    if (EPI != EPI_RESID || !PF) {
+    if ((EPI != EPI_RESID || !PF) && !RSR) {
         for (int m0 = 0; m0 < MP; m0 += 16) {
             const int m = m0 + (tid >> 4), sub = tid & 15;
             float part = 0.0f;
-            if (e.rs != nullptr) {
-                // computed once for the launch
-            } else if (PF && pre.ss_ok) {
+            if (PF && pre.ss_ok) {
 #pragma unroll
                 for (int j = 0; j < EpiPre::SSN; ++j) part += pre.ss[j];
             } else if (e.ss != nullptr && m < M) {
                 for (int gg = sub; gg < e.ss_groups; gg += 16) part += e.ss[(size_t)m * e.ss_gs + gg];
             }
             for (int o = 8; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-            if (sub == 0)
-                rs_s[m] = (e.ss != nullptr && m < M) ? (e.rs != nullptr ? e.rs[m] : 1.0f / sqrtf(part * e.inv_E + e.eps))
-                                                     : 1.0f;
+            if (sub == 0) rs_s[m] = (e.ss != nullptr && m < M) ? 1.0f / sqrtf(part * e.inv_E + e.eps) : 1.0f;
         }
         __syncthreads();
     }
@@ -815,6 +795,6 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                 __hip_atomic_store(e.am_key + (size_t)g * e.ss_stride + mg, argmax_key(bv, bi), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
-        argmax_finish<AMU>(e, G, flag_s, best_s);
+        argmax_finish(e, G, flag_s, best_s);
     }
 }

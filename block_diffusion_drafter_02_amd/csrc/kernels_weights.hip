@@ -582,7 +582,8 @@ hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s
 // rows measured 62 us per step at batch 8.
 // ---------------------------------------------------------------------------
 template <int EPI, int MT>
-__global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S, int M, int N, EpiArgs e) {
+__global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S, int M, int N, EpiArgs e,
+                                                        const float *rs) {
     constexpr int MP = 16 * MT, PT = MP * GROUP_N / 4 / 256;  // float4 per thread per split
     constexpr int UNR = MT >= 8 ? 2 : 8;                               // splits in flight
     __shared__ __attribute__((aligned(16))) float tile[MP * GROUP_N];
@@ -601,15 +602,25 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
     if (row0 > 0) {
         const size_t es = e.act_fmt == ACT_F32 ? 4 : 2;
         if (el.ss) el.ss += (size_t)row0 * e.ss_gs;
-        if (el.rs) el.rs += row0;
         if (el.out) el.out += (size_t)row0 * e.ld_out;
         if (el.x) el.x += (size_t)row0 * e.ld_x;
         if (el.x_out) el.x_out += (size_t)row0 * e.ld_x;
         if (el.ss_out) el.ss_out += (size_t)row0 * e.ss_gs;
         if (el.act_out) el.act_out = (char *)el.act_out + (size_t)row0 * e.act_K * es;
     }
+    // row scales computed once for the launch (by the GEMM before it; scaled and
+    // SwiGLU epilogues): no sums of squares to load
+    constexpr bool RS_KIND = EPI == EPI_SCALED || EPI == EPI_SWIGLU;
+    const bool rs_given = RS_KIND && rs != nullptr;
     EpiPre pre;
-    epi_prefetch<EPI, MT>(el, g, pre);
+    if (rs_given) {
+        EpiArgs ep = el;
+        ep.ss = nullptr;
+        epi_prefetch<EPI, MT>(ep, g, pre);
+        if (tid < MP) rs_s[tid] = tid < rows ? rs[row0 + tid] : 1.0f;
+    } else {
+        epi_prefetch<EPI, MT>(el, g, pre);
+    }
     f32x4 acc[PT];
 #pragma unroll
     for (int j = 0; j < PT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -634,26 +645,31 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
 #pragma unroll
     for (int j = 0; j < PT; ++j) *(f32x4 *)(tile + 4 * (tid + 256 * j)) = acc[j];
     __syncthreads();
-    // the logits' last stage covers every row of the step (up to 128): four 16-row chunks per load round
-    gemv_epilogue<EPI, MT, 1, MT == 1, GROUP_N, EPI == EPI_LOGITS ? 4 : 1>(el, g, G, tile, rs_s, &flag_s, best_s, pre);
+    if constexpr (RS_KIND) {
+        if (rs_given) {  // rs_s was filled before the barrier above
+            gemv_epilogue<EPI, MT, 1, MT == 1, GROUP_N, true>(el, g, G, tile, rs_s, &flag_s, best_s, pre);
+            return;
+        }
+    }
+    gemv_epilogue<EPI, MT, 1, MT == 1>(el, g, G, tile, rs_s, &flag_s, best_s, pre);
 }
 
-hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, hipStream_t s) {
+hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, const float *rs, hipStream_t s) {
     if (M < 1 || M % 16 != 0 || S < 1) return hipErrorInvalidValue;
     const dim3 rows_grid(N / GROUP_N, M / 16);
     switch (e.kind) {
         case EPI_SCALED:
-            hipLaunchKernelGGL((batch_epi_kernel<EPI_SCALED, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e);
+            hipLaunchKernelGGL((batch_epi_kernel<EPI_SCALED, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e, rs);
             break;
         case EPI_RESID:
-            hipLaunchKernelGGL((batch_epi_kernel<EPI_RESID, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e);
+            hipLaunchKernelGGL((batch_epi_kernel<EPI_RESID, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e, rs);
             break;
         case EPI_SWIGLU:
-            hipLaunchKernelGGL((batch_epi_kernel<EPI_SWIGLU, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e);
+            hipLaunchKernelGGL((batch_epi_kernel<EPI_SWIGLU, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e, rs);
             break;
         case EPI_LOGITS:  // one 16-row tile per workgroup; the argmax's last stage covers all M <= 128 rows
             if (M > 128) return hipErrorInvalidValue;
-            hipLaunchKernelGGL((batch_epi_kernel<EPI_LOGITS, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e);
+            hipLaunchKernelGGL((batch_epi_kernel<EPI_LOGITS, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e, rs);
             break;
         default: return hipErrorInvalidValue;
     }

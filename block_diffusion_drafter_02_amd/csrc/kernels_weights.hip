@@ -275,18 +275,22 @@ hipError_t launch_gemv(int wdtype, int act_fmt, int MT, int WN, int NWV, int CW,
 }
 
 // ---------------------------------------------------------------------------
-// Large-M GEMM (encode's fc, inject's fused K/V projection): out[M][N] =
-// act[M][K] . W[N][K]^T (* per-column scale), f32 out, row-major activations
-// (one bf16 plane, three bf16 planes of an exact split, or f32).
+// Large-M GEMM (encode's fc, inject's fused K/V projection, the batched block
+// rows): out[M][N] = act[M][K] . W[N][K]^T (* per-column scale), f32 out,
+// activations row-major or in the block rows' lane order (one bf16 plane,
+// three bf16 planes of an exact split, or f32).
 // ---------------------------------------------------------------------------
-// Workgroup tile 128 rows x 256 columns (four column groups) x one k-split
-// (grid z), 8 wavefronts of 64 rows x 64 columns each; split s writes its
-// partial product to out + s*M*N and the consumer sums the splits in order.
-// Per k-block the workgroup stages the activation rows and the four groups'
+// Workgroup tile 128 rows x 256 columns (four column groups) x one k-split,
+// 8 wavefronts of 64 rows x 64 columns each; split s writes its partial
+// product to out + s*M*N and the consumer sums the splits in order. Per
+// k-block the workgroup stages the activation rows and the four groups'
 // weight tiles in LDS once (activation rows padded against bank conflicts;
 // weight tiles copied in their lane order) and every wave reads its operands
-// from there; the next k-block is loaded into registers while the current one
-// is multiplied. Column groups past N are masked.
+// from there. Where two stages fit the 160 KB of LDS, k-block kb + 1 moves
+// from registers to the free stage and the loads of kb + 2 are issued while kb
+// is multiplied (one barrier per k-block); otherwise the next k-block waits in
+// registers. Column groups past N are masked. With rs_out set, one extra
+// workgroup (the first) computes the row scales of the epilogue that follows.
 template <int AF>
 struct GemmA;
 template <>

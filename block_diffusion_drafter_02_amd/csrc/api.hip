@@ -443,7 +443,7 @@ int prepare_chain(dflash_ctx &x, hipStream_t s) {
     a.block = x.cfg.block;
     a.mask_id = x.cfg.mask_id;
     a.aux_dtype = x.cfg.aux_dtype;
-    a.act_fmt = x.act_fmt;
+    a.act_fmt = ACT_F32;  // one sequence: f32 lane words, split into the bf16 terms at load for bf16 / fp8 weights
     a.act_rows = x.Mmax;
     a.eps = x.cfg.rms_eps;
     a.inv_E = 1.0f / (float)x.E;
@@ -683,7 +683,7 @@ int run_step(dflash_ctx &x, void *const *rings, const int32_t *id_last, const in
              hipStream_t s) {
     // one sequence on the per-launch kernels: f32 activations split at load (4 bytes per value written and
     // read instead of 6); the batched projections and the chain read three bf16 planes
-    x.blk_fmt = (B == 1 && !use_chain(x, B)) ? ACT_F32 : x.act_fmt;
+    x.blk_fmt = B == 1 ? ACT_F32 : x.act_fmt;
     if (use_chain(x, B)) {
         // dataflow chain: head (embed + q/k/v of layer 0); per layer attention, then Wo .. q/k/v(l+1) or lm_head
         ChainIO io{id_last, block_ids, n_past, logits, drafts, target, n_ok, x.gamma, x.temp, (uint32_t)x.seed,

@@ -105,7 +105,8 @@ __device__ __forceinline__ bool chain_item(const ChainArgs &a, unsigned ep, int 
                                            int dep_mul, const int *epi_dep, int epi_dep_n, int *done,
                                            const EpiArgs &e, ChainLds &sh) {
     constexpr int NV = WTraits<WT>::NV;
-    constexpr int NW = AFTraits<AF>::NW;
+    constexpr int AFO = ActOp<WT, AF>::AFO;  // MFMA operand format (f32 words split at load)
+    constexpr int NW = AFTraits<AFO>::NW;
     constexpr int TE = 16 * GROUP_N;
     const int G = N / GROUP_N, KB = K / KBLK;
     if (w >= G * S) return true;
@@ -125,15 +126,15 @@ __device__ __forceinline__ bool chain_item(const ChainArgs &a, unsigned ep, int 
     for (int t = 0; t < 4; ++t) acc[0][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (kb < kb1) {
         u32x4 av[NW];
-        load_act_lanes<AF>(act, a.act_rows, K, 0, true, kb, lane, av);
+        load_act_operands<WT, AF>(act, a.act_rows, K, 0, true, kb, lane, av);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) tile_mfma<WT, AF>(wt[t], av, acc[0][t]);
+        for (int t = 0; t < 4; ++t) tile_mfma<WT, AFO>(wt[t], av, acc[0][t]);
         for (kb += 4; kb < kb1; kb += 4) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) load_wtile<WT>(W, ((size_t)g * KB + kb) * 4 + t, lane, wt[t]);
-            load_act_lanes<AF>(act, a.act_rows, K, 0, true, kb, lane, av);
+            load_act_operands<WT, AF>(act, a.act_rows, K, 0, true, kb, lane, av);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) tile_mfma<WT, AF>(wt[t], av, acc[0][t]);
+            for (int t = 0; t < 4; ++t) tile_mfma<WT, AFO>(wt[t], av, acc[0][t]);
         }
     }
     reduce_waves<1, 1>(acc, sh.tile, 0, wave, lane);
@@ -335,13 +336,12 @@ ChainFns pick(const dflash_ctx *c) {
         case DFLASH_F32:
             return {chain_head_kernel<DFLASH_F32, ACT_F32>, chain_layer_kernel<DFLASH_F32, ACT_F32, false>,
                     chain_layer_kernel<DFLASH_F32, ACT_F32, true>};
-        case DFLASH_BF16:
-            return {chain_head_kernel<DFLASH_BF16, ACT_SPLIT3>, chain_layer_kernel<DFLASH_BF16, ACT_SPLIT3, false>,
-                    chain_layer_kernel<DFLASH_BF16, ACT_SPLIT3, true>};
+        case DFLASH_BF16:  // f32 activation words, split into the three bf16 terms at load
+            return {chain_head_kernel<DFLASH_BF16, ACT_F32>, chain_layer_kernel<DFLASH_BF16, ACT_F32, false>,
+                    chain_layer_kernel<DFLASH_BF16, ACT_F32, true>};
         case DFLASH_FP8_E4M3:
-            return {chain_head_kernel<DFLASH_FP8_E4M3, ACT_SPLIT3>,
-                    chain_layer_kernel<DFLASH_FP8_E4M3, ACT_SPLIT3, false>,
-                    chain_layer_kernel<DFLASH_FP8_E4M3, ACT_SPLIT3, true>};
+            return {chain_head_kernel<DFLASH_FP8_E4M3, ACT_F32>, chain_layer_kernel<DFLASH_FP8_E4M3, ACT_F32, false>,
+                    chain_layer_kernel<DFLASH_FP8_E4M3, ACT_F32, true>};
         default: return {nullptr, nullptr, nullptr};
     }
 }

@@ -256,7 +256,7 @@ size_t carve(dflash_ctx &x, char *base) {
     x.pf_sink = cv.take<unsigned>(64);
     x.n_counters = 2 * gmax;
     x.am_key = cv.take<unsigned long long>(8ull * (V / 32) * Mmax);
-    x.am_counter = cv.take<int>(4);
+    x.am_counter = cv.take<int>(4ull * c.max_batch);  // one per sequence (a batched step's 16-row tiles)
     x.ids = cv.take<int32_t>(4ull * Mmax);
 
     const int T = c.max_inject;
@@ -413,7 +413,7 @@ int prepare(dflash_ctx &x, const dflash_weights *w, hipStream_t s) {
     HIP_TRY(launch_fill_i32(x.counters, 0, x.n_counters, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.written, 0, x.n_counters, s), "counter reset");
     HIP_TRY(launch_fill_i32((int *)x.xslot, (int)XSLOT_EMPTY, x.n_xslot, s), "exchange slot reset");
-    HIP_TRY(launch_fill_i32(x.am_counter, 0, 1, s), "counter reset");
+    HIP_TRY(launch_fill_i32(x.am_counter, 0, x.cfg.max_batch, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.csync, 0, x.n_csync, s), "counter reset");
     HIP_TRY(launch_fill_i32(x.csync, 1, 1, s), "epoch reset");  // epoch 1: flags hold 0 until first set
     return prepare_chain(x, s);

@@ -368,7 +368,7 @@ struct dflash_ctx {
     int n_xslot;
     int n_counters;
     unsigned long long *am_key;  // [G][ss_stride] per-group argmax keys (argmax_key)
-    int *am_counter;
+    int *am_counter;  // [max_batch] argmax arrivals (one per 16-row tile of a batched step)
     int32_t *ids;       // [Mmax] block ids
     // encode / inject buffers
     float *enc_y;       // [max_inject][E]

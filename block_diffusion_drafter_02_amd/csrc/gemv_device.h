@@ -503,9 +503,13 @@ __device__ __forceinline__ int argmax_key_index(unsigned long long k) { return (
 // (am_key[slot][row]), it counts itself in; the last of the arrivals (NK unless e.arrivals is set) takes
 // the largest key of every row of the step (e.rows_all, else M), writes the drafts, runs the acceptance
 // scan and re-arms the counter. best_s holds one int per row of the step.
+// TILE: the arrivals are those of one 16-row tile, rows e.row0 .. e.row0 + e.M
+// (one sequence of a batch), which the last of them finishes on its own.
+template <bool TILE = false>
 __device__ __forceinline__ void argmax_finish(const EpiArgs &e, int NK, int *flag_s, int *best_s) {
     const int tid = threadIdx.x;
-    const int M = e.rows_all ? e.rows_all : e.M;
+    const int M = TILE ? e.M : (e.rows_all ? e.rows_all : e.M);
+    const int r0 = TILE ? e.row0 : 0;  // first row of the step handled here
     const int arrivals = e.arrivals ? e.arrivals : NK;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
@@ -527,7 +531,7 @@ __device__ __forceinline__ void argmax_finish(const EpiArgs &e, int NK, int *fla
                 unsigned long long k[KU];
 #pragma unroll
                 for (int u = 0; u < KU; ++u)
-                    k[u] = g0 + 16 * u < NK ? __hip_atomic_load(e.am_key + (size_t)(g0 + 16 * u) * e.ss_stride + m,
+                    k[u] = g0 + 16 * u < NK ? __hip_atomic_load(e.am_key + (size_t)(g0 + 16 * u) * e.ss_stride + r0 + m,
                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                            : 0ull;
 #pragma unroll
@@ -540,15 +544,15 @@ __device__ __forceinline__ void argmax_finish(const EpiArgs &e, int NK, int *fla
         if (sub == 0 && m < M) {
             const int bi = argmax_key_index(best);
             best_s[m] = bi;
-            const int b = m / e.block, i = m % e.block;
+            const int b = (r0 + m) / e.block, i = (r0 + m) % e.block;
             if (i > 0 && i < e.gamma) st_i32(e.drafts + (size_t)b * (e.gamma - 1) + i - 1, bi);
         }
     }
     __syncthreads();
     if (e.target != nullptr && tid < M / e.block) {
-        const int b = tid;
+        const int b = r0 / e.block + tid;  // sequence; its rows are best_s[tid * block ..]
         int n = 0;
-        while (n < e.gamma - 1 && best_s[b * e.block + 1 + n] == e.target[(size_t)b * (e.gamma - 1) + n]) ++n;
+        while (n < e.gamma - 1 && best_s[tid * e.block + 1 + n] == e.target[(size_t)b * (e.gamma - 1) + n]) ++n;
         st_i32(e.n_ok + b, n);
     }
     if (tid == 0) __hip_atomic_store(e.am_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -599,7 +603,8 @@ __device__ __forceinline__ void logits_exchange(const EpiArgs &e, int g, int G, 
 // CW: columns of group g (64, or 32 for half groups; lanes >= CW idle). The
 // G groups of one launch write ss_out rows 0..G-1.
 // RSR: rs_s already holds the row scales (the batched epilogue's precomputed ones).
-template <int EPI, int MT, int WN, bool PF = false, int CW = GROUP_N, bool RSR = false>  // PF: operands from epi_prefetch (MT = 1)
+// ATILE: the logits' argmax finishes per 16-row tile (argmax_finish<true>).
+template <int EPI, int MT, int WN, bool PF = false, int CW = GROUP_N, bool RSR = false, bool ATILE = false>  // PF: operands from epi_prefetch (MT = 1)
 __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, float *tile, float *rs_s, int *flag_s,
                                               int *best_s, const EpiPre &pre = EpiPre{}) {
     static_assert(!PF || MT == 1, "prefetched epilogue operands cover one row tile");
@@ -795,6 +800,6 @@ __device__ __forceinline__ void gemv_epilogue(const EpiArgs &e, int g, int G, fl
                 __hip_atomic_store(e.am_key + (size_t)g * e.ss_stride + mg, argmax_key(bv, bi), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
-        argmax_finish(e, G, flag_s, best_s);
+        argmax_finish<ATILE>(e, G, flag_s, best_s);
     }
 }

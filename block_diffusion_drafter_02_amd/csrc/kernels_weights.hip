@@ -580,10 +580,13 @@ hipError_t launch_gemm(int wdtype, int act_fmt, const GemmArgs &a, hipStream_t s
 // k-split partials [S][M][N] of that tile in split order (loads of eight
 // splits in flight at a time) into LDS and runs the fused epilogue of the
 // block-row kernels on it, with the row-indexed pointers moved to its first
-// row. The logits epilogue also runs per 16-row tile; its argmax keys go to
-// the rows of the whole step, and the last of all G x M/16 workgroups reduces
-// the argmax of every row (M <= 128). One workgroup per group over all 128
-// rows measured 62 us per step at batch 8.
+// row. The logits epilogue also runs per 16-row tile, which is one sequence
+// (block width 16): its argmax keys go to the rows of the whole step, and the
+// last of the G workgroups of a tile reduces that tile's rows, writes its
+// drafts and runs its acceptance scan, each tile on its own arrival counter
+// (M <= 128, the counters held for eight sequences). One workgroup per group
+// over all 128 rows measured 62 us per step at batch 8; one last stage over
+// all rows, after every tile had arrived, 34 us against 25 us per tile.
 // ---------------------------------------------------------------------------
 template <int EPI, int MT>
 __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S, int M, int N, EpiArgs e,
@@ -592,16 +595,19 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
     constexpr int UNR = MT >= 8 ? 2 : 8;                               // splits in flight
     __shared__ __attribute__((aligned(16))) float tile[MP * GROUP_N];
     __shared__ float rs_s[MP];
-    __shared__ int best_s[EPI == EPI_LOGITS ? 128 : MP];  // the argmax's last stage holds every row
+    __shared__ int best_s[MP];
     __shared__ int flag_s;
     const int g = blockIdx.x, G = N / GROUP_N, row0 = blockIdx.y * MP, tid = threadIdx.x;
     const int rows = min(MP, M - row0);
     EpiArgs el = e;
     el.M = rows;
-    if constexpr (EPI == EPI_LOGITS) {  // argmax keys, noise and drafts index the step's rows
+    if constexpr (EPI == EPI_LOGITS) {
+        // argmax keys, noise and drafts index the step's rows; a 16-row tile is one sequence, and the last
+        // of its G workgroups finishes its argmax and acceptance (one arrival counter per tile)
         el.row0 = row0;
-        el.rows_all = M;
-        el.arrivals = G * (int)gridDim.y;
+        el.rows_all = 0;
+        el.arrivals = G;
+        el.am_counter = e.am_counter + blockIdx.y;
     }
     if (row0 > 0) {
         const size_t es = e.act_fmt == ACT_F32 ? 4 : 2;
@@ -655,7 +661,7 @@ __global__ __launch_bounds__(256) void batch_epi_kernel(const float *part, int S
             return;
         }
     }
-    gemv_epilogue<EPI, MT, 1, MT == 1>(el, g, G, tile, rs_s, &flag_s, best_s, pre);
+    gemv_epilogue<EPI, MT, 1, MT == 1, GROUP_N, false, EPI == EPI_LOGITS>(el, g, G, tile, rs_s, &flag_s, best_s, pre);
 }
 
 hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArgs &e, const float *rs, hipStream_t s) {
@@ -671,8 +677,8 @@ hipError_t launch_batch_epi(const float *part, int S, int M, int N, const EpiArg
         case EPI_SWIGLU:
             hipLaunchKernelGGL((batch_epi_kernel<EPI_SWIGLU, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e, rs);
             break;
-        case EPI_LOGITS:  // one 16-row tile per workgroup; the argmax's last stage covers all M <= 128 rows
-            if (M > 128) return hipErrorInvalidValue;
+        case EPI_LOGITS:  // one 16-row tile (one sequence) per workgroup row; one arrival counter per tile
+            if (M > 128 || e.block != 16) return hipErrorInvalidValue;
             hipLaunchKernelGGL((batch_epi_kernel<EPI_LOGITS, 1>), rows_grid, dim3(256), 0, s, part, S, M, N, e, rs);
             break;
         default: return hipErrorInvalidValue;

@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the DFlash drafter block step on one MI355X.
 
-One step = one captured block step (embed, 5 drafter layers with ring + block
+One step = one block step (embed, 5 drafter layers with ring + block
 attention, output norm, lm_head, greedy drafts) plus the device-side
-acceptance scan, on inputs already resident in HBM. Default workload: real
+acceptance scan, on inputs already resident in HBM, launched eagerly on a
+stream (dflash_block_step_accept; --launch graph replays a captured step
+instead, which measured about 6 us slower per step). Default workload: real
 drafter dimensions (5 layers, n_embd 6656, heads 32/8, head_dim 128, n_ff
 19968, window 2048, block 16, vocab 8192), bf16 weights and bf16 ring, ring full
 (positions 0..2047 injected), n_past 2048; every step gets a fresh id_last and a
@@ -300,6 +302,9 @@ def main() -> int:
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--path", default="auto", choices=["auto", "kernels", "persistent"],
                     help="block-step path (auto: the per-launch kernels; persistent: the opt-in persistent chain)")
+    ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
+                    help="how each timed step is launched: eager (dflash_block_step_accept on the stream, the default) "
+                         "or graph (a replay of the step captured with dflash_step_graph_create)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (five times) to calibrate byte counters")
     ap.add_argument("--summarize-trace", metavar="RUN_DIR",
@@ -410,11 +415,17 @@ def main() -> int:
         dr.inject(rings[0], h_inj, pos_all[k], stream=stream)
         npst.copy_(np_all[k])
 
+    def launch_step():
+        if args.launch == "graph":
+            graph.launch(stream)
+        else:
+            dr.block_step(table, il, npst, out=(logits, drafts), stream=stream, target=target, n_ok=n_ok)
+
     def step(k):
         if T_inj:
             inject_step(k)
         inputs.copy_(inputs_all[k])
-        graph.launch(stream)
+        launch_step()
 
     # untimed pass over the same step sequence: learn each step's drafts and plant its target
     print("[bench] planting per-step targets", file=sys.stderr, flush=True)
@@ -446,14 +457,18 @@ def main() -> int:
         ev_ms = ev[0].elapsed_time(ev[K]) / K
         n_ok_last = n_ok.cpu().numpy()
         accept_ok = bool(np.array_equal(n_ok_last, mism_all[W + K - 1]))
-        # replays alone, without the per-step input refresh
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # steps alone, without the per-step input refresh: graph replays, then eager launches
+        g0, g1, g2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         g0.record(stream)
         for k in range(K):
             graph.launch(stream)
         g1.record(stream)
+        for k in range(K):
+            dr.block_step(table, il, npst, out=(logits, drafts), stream=stream, target=target, n_ok=n_ok)
+        g2.record(stream)
         torch.cuda.synchronize()
         graph_ms = g0.elapsed_time(g1) / K
+        eager_ms = g1.elapsed_time(g2) / K
         # dominant kernel of the block step: the gate/up GEMV of layer 0, launched alone on the same stream
         r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for _ in range(3):
@@ -506,6 +521,7 @@ def main() -> int:
         "step_us_p10": round(float(np.percentile(per_step_us, 10)), 2),
         "step_us_p90": round(float(np.percentile(per_step_us, 90)), 2),
         "graph_only_ms_per_step": round(graph_ms, 5),
+        "eager_only_ms_per_step": round(eager_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -522,6 +538,7 @@ def main() -> int:
             "temperature": temp,
             "paged_kv": paged,
             "path": "persistent" if dr.step_path(B) == _lib.PATH_PERSISTENT else "kernels",
+            "launch": args.launch,
             "algorithmic_bytes_per_step": total,
             "weight_bytes_per_step": nb["weights"],
             "ring_bytes_per_step": nb["ring"],

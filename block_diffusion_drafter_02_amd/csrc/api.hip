@@ -954,6 +954,14 @@ int dflash_block_step(dflash_ctx *x, void *const *rings, const int32_t *id_last,
     return run_step(*x, rings, id_last, nullptr, n_past, B, logits, drafts, nullptr, nullptr, (hipStream_t)stream);
 }
 
+int dflash_block_step_accept(dflash_ctx *x, void *const *rings, const int32_t *id_last, const int32_t *n_past,
+                             int32_t B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
+                             void *stream) {
+    TRY(check_step_args(x, rings, id_last, n_past, B, logits, drafts));
+    if (!target || !n_ok) return fail(DFLASH_EINVAL, "target or n_ok is NULL");
+    return run_step(*x, rings, id_last, nullptr, n_past, B, logits, drafts, target, n_ok, (hipStream_t)stream);
+}
+
 int dflash_block_forward(dflash_ctx *x, void *const *rings, const int32_t *block_ids, const int32_t *n_past, int32_t B,
                          float *logits, int32_t *drafts, void *stream) {
     TRY(check_step_args(x, rings, block_ids, n_past, B, logits, drafts));

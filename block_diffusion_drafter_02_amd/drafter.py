@@ -255,13 +255,23 @@ class Drafter:
         return logits, drafts
 
     def block_step(self, ring_table: torch.Tensor, id_last: torch.Tensor, n_past: torch.Tensor, out=None,
-                   stream=None):
+                   stream=None, target: torch.Tensor | None = None, n_ok: torch.Tensor | None = None):
+        """The block step; with target [B, g-1] (and optionally n_ok [B]) also the acceptance scan, fused into
+        the logits launch (dflash_block_step_accept). Returns (logits, drafts), plus n_ok when target is given."""
         B = id_last.shape[0]
         logits, drafts = out if out is not None else self._outputs(B)
-        check(lib().dflash_block_step(self._ctx, _dev(ring_table, torch.int64, "rings"),
-                                      _dev(id_last, torch.int32, "id_last"), _dev(n_past, torch.int32, "n_past"), B,
-                                      logits.data_ptr(), drafts.data_ptr(), _stream(stream)))
-        return logits, drafts
+        rings, il, npst = (_dev(ring_table, torch.int64, "rings"), _dev(id_last, torch.int32, "id_last"),
+                           _dev(n_past, torch.int32, "n_past"))
+        if target is None:
+            check(lib().dflash_block_step(self._ctx, rings, il, npst, B, logits.data_ptr(), drafts.data_ptr(),
+                                          _stream(stream)))
+            return logits, drafts
+        if n_ok is None:
+            n_ok = torch.empty((B,), dtype=torch.int32, device=self.device)
+        check(lib().dflash_block_step_accept(self._ctx, rings, il, npst, B, logits.data_ptr(), drafts.data_ptr(),
+                                             _dev(target, torch.int32, "target"), _dev(n_ok, torch.int32, "n_ok"),
+                                             _stream(stream)))
+        return logits, drafts, n_ok
 
     def block_forward(self, ring_table: torch.Tensor, block_ids: torch.Tensor, n_past: torch.Tensor, stream=None):
         B = block_ids.shape[0]

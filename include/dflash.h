@@ -201,6 +201,19 @@ int dflash_inject_batch(dflash_ctx *ctx, void *const *rings, int32_t n_seq, cons
 int dflash_block_step(dflash_ctx *ctx, void *const *rings, const int32_t *id_last, const int32_t *n_past, int32_t B,
                       float *logits, int32_t *drafts, void *stream);
 
+/* dflash_block_step followed by the first-mismatch acceptance of
+ * dflash_accept (dflash-ops card, Usage; dflash_engine.py page,
+ * DFlashSpeculativeVerifier.verify_block), launched directly on `stream`:
+ * the scan runs in the last workgroup of the logits launch, as in a graph
+ * captured with target and n_ok. target [B, g-1] int32 (device) holds the
+ * target's tokens at the draft positions; n_ok [B] int32 (device) receives
+ * the number of leading draft positions that match. The other arguments,
+ * outputs and errors are those of dflash_block_step; target and n_ok must be
+ * non-NULL. */
+int dflash_block_step_accept(dflash_ctx *ctx, void *const *rings, const int32_t *id_last, const int32_t *n_past,
+                             int32_t B, float *logits, int32_t *drafts, const int32_t *target, int32_t *n_ok,
+                             void *stream);
+
 /* As dflash_block_step but with explicit block ids [B, 16] (device) instead
  * of id_last: a hook for testing joint (non-causal) denoising (dflash-ops
  * card, Correctness: a change at a later block position must move the logits

@@ -95,6 +95,7 @@ def test_null_arguments_fail_before_any_gpu_work(L):
     assert L.dflash_encode(None, None, 1, None, None) == _lib.EINVAL
     assert L.dflash_inject(None, None, None, None, 1, None) == _lib.EINVAL
     assert L.dflash_block_step(None, None, None, None, 1, None, None, None) == _lib.EINVAL
+    assert L.dflash_block_step_accept(None, None, None, None, 1, None, None, None, None, None) == _lib.EINVAL
     assert L.dflash_block_forward(None, None, None, None, 1, None, None, None) == _lib.EINVAL
     assert L.dflash_accept(None, None, None, 1, None, None) == _lib.EINVAL
     assert L.dflash_step_graph_create(None, None, None, None, 1, None, None, None, None, None, C.byref(h)) == _lib.EINVAL

@@ -270,6 +270,36 @@ def test_graph_replay_is_bitwise_equal_to_eager_with_interleaved_traffic(gpu, pa
     dr.check_device()
 
 
+@pytest.mark.parametrize("path,B", [("kernels", 1), ("persistent", 1), ("kernels", 3)])
+def test_eager_step_with_acceptance(gpu, path, B):
+    """dflash_block_step_accept: logits and drafts bitwise those of dflash_block_step, and n_ok that of the
+    oracle's acceptance scan on those drafts against a target with a planted mismatch per sequence (the scan
+    runs inside the logits launch; at B = 3 per 16-row tile of the batched epilogue)."""
+    torch = _torch()
+    spec = WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16")
+    dr, ring, fdev, _, raw, feats = _build(spec, 300, max_batch=B)
+    dr.set_path(PATHS[path])
+    print(f"[case] eager accept {path} B={B}", flush=True)
+    table = dr.ring_table([ring] * B)
+    il = torch.tensor([5 + 4 * b for b in range(B)], dtype=torch.int32, device=dr.device)
+    npst = torch.tensor([300 - 7 * b for b in range(B)], dtype=torch.int32, device=dr.device)
+    e_logits, e_drafts = dr.block_step(table, il, npst)
+    torch.cuda.synchronize()
+    g1 = e_drafts.shape[1]
+    for m in ([4] * B, [g1, 0, 9][:B]):  # planted mismatch per sequence (g - 1: none)
+        target = e_drafts.clone()
+        for b, mb in enumerate(m):
+            if mb < g1:
+                target[b, mb] = (target[b, mb] + 1) % spec.shape.n_vocab
+        logits, drafts, n_ok = dr.block_step(table, il, npst, target=target)
+        torch.cuda.synchronize()
+        assert torch.equal(logits, e_logits) and torch.equal(drafts, e_drafts)
+        d, t = drafts.cpu().numpy(), target.cpu().numpy()
+        got = n_ok.cpu().numpy().tolist()
+        assert got == [O.accept(d[b], t[b]) for b in range(B)] == m, (got, m)
+    dr.check_device()
+
+
 @pytest.mark.parametrize("spec", [WL.Spec(WL.MEDIUM, "bf16", "bf16", "bf16"), WL.Spec(WL.MEDIUM, "f32", "f32", "f32"),
                                   WL.Spec(WL.MEDIUM, "fp8", "bf16", "bf16")], ids=_spec_id)
 def test_persistent_and_per_launch_paths_agree(gpu, spec):

@@ -413,19 +413,19 @@ def main() -> int:
     def inject_step(k):
         dr.encode(pool[k % FEATURE_POOL], h_inj, stream=stream)
         dr.inject(rings[0], h_inj, pos_all[k], stream=stream)
-        npst.copy_(np_all[k])
-
-    def launch_step():
-        if args.launch == "graph":
-            graph.launch(stream)
-        else:
-            dr.block_step(table, il, npst, out=(logits, drafts), stream=stream, target=target, n_ok=n_ok)
 
     def step(k):
         if T_inj:
             inject_step(k)
-        inputs.copy_(inputs_all[k])
-        launch_step()
+        if args.launch == "graph":  # the graph reads fixed buffers: refresh them
+            if T_inj:
+                npst.copy_(np_all[k])
+            inputs.copy_(inputs_all[k])
+            graph.launch(stream)
+        else:  # an eager step takes this step's inputs where they lie
+            row = inputs_all[k]
+            dr.block_step(table, row[:B], np_all[k] if T_inj else npst, out=(logits, drafts), stream=stream,
+                          target=row[B:].view(B, g - 1), n_ok=n_ok)
 
     # untimed pass over the same step sequence: learn each step's drafts and plant its target
     print("[bench] planting per-step targets", file=sys.stderr, flush=True)

@@ -255,11 +255,11 @@ NON_GEMM = ("attn_partial_kernel", "attn_combine_kernel", "embed_kernel", "accep
 STEP_FIRST = ("embed_kernel", "chain_head_kernel")  # the first kernel of every block step
 
 
-def summarize_trace(run_dir: str, skip_replays: int = 5) -> dict:
-    """Per-kernel durations, per-replay span (first kernel start to last kernel end of one block step) and
+def summarize_trace(run_dir: str, skip_steps: int = 5) -> dict:
+    """Per-kernel durations, per-step span (first kernel start to last kernel end of one block step) and
     the non-GEMM share of kernel time from a rocprofv3 --kernel-trace CSV of bench runs. Steps are cut at
     the first kernel of each step; setup kernels before the first step and after the last are dropped, and
-    so are the first ``skip_replays`` steps."""
+    so are the first ``skip_steps`` steps."""
     import csv
     import glob
 
@@ -268,10 +268,10 @@ def summarize_trace(run_dir: str, skip_replays: int = 5) -> dict:
         rows += [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in csv.DictReader(open(f))]
     rows.sort()
     starts = [i for i, r in enumerate(rows) if r[2].startswith(STEP_FIRST)]
-    if len(starts) < skip_replays + 2:
+    if len(starts) < skip_steps + 2:
         raise SystemExit(f"{run_dir}: {len(starts)} block steps in the trace")
     spans, per_kernel, gemm_t, other_t = [], {}, 0.0, 0.0
-    for a, b in zip(starts[skip_replays:-1], starts[skip_replays + 1:]):
+    for a, b in zip(starts[skip_steps:-1], starts[skip_steps + 1:]):
         step = [r for r in rows[a:b] if not r[2].startswith("__amd_rocclr")]
         # a step ends with the projection that writes the logits; later kernels belong to the host loop
         spans.append((max(r[1] for r in step) - step[0][0]) / 1e3)
@@ -308,7 +308,7 @@ def main() -> int:
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (five times) to calibrate byte counters")
     ap.add_argument("--summarize-trace", metavar="RUN_DIR",
-                    help="summarise a rocprofv3 --kernel-trace run of this bench (per-kernel times, per-replay span, "
+                    help="summarise a rocprofv3 --kernel-trace run of this bench (per-kernel times, per-step span, "
                          "non-GEMM share) as JSON, then exit (no GPU needed)")
     ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="reduce two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy-mib bench "

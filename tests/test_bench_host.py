@@ -100,7 +100,7 @@ def test_trace_summary_spans_and_non_gemm_share(tmp_path):
         w.writeheader()
         for name, a, b in rows:
             w.writerow({"Kernel_Name": name, "Start_Timestamp": a * 1000, "End_Timestamp": b * 1000})
-    out = bench.summarize_trace(str(path), skip_replays=0)
+    out = bench.summarize_trace(str(path), skip_steps=0)
     assert out["steps"] == 2  # the last step has no following step start and is dropped
     assert out["span_us_median"] == 5 + 1 + 20 + 1 + 10 + 1 + 5 + 1 + 60
     assert out["non_gemm_share"] == round(20 / 100, 4)

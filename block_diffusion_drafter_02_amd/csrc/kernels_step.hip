@@ -507,7 +507,12 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
     const bool is_block = (c == a.NCH);
     const bool bf16_ring = a.ring_dtype == DFLASH_BF16;
     const bool split_kv = is_block || !bf16_ring;  // fp32 keys/values need three terms
-    const int nkeys = is_block ? 16 : a.CH;
+    // A ring chunk whose slots all lie at or past n_past + block holds no key that a block row sees: slot s
+    // holds a position p = s (mod W) with p >= s > n_past + i for every row i. It loads nothing and its
+    // partial comes out empty (m = -inf, l = 0, o = 0), exactly as for a chunk of masked keys.
+    const int np = a.n_past[b];
+    const bool past = !is_block && c * a.CH >= np + a.block;
+    const int nkeys = is_block ? 16 : (past ? 0 : a.CH);
     const int nks2 = (nkeys + 31) / 32;    // k-steps over keys for P V (the block pads 16 keys to 32)
     const int CHP = nks2 * 32 + 4;         // V^T row length: keys padded to 32, +4 to spread LDS banks
     const int nplanes = split_kv ? 3 : 1;
@@ -536,13 +541,13 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
     // position, this wave's query row (and the block's key row), the chunk's slot
     // positions, and (staged to LDS with the chunk) the two norm weight vectors
     // and the block rows' rope pairs ----
-    const int qpos = a.n_past[b] + q;
+    const int qpos = np + q;
     float qv[KS][8], kbv[KS][8];
     if (active) {
         head_load<D>(qv, qkvb + (size_t)q * a.nqkv + (size_t)(j * a.G + hh) * D, grp);
         if (is_block) head_load<D>(kbv, qkvb + (size_t)q * a.nqkv + a.qdim + (size_t)j * D, grp);
     }
-    const int kp_reg = (!is_block && tid < a.CH) ? (loc.ok ? sp[s0 + tid] : -1) : 0;  // bad page: empty
+    const int kp_reg = (!is_block && !past && tid < a.CH) ? (loc.ok ? sp[s0 + tid] : -1) : 0;  // bad page: empty
     const int ncs4 = a.block * D / 4;  // float4 words of the rope table rows (at most 512)
     constexpr int NCS = 512 / NT;
     float4 cs_reg[NCS], w_reg = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -564,6 +569,8 @@ __global__ __launch_bounds__(NT) void attn_partial_kernel(AttnArgs a) {
             vt[(1 * D + d) * CHP + key] = t1;
             vt[(2 * D + d) * CHP + key] = t2;
         }
+    } else if (past) {
+        // nothing to stage
     } else if (bf16_ring) {
         // K rows and V rows: CH*D/8 16-byte words each, in batches with all loads in flight
         constexpr int NWORD = (16 * NHALF * HKT * D / 8 + NT - 1) / NT;

@@ -117,7 +117,10 @@ size_t dflash_workspace_bytes(const dflash_config *cfg);
 
 /* Bytes of one sequence's ring: K and V [n_layer][n_kv][window][head_dim] in
  * ring_dtype, then int32 slot_pos[window] (the position each slot holds, -1
- * when empty). 256-byte alignment required. */
+ * when empty). 256-byte alignment required. Slot s holds -1 or a position p
+ * >= 0 with p % window == s, as dflash_inject and dflash_ring_reset leave it;
+ * the block step relies on this to skip slots at or past n_past + 16, which
+ * no block row can see (a ring written by other means must keep it). */
 size_t dflash_ring_bytes(const dflash_config *cfg);
 
 /* Validate cfg, carve the caller's workspace and, on `stream`, re-tile every

@@ -903,7 +903,6 @@ struct CombArgs {
     int act_fmt, act_rows, qdim;
 };
 
-template <int UNR>
 __global__ __launch_bounds__(256) void attn_combine_kernel(CombArgs a) {
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x;
@@ -913,11 +912,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(CombArgs a) {
     const int NQ = a.G * 16, qi = hh * 16 + i;
     const size_t base = ((size_t)b * a.Hkv + j) * (a.NCH + 1);
     const int nc = a.NCH + 1;
-    // batches of UNR chunks whose loads are all in flight together (17 when that
-    // covers every chunk: one sequence's 128-slot chunks of a 2048-slot window,
-    // 4.6 against 5.3 us with batches of 24, the same arithmetic); per batch
+    // batches of 17 chunks whose loads are all in flight together (one batch for
+    // one sequence's 128-slot chunks of a 2048-slot window: 4.6 against 5.3 us
+    // with batches of 24; two for the 64-slot chunks of a batch: 17.2 against
+    // 19.6 us at batch 8); per batch
     // the running state is rescaled once to the batch's maximum and every
     // chunk weight exp(m_c - max) is independent of the others
+    constexpr int UNR = 17;
     float mstar = -INFINITY, lsum = 0.0f, o0 = 0.0f, o1 = 0.0f;
     for (int c0 = 0; c0 < nc; c0 += UNR) {
         float2 mlb[UNR], ovb[UNR];
@@ -1026,10 +1027,7 @@ hipError_t launch_attention(const dflash_ctx *c, int l, void *const *rings, cons
     cb.act_fmt = c->blk_fmt;
     cb.act_rows = c->Mmax;
     cb.qdim = c->qdim;
-    if (a.NCH + 1 <= 17)
-        hipLaunchKernelGGL(attn_combine_kernel<17>, dim3(c->H, B, c->D / 32), dim3(256), 0, s, cb);
-    else
-        hipLaunchKernelGGL(attn_combine_kernel<24>, dim3(c->H, B, c->D / 32), dim3(256), 0, s, cb);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(c->H, B, c->D / 32), dim3(256), 0, s, cb);
     return hipGetLastError();
 }
 

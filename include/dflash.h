@@ -207,8 +207,8 @@ int dflash_block_step(dflash_ctx *ctx, void *const *rings, const int32_t *id_las
 /* dflash_block_step followed by the first-mismatch acceptance of
  * dflash_accept (dflash-ops card, Usage; dflash_engine.py page,
  * DFlashSpeculativeVerifier.verify_block), launched directly on `stream`:
- * the scan runs in the last workgroup of the logits launch, as in a graph
- * captured with target and n_ok. target [B, g-1] int32 (device) holds the
+ * the scan runs inside the logits launch (in the last workgroup to finish a
+ * sequence's logits), as in a graph captured with target and n_ok. target [B, g-1] int32 (device) holds the
  * target's tokens at the draft positions; n_ok [B] int32 (device) receives
  * the number of leading draft positions that match. The other arguments,
  * outputs and errors are those of dflash_block_step; target and n_ok must be

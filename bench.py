@@ -3,9 +3,11 @@
 
 One step = one block step (embed, 5 drafter layers with ring + block
 attention, output norm, lm_head, greedy drafts) plus the device-side
-acceptance scan, on inputs already resident in HBM, launched eagerly on a
-stream (dflash_block_step_accept; --launch graph replays a captured step
-instead, which measured about 6 us slower per step). Default workload: real
+acceptance scan, on inputs already resident in HBM: by default a replay of
+the step captured in a HIP graph (its inputs refreshed by one device copy per
+step); --launch eager launches it directly on the stream instead
+(dflash_block_step_accept, about 10 us faster per step), and every line also
+reports the other launch mode's time on the same steps. Default workload: real
 drafter dimensions (5 layers, n_embd 6656, heads 32/8, head_dim 128, n_ff
 19968, window 2048, block 16, vocab 8192), bf16 weights and bf16 ring, ring full
 (positions 0..2047 injected), n_past 2048; every step gets a fresh id_last and a
@@ -302,9 +304,9 @@ def main() -> int:
     ap.add_argument("--stage-reps", type=int, default=50)
     ap.add_argument("--path", default="auto", choices=["auto", "kernels", "persistent"],
                     help="block-step path (auto: the per-launch kernels; persistent: the opt-in persistent chain)")
-    ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
-                    help="how each timed step is launched: eager (dflash_block_step_accept on the stream, the default) "
-                         "or graph (a replay of the step captured with dflash_step_graph_create)")
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="how each timed step is launched: graph (a replay of the step captured with "
+                         "dflash_step_graph_create, the default) or eager (dflash_block_step_accept on the stream)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (five times) to calibrate byte counters")
     ap.add_argument("--summarize-trace", metavar="RUN_DIR",
@@ -414,10 +416,10 @@ def main() -> int:
         dr.encode(pool[k % FEATURE_POOL], h_inj, stream=stream)
         dr.inject(rings[0], h_inj, pos_all[k], stream=stream)
 
-    def step(k):
+    def step(k, mode=None):
         if T_inj:
             inject_step(k)
-        if args.launch == "graph":  # the graph reads fixed buffers: refresh them
+        if (mode or args.launch) == "graph":  # the graph reads fixed buffers: refresh them
             if T_inj:
                 npst.copy_(np_all[k])
             inputs.copy_(inputs_all[k])
@@ -465,6 +467,15 @@ def main() -> int:
         ev[K].record(stream)
         torch.cuda.synchronize()
         per_step_us = np.array([ev[k].elapsed_time(ev[k + 1]) * 1e3 for k in range(K)])
+        # the same K steps launched the other way
+        other = "eager" if args.launch == "graph" else "graph"
+        o0, o1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        o0.record(stream)
+        for k in range(K):
+            step(W + k, other)
+        o1.record(stream)
+        torch.cuda.synchronize()
+        other_ms = o0.elapsed_time(o1) / K
         # steps alone, without the per-step input refresh: graph replays, then eager launches
         g0, g1, g2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         g0.record(stream)
@@ -530,6 +541,8 @@ def main() -> int:
         "step_us_p90": round(float(np.percentile(per_step_us, 90)), 2),
         "graph_only_ms_per_step": round(graph_ms, 5),
         "eager_only_ms_per_step": round(eager_ms, 5),
+        "other_launch": {"launch": other, "ms_per_step": round(other_ms, 5), "step_us": round(other_ms * 1e3, 2),
+                         "value": round(total / (other_ms * 1e-3) / 1e9, 2)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
